@@ -1,0 +1,143 @@
+"""Python binding of libcattn (ctypes): argument marshalling only.
+
+Every step of the forward runs in the HIP kernels behind the C ABI
+(``include/cattn.h``); PyTorch provides device memory and the current stream.
+There is no fallback: if the library is not built, calls raise.
+
+Tensors are ``[B, H, T, d_h]``, contiguous, on a ROCm device:
+
+* complex64: ``q, k, v`` are ``torch.complex64`` tensors;
+* bf16 planes: ``q, k, v`` are ``(re, im)`` pairs of ``torch.bfloat16`` tensors.
+
+The output has the layout of the inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libcattn.so")
+
+LAYOUT_C64 = 0
+LAYOUT_BF16_PLANES = 1
+
+STATUS = {
+    0: "CATTN_OK", 1: "CATTN_E_NULL", 2: "CATTN_E_SHAPE", 3: "CATTN_E_LAYOUT", 4: "CATTN_E_ALIGN",
+    5: "CATTN_E_ALIAS", 6: "CATTN_E_UNSUPPORTED", 7: "CATTN_E_LAUNCH", 8: "CATTN_E_ARG",
+}
+
+_lib = None
+
+
+class CattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcattn.so, with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libcattn.so is not built ({LIB_PATH}); run "
+                           "`python -m complex_valued_attention_amd.build` or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.cattn_born_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                 ctypes.c_int, ctypes.c_float, vp, vp]
+    L.cattn_born_fwd.restype = ctypes.c_int
+    L.cattn_pct_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                ctypes.c_int, ctypes.c_float, vp]
+    L.cattn_pct_fwd.restype = ctypes.c_int
+    L.cattn_status_str.argtypes = [ctypes.c_int]
+    L.cattn_status_str.restype = ctypes.c_char_p
+    L.cattn_abi_version.argtypes = []
+    L.cattn_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(s: int) -> str:
+    return lib().cattn_status_str(s).decode()
+
+
+def _check(s: int):
+    if s != 0:
+        raise CattnError(s, status_str(s))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _unpack(x, name):
+    """(layout, re, im, shape) of one operand."""
+    import torch
+    if isinstance(x, (tuple, list)):
+        re, im = x
+        if re.dtype != torch.bfloat16 or im.dtype != torch.bfloat16:
+            raise TypeError(f"{name}: bf16 planes expected")
+        if re.shape != im.shape:
+            raise ValueError(f"{name}: real and imaginary planes differ in shape")
+        for t in (re, im):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}: contiguous device tensors expected")
+        return LAYOUT_BF16_PLANES, re, im, tuple(re.shape)
+    if x.dtype != torch.complex64:
+        raise TypeError(f"{name}: torch.complex64 or a (re, im) pair of bf16 tensors expected")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name}: contiguous device tensor expected")
+    return LAYOUT_C64, x, None, tuple(x.shape)
+
+
+def _prepare(q, k, v, out):
+    import torch
+    lq, qre, qim, shape = _unpack(q, "q")
+    lk, kre, kim, sk = _unpack(k, "k")
+    lv, vre, vim, sv = _unpack(v, "v")
+    if not (lq == lk == lv):
+        raise TypeError("q, k and v must share one layout")
+    if not (shape == sk == sv) or len(shape) != 4:
+        raise ValueError(f"q, k, v must all be [B, H, T, d_h]; got {shape}, {sk}, {sv}")
+    if out is None:
+        if lq == LAYOUT_C64:
+            out = torch.empty_like(qre)
+        else:
+            out = (torch.empty_like(qre), torch.empty_like(qre))
+    lo, ore, oim, so = _unpack(out, "out")
+    if lo != lq or so != shape:
+        raise ValueError("out must match the inputs' layout and shape")
+    return lq, (qre, qim, kre, kim, vre, vim, ore, oim), shape, out
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def born_fwd(q, k, v, causal: bool = True, eps: float = 0.0, out=None, row_den=None):
+    """Born-rule attention forward (cattn_born_fwd).  Returns the output tensor(s)."""
+    layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
+    if row_den is not None and (row_den.numel() != B * H * T or not row_den.is_contiguous()):
+        raise ValueError("row_den must be a contiguous float32 tensor of B*H*T elements")
+    s = lib().cattn_born_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, int(bool(causal)),
+                             float(eps), _ptr(row_den), _stream(ts[0]))
+    _check(s)
+    return out
+
+
+def pct_fwd(q, k, v, causal: bool = False, bias: float = 0.0, out=None):
+    """Phase-coherent attention forward (cattn_pct_fwd).  Returns the output tensor(s)."""
+    layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
+    s = lib().cattn_pct_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, int(bool(causal)),
+                            float(bias), _stream(ts[0]))
+    _check(s)
+    return out
+
+
+def default_pct_bias(T: int) -> float:
+    """The pages' initial gate bias -log N."""
+    return -math.log(T)

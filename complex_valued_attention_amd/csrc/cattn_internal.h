@@ -1,0 +1,39 @@
+// Internal launch interface shared by the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cattn {
+
+enum Op : int { OP_BORN = 0, OP_PCT = 1 };
+enum Layout : int { LAYOUT_C64 = 0, LAYOUT_BF16 = 1 };
+
+// One validated forward call.  Pointers are device pointers; tensors are
+// [BH, T, d] row-major (B and H folded, they never interact).
+struct Problem {
+    int op;
+    int layout;
+    const void *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
+    void *o_re, *o_im;
+    float *row_den;     // Born only, may be null
+    int BH;
+    int T;
+    int d;
+    int causal;
+    float eps;          // Born
+    float bias;         // PCT
+    hipStream_t stream;
+};
+
+// Each launcher enqueues the whole forward for `p` and returns the launch
+// status.  `supports_*` say whether a specialised kernel covers `p`.
+hipError_t launch_generic(const Problem &p);
+
+bool supports_born_bf16_mfma(const Problem &p);
+hipError_t launch_born_bf16_mfma(const Problem &p);
+
+bool supports_f32_mfma(const Problem &p);
+hipError_t launch_f32_mfma(const Problem &p);
+
+}  // namespace cattn

@@ -1,0 +1,116 @@
+/*
+ * cattn.h -- fused forward pass of complex-valued attention on AMD Instinct
+ * gfx950 (CDNA4).  C ABI: plain pointers and sizes, no C++ or framework types.
+ *
+ * Two operators, both ending in O = W V over complex values V:
+ *
+ *   Born-rule attention ("CNet: A Complex-Valued Deep Learning Framework with
+ *   Wirtinger Autodifferentiation and FFT-Hadamard Convolution", section 11.2,
+ *   paragraph "Closing it: Born-rule attention", Figure 2):
+ *       S[k,j] = sum_m Q[k,m] conj(K[j,m])          (Hermitian inner product)
+ *       w[k,j] = |S[k,j]|^2
+ *       O[k]   = sum_{j in J(k)} w[k,j] V[j] / (sum_{j in J(k)} w[k,j] + eps)
+ *   A row whose denominator is 0 is written as 0.
+ *
+ *   Phase-coherent (PCT) attention ("Complex-valued Phase-Coherent
+ *   Transformers", section 1 and Appendix D.2, the PCT cell):
+ *       s[i,j] = sqrt(d_h) Re < q_i/||q_i||, k_j/||k_j|| >
+ *       w[i,j] = sigmoid(s[i,j] + bias)
+ *       O[i]   = sum_{j in J(i)} w[i,j] V[j]             (no row normalisation)
+ *   A zero-norm q or k contributes score 0 (weight sigmoid(bias)).
+ *
+ * J(k) = {0..k} if causal != 0, else {0..T-1}.
+ *
+ * Tensors.  Q, K, V and O are [B, H, T, d_h], dense and row-major (d_h
+ * fastest), in DEVICE memory owned by the caller; the library allocates
+ * nothing and keeps no state.  Two layouts:
+ *   CATTN_LAYOUT_C64        interleaved complex64 (float re, float im); pass
+ *                           the tensor in the *_re argument, *_im must be NULL.
+ *   CATTN_LAYOUT_BF16_PLANES two bf16 tensors per operand, real plane in *_re
+ *                           and imaginary plane in *_im.
+ * O is written in the layout of the inputs and fully overwritten.
+ * Arithmetic: bf16 planes use bf16 matrix-core products with fp32
+ * accumulation; complex64 uses fp32 throughout.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ * stream of the current device) and run on the current HIP device.
+ *
+ * Errors.  All argument checks happen before any HIP call; on an argument
+ * error nothing is enqueued and a status other than CATTN_OK is returned.
+ * A failed kernel launch returns CATTN_E_LAUNCH.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  Sizes B, H or T equal to 0
+ * are an empty problem: CATTN_OK, nothing enqueued.
+ */
+#ifndef CATTN_H
+#define CATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CATTN_OK = 0,
+    CATTN_E_NULL = 1,        /* a required pointer is NULL, or *_im is non-NULL for C64 */
+    CATTN_E_SHAPE = 2,       /* a size is negative, or the byte size overflows int64 */
+    CATTN_E_LAYOUT = 3,      /* unknown layout value */
+    CATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    CATTN_E_ALIAS = 5,       /* O or row_den overlaps an input or each other */
+    CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 */
+    CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
+    CATTN_E_ARG = 8          /* eps negative or not finite, or bias not finite */
+} cattn_status;
+
+typedef enum {
+    CATTN_LAYOUT_C64 = 0,
+    CATTN_LAYOUT_BF16_PLANES = 1
+} cattn_layout;
+
+/* Largest head width accepted. */
+#define CATTN_MAX_DH 128
+
+/*
+ * Born-rule attention forward (definition above).
+ *   layout        CATTN_LAYOUT_C64 or CATTN_LAYOUT_BF16_PLANES.
+ *   q_*, k_*, v_* inputs, o_* output (device pointers, see "Tensors").
+ *   B, H, T, d_h  batch, heads, sequence length, head width (complex
+ *                 components per token); 1 <= d_h <= CATTN_MAX_DH.
+ *   causal        non-zero: query k sees keys 0..k; zero: all keys.
+ *   eps           added to each row denominator; >= 0 and finite.
+ *   row_den       optional (NULL allowed) device float[B*H*T]: receives each
+ *                 row's denominator sum_j w + eps.
+ *   stream        hipStream_t to enqueue on.
+ */
+cattn_status cattn_born_fwd(int layout,
+                            const void *q_re, const void *q_im,
+                            const void *k_re, const void *k_im,
+                            const void *v_re, const void *v_im,
+                            void *o_re, void *o_im,
+                            int64_t B, int64_t H, int64_t T, int64_t d_h,
+                            int causal, float eps, float *row_den, void *stream);
+
+/*
+ * Phase-coherent (PCT) attention forward (definition above).  Arguments as
+ * for cattn_born_fwd; `bias` is the gate bias b (finite; the pages
+ * initialise it to -log N, 0 gives a plain sigmoid of the score).
+ */
+cattn_status cattn_pct_fwd(int layout,
+                           const void *q_re, const void *q_im,
+                           const void *k_re, const void *k_im,
+                           const void *v_re, const void *v_im,
+                           void *o_re, void *o_im,
+                           int64_t B, int64_t H, int64_t T, int64_t d_h,
+                           int causal, float bias, void *stream);
+
+/* Static, NUL-terminated description of a status value (never NULL). */
+const char *cattn_status_str(int status);
+
+/* ABI version of this header: 1. */
+int cattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CATTN_H */

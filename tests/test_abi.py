@@ -1,0 +1,114 @@
+"""The C-ABI library: it loads, exports every function include/cattn.h declares,
+and rejects bad arguments before any HIP call (CPU only, no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from complex_valued_attention_amd import cattn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "cattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(cattn.LIB_PATH), reason="libcattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == ["cattn_abi_version", "cattn_born_fwd", "cattn_pct_fwd", "cattn_status_str"]
+
+
+def test_library_exports_every_declared_symbol():
+    L = cattn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.cattn_abi_version() == 1
+
+
+def test_status_strings():
+    L = cattn.lib()
+    for s in range(0, 9):
+        assert L.cattn_status_str(s)
+    assert L.cattn_status_str(12345) == b"unknown status"
+
+
+# fake, aligned, never dereferenced addresses: each call below must fail validation first
+P = [0x100000 * (i + 1) for i in range(8)]
+
+
+def born(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=1, eps=0.0, row_den=None):
+    q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
+    return cattn.lib().cattn_born_fwd(layout, *q, B, H, T, d, causal, eps, row_den, None)
+
+
+def pct(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0):
+    q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
+    return cattn.lib().cattn_pct_fwd(layout, *q, B, H, T, d, causal, bias, None)
+
+
+def test_bad_layout():
+    assert born(layout=7) == 3
+    assert pct(layout=-1) == 3
+
+
+def test_bad_sizes():
+    assert born(B=-1) == 2
+    assert born(T=-5) == 2
+    assert born(d=0) == 6
+    assert born(d=129) == 6
+    assert pct(d=1000) == 6
+    assert born(T=2 ** 40) == 2
+    assert born(B=2 ** 20, H=2 ** 20, T=2 ** 20) == 2
+
+
+def test_empty_problem_is_ok_and_launches_nothing():
+    # B, H or T equal to 0: OK, and pointers may even be NULL
+    assert born(ptrs=[None] * 8, B=0) == 0
+    assert pct(ptrs=[None] * 8, T=0) == 0
+    assert born(ptrs=[None] * 8, H=0, layout=1) == 0
+
+
+def test_null_pointers():
+    assert born(ptrs=[None, None, P[1], None, P[2], None, P[3], None]) == 1
+    assert born(ptrs=[P[0], None, P[1], None, P[2], None, None, None]) == 1
+    # C64 must not carry imaginary-plane pointers
+    assert born(ptrs=[P[0], P[4], P[1], None, P[2], None, P[3], None]) == 1
+    # bf16 needs both planes
+    assert born(layout=1, ptrs=[P[0], None, P[1], P[5], P[2], P[6], P[3], P[7]]) == 1
+
+
+def test_alignment():
+    assert born(ptrs=[P[0] + 8, None, P[1], None, P[2], None, P[3], None]) == 4
+    assert pct(layout=1, ptrs=[P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7] + 2]) == 4
+    assert born(row_den=P[7] + 4) == 4
+
+
+def test_aliasing():
+    # O overlapping Q
+    assert born(ptrs=[P[0], None, P[1], None, P[2], None, P[0] + 16, None]) == 5
+    # bf16: O real and imaginary planes overlapping each other
+    assert born(layout=1, ptrs=[P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[6] + 16]) == 5
+    # row_den overlapping O
+    assert born(row_den=P[3]) == 5
+
+
+def test_bad_scalars():
+    assert born(eps=-1.0) == 8
+    assert born(eps=float("nan")) == 8
+    assert born(eps=float("inf")) == 8
+    assert pct(bias=float("nan")) == 8
+    assert pct(bias=float("-inf")) == 8
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 4, dtype=torch.complex64)
+    with pytest.raises(ValueError):
+        cattn.born_fwd(x, x, x)            # host tensors are refused before any call
+    with pytest.raises(TypeError):
+        cattn.born_fwd(x.real, x.real, x.real)
