@@ -1,0 +1,174 @@
+"""Benchmark: Born-rule attention forward, B8 H16 T4096 d_h 64, bf16 real/imag planes.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one call of the fused forward (score GEMM, weight map, Born
+denominator, value GEMM, epilogue: the whole hot path, one kernel launch)
+over one batch of synthetic inputs already resident in HBM.  Prints ONE JSON
+line on stdout: the throughput in real TFLOP/s (8 T^2 d_h for S plus
+4 T^2 d_h for W V per head, halved for causal attention), the roofline of
+the kernel measured with HIP events on the launch stream, parity on sampled
+rows against the fp64 oracle, and the oracle itself timed on a bounded sample
+on the host cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Born-attn fwd real TFLOP/s (B8 H16 T4096 d64) + % MFMA peak"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "c64": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(w) -> float:
+    """Flops the method needs: Born 12 d_h per (query, key) pair, PCT 8 d_h (only Re S)."""
+    from complex_valued_attention_amd.inputs import attention_flops
+    f = attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
+    return f if w.op == "born" else f * 8.0 / 12.0
+
+
+def run_gpu(w, steps: int, warmup: int):
+    import torch
+    from complex_valued_attention_amd import cattn, inputs as gen
+    from complex_valued_attention_amd.check import from_device, to_device
+
+    cattn.lib()  # fails loudly if the HIP library is not built
+    t0 = time.time()
+    inp = gen.make_inputs(w)
+    log(f"[bench] inputs {w.name}: {time.time() - t0:.1f} s")
+    q, k, v = to_device(inp)
+    if w.layout == "c64":
+        out = torch.empty_like(q)
+    else:
+        out = (torch.empty_like(q[0]), torch.empty_like(q[0]))
+    fn = cattn.born_fwd if w.op == "born" else cattn.pct_fwd
+
+    def step():
+        fn(q, k, v, causal=w.causal, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    return inp, from_device(out), total_ms / steps, per, wall_ms
+
+
+def parity(w, inp, got, n=64):
+    import oracle
+    from complex_valued_attention_amd.check import TOL, rowwise_rel_err, sample_rows
+    rows = sample_rows(w.B, w.H, w.T, n, seed=123)
+    fn = oracle.born_attention_rows if w.op == "born" else oracle.pct_attention_rows
+    ref = fn(inp.q64, inp.k64, inp.v64, rows, causal=w.causal)
+    err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
+    return {"rowwise_rel_err": err, "tol": TOL[w.layout], "rows_checked": int(len(rows)),
+            "pass": bool(err <= TOL[w.layout])}
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0):
+    """The fp64 oracle on whole heads of the same inputs, as many heads as fit the budget."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from complex_valued_attention_amd.inputs import attention_flops
+
+    fn = oracle.born_attention if w.op == "born" else oracle.pct_attention
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_used = 0, 0.0
+    for b, h in heads:
+        t0 = time.perf_counter()
+        fn(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], causal=w.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    flops = attention_flops(w.T, w.d_h, w.causal, done)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads (full T={w.T} each), fp64 numpy, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from complex_valued_attention_amd import inputs as gen
+    name = args.workload or gen.BENCH_WORKLOAD
+    w = gen.WORKLOADS[name]
+
+    inp, got, ms, per, wall_ms = run_gpu(w, args.steps, args.warmup)
+    flops = gen.attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
+    alg = algorithmic_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.layout]
+    kernel_ms = float(np.mean(per))
+    achieved = alg / (kernel_ms * 1e-3) / 1e12
+    log(f"[bench] {name}: {ms:.4f} ms/step (median launch {np.median(per):.4f} ms, wall {wall_ms / args.steps:.4f} "
+        f"ms/step), {tflops:.1f} TFLOP/s")
+
+    rec = {
+        "metric": METRIC if name == gen.BENCH_WORKLOAD else f"{w.op} fwd real TFLOP/s ({name})",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.layout == "bf16" else "f32",
+        "data": "synthetic (seeded complex Gaussian, unit-norm rotary Q/K)" if w.rotary else "synthetic",
+        "config": {"workload": name, "op": w.op, "causal": w.causal, "B": w.B, "H": w.H, "T": w.T,
+                   "d_h": w.d_h, "layout": w.layout, "seed": w.seed},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "born_bf16_mfma_kernel" if (w.op == "born" and w.layout == "bf16") else "f32 path",
+                     "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per))},
+    }
+    if not args.no_parity:
+        rec["parity"] = parity(w, inp, got)
+        log(f"[bench] parity {rec['parity']}")
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp)
+        log(f"[bench] cpu baseline {rec['cpu_baseline']}")
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
