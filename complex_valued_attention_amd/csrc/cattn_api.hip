@@ -1,6 +1,6 @@
 // C-ABI entry points: argument validation (no HIP call before it passes),
 // kernel selection, launch.
-#include "../../include/cattn.h"
+#include "cattn.h"
 #include "cattn_internal.h"
 
 #include <math.h>

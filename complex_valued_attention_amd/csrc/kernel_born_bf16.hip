@@ -35,10 +35,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BN = 64;   // keys per LDS stage (two 32-key sub-blocks)
 constexpr int PAD = 8;   // bf16 padding per LDS row (16 bytes): conflict-free 16-byte lane reads
 
-template <int D, int NQT, int NW>
+template <int D, int NQT, int NW, int BN>
 struct BornCfg {
     static constexpr int KD = 2 * D;             // real contraction width of S
     static constexpr int KSTEPS = KD / 16;       // MFMA k-steps for S
@@ -75,9 +74,9 @@ __device__ inline int vt_key_of_pos(int pos) {   // pos in 0..31 -> key in 0..31
     return 16 * m + 8 * (s >> 2) + 4 * h + (s & 3);
 }
 
-template <int D, int NQT, int NW>
+template <int D, int NQT, int NW, int BN>
 __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int nrb) {
-    using C = BornCfg<D, NQT, NW>;
+    using C = BornCfg<D, NQT, NW, BN>;
     extern __shared__ __align__(16) __bf16 smem[];
 
     const int tid = threadIdx.x;
@@ -323,10 +322,10 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
     }
 }
 
-template <int D, int NQT, int NW>
+template <int D, int NQT, int NW, int BN>
 hipError_t launch_cfg(const Problem &p) {
-    using C = BornCfg<D, NQT, NW>;
-    auto kern = born_bf16_mfma_kernel<D, NQT, NW>;
+    using C = BornCfg<D, NQT, NW, BN>;
+    auto kern = born_bf16_mfma_kernel<D, NQT, NW, BN>;
     static bool attr_done = false;   // set once per process; idempotent
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -349,10 +348,10 @@ bool supports_born_bf16_mfma(const Problem &p) {
 
 hipError_t launch_born_bf16_mfma(const Problem &p) {
     switch (p.d) {
-        case 16: return launch_cfg<16, 1, 8>(p);
-        case 32: return launch_cfg<32, 1, 8>(p);
-        case 64: return launch_cfg<64, 1, 8>(p);
-        case 128: return launch_cfg<128, 1, 4>(p);
+        case 16: return launch_cfg<16, 1, 8, 64>(p);
+        case 32: return launch_cfg<32, 1, 8, 64>(p);
+        case 64: return launch_cfg<64, 1, 8, 64>(p);
+        case 128: return launch_cfg<128, 1, 4, 64>(p);
         default: return hipErrorNotSupported;
     }
 }
