@@ -201,6 +201,21 @@ def test_exhaustive_small_gaussian_integers():
     assert n == 600
 
 
+def test_real_inputs_match_library_polynomial_kernel():
+    # real Q, K: |<q,k>|^2 is the degree-2 homogeneous polynomial kernel (q.k)^2 of scikit-learn
+    from sklearn.metrics.pairwise import polynomial_kernel
+    rng = np.random.default_rng(12)
+    T, d = 20, 6
+    q, k = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    v = crandn(rng, T, d)
+    s = polynomial_kernel(q, k, degree=2, gamma=1.0, coef0=0.0)
+    for causal in (True, False):
+        w = np.tril(s) if causal else s
+        want = (w @ v) / w.sum(1, keepdims=True)
+        np.testing.assert_allclose(born_attention(q.astype(complex), k.astype(complex), v, causal=causal), want,
+                                   rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _mutants():

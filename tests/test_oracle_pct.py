@@ -117,6 +117,9 @@ def test_real_inputs_give_cosine_similarity():
     q, k = rng.standard_normal((10, d)), rng.standard_normal((12, d))
     cos = (q / np.linalg.norm(q, axis=1, keepdims=True)) @ (k / np.linalg.norm(k, axis=1, keepdims=True)).T
     np.testing.assert_allclose(pct_scores(q.astype(complex), k.astype(complex)), 4.0 * cos, rtol=1e-12)
+    from sklearn.metrics.pairwise import cosine_similarity
+    np.testing.assert_allclose(pct_scores(q.astype(complex), k.astype(complex)), 4.0 * cosine_similarity(q, k),
+                               rtol=1e-12, atol=1e-14)
 
 
 def test_rows_match_full():
