@@ -86,7 +86,9 @@ cattn_status validate(int op, int layout, const void *q_re, const void *q_im, co
 
 cattn_status run(const Problem &p) {
     hipError_t e;
-    if (cattn::supports_born_bf16_mfma(p))
+    if (cattn::supports_born_bf16_d64(p))
+        e = cattn::launch_born_bf16_d64(p);
+    else if (cattn::supports_born_bf16_mfma(p))
         e = cattn::launch_born_bf16_mfma(p);
     else if (cattn::supports_f32_mfma(p))
         e = cattn::launch_f32_mfma(p);

@@ -30,6 +30,9 @@ struct Problem {
 // status.  `supports_*` say whether a specialised kernel covers `p`.
 hipError_t launch_generic(const Problem &p);
 
+bool supports_born_bf16_d64(const Problem &p);
+hipError_t launch_born_bf16_d64(const Problem &p);
+
 bool supports_born_bf16_mfma(const Problem &p);
 hipError_t launch_born_bf16_mfma(const Problem &p);
 
