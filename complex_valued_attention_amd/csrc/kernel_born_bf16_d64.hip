@@ -22,8 +22,13 @@
 // rows of 128 bytes = eight 16-byte chunks, chunk c of row r stored at slot
 // c ^ swz(r).  The K swizzle spreads the 32 rows read by one A operand fetch
 // over all banks; the V swizzle does the same for the 4-key x 2-chunk
-// footprint of a transposing read.  Stages are double-buffered: the global
-// loads of stage s + 1 sit in registers while stage s is multiplied.
+// footprint of a transposing read.  Stages go from global memory straight
+// into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at base +
+// 16 * lane, so the swizzle is applied by choosing which chunk a lane fetches),
+// into two stage buffers that alternate: the loads of stage s + 1 are in
+// flight while stage s is multiplied.  The two buffers are separate LDS
+// variables, which lets the compiler see that the transposing reads of one
+// never alias the loads into the other.
 //
 // Work split.  A workgroup of NW waves (two per SIMD) covers row blocks of
 // 32 NW queries of one (batch, head), one 32-query tile per wave.  For causal
@@ -38,6 +43,7 @@
 #define CATTN_D64_WAVES 8
 #endif
 
+
 namespace cattn {
 namespace {
 
@@ -50,6 +56,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
 
 constexpr int D = 64;
 constexpr int NW = CATTN_D64_WAVES;   // waves per workgroup (4 or 8)
@@ -59,9 +66,9 @@ constexpr int BN = 64;                // keys per stage
 constexpr int ROWB = 2 * D;           // bytes per row of one plane region
 constexpr int REGION = BN * ROWB;     // 8 KiB
 constexpr int STAGE = 4 * REGION;     // Re K, Im K, Re V, Im V
-constexpr int LDS_BYTES = 2 * STAGE;  // double-buffered
+constexpr int NSB = BN / 32;          // 32-key blocks per stage
 constexpr int RPT = REGION / 16 / NT; // 16-byte chunks per thread per region per stage
-constexpr int CHUNKS_PER_T = 4 * RPT;
+constexpr int LOADS_PER_T = 4 * RPT;  // LDS-direct loads per thread per stage
 constexpr int WAVES_PER_SIMD = 2;     // 8 waves: one workgroup per CU; 4 waves: two
 static_assert(RPT * 16 * NT == REGION, "staging split");
 static_assert(NW == 4 || NW == 8, "workgroup size");
@@ -81,13 +88,23 @@ __device__ inline u32x2 ds_read_tr(const char *p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// All of this wave's LDS-direct loads have landed; then workgroup barrier.  A
+// bare s_barrier is used (the fence of __syncthreads adds nothing here).
+__device__ inline void loads_done_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
-    extern __shared__ __align__(16) char smem[];
+    __shared__ __align__(16) char stage_a[STAGE];   // even stages
+    __shared__ __align__(16) char stage_b[STAGE];   // odd stages
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -119,33 +136,26 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + head;
     uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + head;
 
-    // ---- staging: thread t moves chunk (row, slot) of every region --------
+    // ---- staging: global -> LDS, no registers ------------------------------
     // Within a region, chunk id = NT e + t (e < RPT) covers row id / 8 and
-    // physical slot t % 8, and holds logical chunk slot ^ swz(row) of that
-    // key row.
+    // physical slot t % 8, and receives logical chunk slot ^ swz(row) of that
+    // key row.  A wave's 64 chunks of one (region, e) are 1 KiB of LDS.
     const int srow = tid >> 3;
     const int sslot = tid & 7;
     const int lck = sslot ^ swz_k(srow);   // swizzles depend on row % 16 only
     const int lcv = sslot ^ swz_v(srow);
-    u32x4 stg[CHUNKS_PER_T];
 
-    auto load_stage = [&](int k0) {
+    auto issue_stage = [&](int k0, char *buf) {
         const bool tail = k0 + BN > T;
+        char *dst = buf + wave * 1024;
 #pragma unroll
-        for (int i = 0; i < CHUNKS_PER_T; ++i) {
+        for (int i = 0; i < LOADS_PER_T; ++i) {
             const int g = i / RPT, e = i % RPT;
             int row = k0 + srow + (NT / 8) * e;
             if (tail) row = min(row, T - 1);   // rows past T are masked out of the weights
             const int lc = g < 2 ? lck : lcv;
-            stg[i] = *reinterpret_cast<const u32x4 *>(planes[g] + (int64_t)row * D + 8 * lc);
-        }
-    };
-    auto store_stage = [&](int buf) {
-        char *base = smem + buf * STAGE + tid * 16;
-#pragma unroll
-        for (int i = 0; i < CHUNKS_PER_T; ++i) {
-            const int g = i / RPT, e = i % RPT;
-            *reinterpret_cast<u32x4 *>(base + g * REGION + e * (NT * 16)) = stg[i];
+            __builtin_amdgcn_global_load_lds((GLB_AS void *)(planes[g] + (int64_t)row * D + 8 * lc),
+                                             (LDS_AS void *)(dst + g * REGION + e * (NT * 16)), 16, 0, 0);
         }
     };
 
@@ -239,33 +249,36 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         const int kend = p.causal ? min(T, m0 + BM) : T;
         const int nstages = (kend + BN - 1) / BN;
 
-        __syncthreads();   // the previous row block is done with the LDS
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-
         const bool wave_live = qt0 < T;
-        for (int s = 0; s < nstages; ++s) {
-            const int k0 = s * BN;
-            const char *st = smem + (s & 1) * STAGE;
-            if (s + 1 < nstages) load_stage(k0 + BN);
-
-            if (wave_live) {
+        auto compute_stage = [&](int k0, const char *st) {
+            if (!wave_live) return;
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    const int kb0 = k0 + 32 * sb;
-                    const bool skip = kb0 >= T || (p.causal && kb0 > qt0);
-                    const bool full = (!p.causal || kb0 + 32 <= qt0) && kb0 + 32 <= T;
-                    if (full) {
-                        key_block(st, sb, false, 31);
-                    } else if (!skip) {
-                        key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0));
-                    }
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int kb0 = k0 + 32 * sb;
+                const bool skip = kb0 >= T || (p.causal && kb0 > qt0);
+                const bool full = (!p.causal || kb0 + 32 <= qt0) && kb0 + 32 <= T;
+                if (full) {
+                    key_block(st, sb, false, 31);
+                } else if (!skip) {
+                    key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0));
                 }
             }
+        };
 
-            if (s + 1 < nstages) store_stage((s + 1) & 1);
-            __syncthreads();
+        // Stage s lives in stage_a (s even) or stage_b (s odd).  At the top of
+        // stage s its loads have landed for every wave (barrier), and every
+        // wave is done reading the other buffer, which then takes stage s + 1.
+        loads_done_barrier();   // the previous row block is done with both buffers
+        issue_stage(0, stage_a);
+        for (int s = 0; s < nstages; s += 2) {
+            loads_done_barrier();
+            if (s + 1 < nstages) issue_stage((s + 1) * BN, stage_b);
+            compute_stage(s * BN, stage_a);
+            if (s + 1 < nstages) {
+                loads_done_barrier();
+                if (s + 2 < nstages) issue_stage((s + 2) * BN, stage_a);
+                compute_stage((s + 1) * BN, stage_b);
+            }
         }
 
         // ---- epilogue: O = acc / (sum w + eps), bf16 planes ----------------
@@ -295,18 +308,11 @@ bool supports_born_bf16_d64(const Problem &p) {
 }
 
 hipError_t launch_born_bf16_d64(const Problem &p) {
-    static bool attr_done = false;   // set once per process; idempotent
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(born_bf16_d64_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
     const int nrb = (p.T + BM - 1) / BM;
     const int nwork = p.causal ? (nrb + 1) / 2 : nrb;   // causal: mirrored pairs of row blocks
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_bf16_d64_kernel, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, p.stream, p, nrb, nwork);
+    hipLaunchKernelGGL(born_bf16_d64_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nrb, nwork);
     return hipGetLastError();
 }
 
