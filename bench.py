@@ -30,6 +30,29 @@ METRIC = "Born-attn fwd real TFLOP/s (B8 H16 T4096 d64) + % MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "c64": 157.3}
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 passes
+# (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for the
+# --copy-probe kernel.  Valid only for the kernel source it was measured on:
+# any other source gives traffic = null.
+MEASURED_TRAFFIC = {
+    "born_causal_bf16_b8h16t4096d64_rotary": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_d64.hip",
+        "sha256": "1ea06ab789c9db176c51489e8839f1ee6cad3e1863445d4fac4248dcb78e7f02",
+        "bytes": 882.4e6,   # read 748.1 MB + write 134.2 MB
+    },
+}
+
+
+def measured_traffic(name: str):
+    import hashlib
+    m = MEASURED_TRAFFIC.get(name)
+    if m is None:
+        return None
+    with open(os.path.join(ROOT, m["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m["sha256"]:
+            return None
+    return m["bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -40,6 +63,15 @@ def algorithmic_flops(w) -> float:
     from complex_valued_attention_amd.inputs import attention_flops
     f = attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
     return f if w.op == "born" else f * 8.0 / 12.0
+
+
+def kernel_name(w) -> str:
+    """The HIP kernel the library dispatches for this workload."""
+    if w.op == "born" and w.layout == "bf16":
+        return "born_bf16_d64_kernel" if w.d_h == 64 else "born_bf16_mfma_kernel"
+    if w.layout == "c64" and w.d_h in (16, 32, 64):
+        return "attn_f32_mfma_kernel"
+    return "generic_fwd_kernel"
 
 
 def run_gpu(w, steps: int, warmup: int):
@@ -155,8 +187,8 @@ def main():
         "config": {"workload": name, "op": w.op, "causal": w.causal, "B": w.B, "H": w.H, "T": w.T,
                    "d_h": w.d_h, "layout": w.layout, "seed": w.seed},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "kernel": "born_bf16_mfma_kernel" if (w.op == "born" and w.layout == "bf16") else "f32 path",
+                     "frac": achieved / peak, "traffic": measured_traffic(name),
+                     "kernel": kernel_name(w),
                      "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per))},
     }
     if not args.no_cpu_baseline:

@@ -30,8 +30,8 @@
 // variables, which lets the compiler see that the transposing reads of one
 // never alias the loads into the other.
 //
-// Work split.  A workgroup of NW waves (two per SIMD) covers row blocks of
-// 32 NW queries of one (batch, head), one 32-query tile per wave.  For causal
+// Work split.  A workgroup of 8 waves (two per SIMD) covers row blocks of
+// 256 queries of one (batch, head), one 32-query tile per wave.  For causal
 // attention a workgroup takes the mirrored pair of row blocks nrb-1-i and i,
 // so every workgroup carries the same number of key blocks and the grid
 // drains evenly.  Key blocks of 32 strictly below a tile's diagonal take a
@@ -39,9 +39,6 @@
 // masked; blocks above the diagonal are skipped.
 #include "cattn_internal.h"
 
-#ifndef CATTN_D64_WAVES
-#define CATTN_D64_WAVES 8
-#endif
 
 
 namespace cattn {
@@ -59,7 +56,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define GLB_AS __attribute__((address_space(1)))
 
 constexpr int D = 64;
-constexpr int NW = CATTN_D64_WAVES;   // waves per workgroup (4 or 8)
+constexpr int NW = 8;                 // waves per workgroup, two per SIMD
 constexpr int NT = 64 * NW;
 constexpr int BM = 32 * NW;           // query rows per row block
 constexpr int BN = 64;                // keys per stage
@@ -69,9 +66,7 @@ constexpr int STAGE = 4 * REGION;     // Re K, Im K, Re V, Im V
 constexpr int NSB = BN / 32;          // 32-key blocks per stage
 constexpr int RPT = REGION / 16 / NT; // 16-byte chunks per thread per region per stage
 constexpr int LOADS_PER_T = 4 * RPT;  // LDS-direct loads per thread per stage
-constexpr int WAVES_PER_SIMD = 2;     // 8 waves: one workgroup per CU; 4 waves: two
 static_assert(RPT * 16 * NT == REGION, "staging split");
-static_assert(NW == 4 || NW == 8, "workgroup size");
 
 __device__ inline int swz_k(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
@@ -101,7 +96,7 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     __shared__ __align__(16) char stage_a[STAGE];   // even stages
     __shared__ __align__(16) char stage_b[STAGE];   // odd stages
@@ -179,45 +174,53 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
-    for (int blk = 0; blk < nblocks; ++blk) {
-        const int rb = p.causal ? (blk == 0 ? nrb - 1 - item : item) : item;
-        const int m0 = rb * BM;
-        const int qt0 = m0 + 32 * wave;   // first query of this wave's tile
+    auto row_block = [&](int blk) { return p.causal ? (blk == 0 ? nrb - 1 - item : item) : item; };
+    auto tile_of = [&](int blk) { return row_block(blk) * BM + 32 * wave; };   // this wave's first query
 
-        // Q operands (B operand of the score products): k-step kk, lane
-        // (query l32, half h) holds Q'[q][16 kk + 8 h .. + 8].
-        bf16x8 qb[8];
-        bf16x8 qneg[4];   // -Re Q chunks: second half of [Im Q | -Re Q]
-        {
-            const int q = qt0 + l32;
+    // Q operands (B operand of the score products): k-step kk, lane
+    // (query l32, half h) holds Q'[q][16 kk + 8 h .. + 8].
+    bf16x8 qb[8];
+    bf16x8 qneg[4];   // -Re Q chunks: second half of [Im Q | -Re Q]
+    auto load_q = [&](int qt0) {
+        const int q = qt0 + l32;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (q < T) {
-                    const uint16_t *src = (kk < 4 ? qre : qim) + (int64_t)q * D + 16 * (kk & 3) + 8 * h;
-                    x = *reinterpret_cast<const u32x4 *>(src);
-                }
-                qb[kk] = as_bf16x8(x);
-                if (kk < 4) qneg[kk] = as_bf16x8(x ^ 0x80008000u);
+        for (int kk = 0; kk < 8; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (q < T) {
+                const uint16_t *src = (kk < 4 ? qre : qim) + (int64_t)q * D + 16 * (kk & 3) + 8 * h;
+                x = *reinterpret_cast<const u32x4 *>(src);
             }
+            qb[kk] = as_bf16x8(x);
+            if (kk < 4) qneg[kk] = as_bf16x8(x ^ 0x80008000u);
         }
+    };
+    load_q(tile_of(0));
+    bool stage0_issued = false;   // the next row block's first stage is already in flight
+
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const int rb = row_block(blk);
+        const int m0 = rb * BM;
+        const int qt0 = tile_of(blk);   // first query of this wave's tile
 
         f32x16 oacc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) oacc[c] = f32x16{};
         float rsum = 0.f;
 
-        // One 32-key block at LDS stage `st`, block `sb` within it.  MASKED
-        // zeroes keys past `lim` (per lane): the causal diagonal, a ragged tail.
-        auto key_block = [&](const char *st, int sb, bool masked, int lim) {
-            f32x16 sr = f32x16{}, si = f32x16{};
+        // Scores S^T of 32-key block sb of LDS stage st
+        auto scores = [&](const char *st, int sb, f32x16 &sr, f32x16 &si) {
+            sr = f32x16{};
+            si = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + (kk >> 2) * REGION + sb * 32 * ROWB + koff[kk & 3]);
                 sr = mfma(a, qb[kk], sr);
                 si = mfma(a, kk < 4 ? qb[kk + 4] : qneg[kk - 4], si);
             }
-            // w = |S|^2 packed to bf16; register r of lane half h is key 8 (r/4) + 4 h + r % 4
+        };
+        // w = |S|^2 packed to bf16; register r of lane half h is key 8 (r/4) + 4 h + r % 4.
+        // MASKED zeroes keys past `lim` (per lane): the causal diagonal, a ragged tail.
+        auto weights = [&](const f32x16 &sr, const f32x16 &si, bf16x8 (&wop)[2], bool masked, int lim) {
             uint32_t pk[8];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
@@ -231,9 +234,11 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
                 pk[r >> 1] = pack_bf16x2(w0, w1);
                 rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]), ones, rsum, false);
             }
-            const bf16x8 wop[2] = {as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]}),
-                                   as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]})};
-            // O^T += V'^T W^T
+            wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+            wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+        };
+        // O^T += V'^T W^T for block sb
+        auto values = [&](const char *st, int sb, const bf16x8 (&wop)[2]) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -244,6 +249,13 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
                     oacc[c] = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), wop[m], oacc[c]);
                 }
             }
+        };
+        auto key_block = [&](const char *st, int sb, bool masked, int lim) {
+            f32x16 sr, si;
+            bf16x8 wop[2];
+            scores(st, sb, sr, si);
+            weights(sr, si, wop, masked, lim);
+            values(st, sb, wop);
         };
 
         const int kend = p.causal ? min(T, m0 + BM) : T;
@@ -268,18 +280,28 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         // Stage s lives in stage_a (s even) or stage_b (s odd).  At the top of
         // stage s its loads have landed for every wave (barrier), and every
         // wave is done reading the other buffer, which then takes stage s + 1.
-        loads_done_barrier();   // the previous row block is done with both buffers
-        issue_stage(0, stage_a);
+        if (!stage0_issued) {
+            loads_done_barrier();   // the previous row block is done with both buffers
+            issue_stage(0, stage_a);
+        }
+        // with an even stage count the last stage sits in stage_b; from its top
+        // on stage_a is free and takes the next row block's first stage
+        const bool prefetch_next = blk + 1 < nblocks && (nstages & 1) == 0;
         for (int s = 0; s < nstages; s += 2) {
             loads_done_barrier();
             if (s + 1 < nstages) issue_stage((s + 1) * BN, stage_b);
             compute_stage(s * BN, stage_a);
             if (s + 1 < nstages) {
                 loads_done_barrier();
-                if (s + 2 < nstages) issue_stage((s + 2) * BN, stage_a);
+                if (s + 2 < nstages)
+                    issue_stage((s + 2) * BN, stage_a);
+                else if (prefetch_next)
+                    issue_stage(0, stage_a);
                 compute_stage((s + 1) * BN, stage_b);
             }
         }
+        stage0_issued = prefetch_next;
+        if (blk + 1 < nblocks) load_q(tile_of(blk + 1));   // in flight during the epilogue
 
         // ---- epilogue: O = acc / (sum w + eps), bf16 planes ----------------
         const float den = rsum + __shfl_xor(rsum, 32) + p.eps;   // both lane halves hold this query
