@@ -16,6 +16,10 @@ to fp64) and computes the plain definitions in complex128:
   Shortcut", section 2, the Born rule as a linear functional of the density
   matrix; "Show HN: CNET", BornAttention, its exact finite feature map).  It is
   used only to pin :mod:`oracle.born`.
+* :mod:`oracle.born_grad`, :mod:`oracle.pct_grad` -- the backward of both
+  operators in closed form (gradients dL/d(conj z) as in "CNet ...", section 3,
+  rule (2)), derived from the forward definitions and pinned by finite
+  differences.
 
 Every function here is pinned by the CPU tests against closed forms,
 invariants, hand-derived worked examples and the second formulation.
@@ -23,9 +27,12 @@ invariants, hand-derived worked examples and the second formulation.
 from .born import born_attention, born_attention_rows
 from .pct import pct_attention, pct_attention_rows, pct_scores
 from .born_density import born_attention_density
+from .born_grad import born_attention_bwd
+from .pct_grad import pct_attention_bwd
 
 __all__ = [
     "born_attention", "born_attention_rows",
     "pct_attention", "pct_attention_rows", "pct_scores",
     "born_attention_density",
+    "born_attention_bwd", "pct_attention_bwd",
 ]
