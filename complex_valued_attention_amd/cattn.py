@@ -1,6 +1,6 @@
 """Python binding of libcattn (ctypes): argument marshalling only.
 
-Every step of the forward runs in the HIP kernels behind the C ABI
+Every step of the forward and backward runs in the HIP kernels behind the C ABI
 (``include/cattn.h``); PyTorch provides device memory and the current stream.
 There is no fallback: if the library is not built, calls raise.
 
@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
     L.cattn_pct_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                 ctypes.c_int, ctypes.c_float, vp]
     L.cattn_pct_fwd.restype = ctypes.c_int
+    L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
+    L.cattn_born_bwd.restype = ctypes.c_int
+    L.cattn_pct_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [vp] * 6 + [i64] * 4 +
+                                [ctypes.c_int, ctypes.c_float, vp, vp])
+    L.cattn_pct_bwd.restype = ctypes.c_int
     L.cattn_status_str.argtypes = [ctypes.c_int]
     L.cattn_status_str.restype = ctypes.c_char_p
     L.cattn_abi_version.argtypes = []
@@ -136,6 +141,64 @@ def pct_fwd(q, k, v, causal: bool = False, bias: float = 0.0, out=None):
                             float(bias), _stream(ts[0]))
     _check(s)
     return out
+
+
+def _like(x):
+    import torch
+    if isinstance(x, (tuple, list)):
+        return (torch.empty_like(x[0]), torch.empty_like(x[1]))
+    return torch.empty_like(x)
+
+
+def _same(x, ref, name):
+    """(re, im) pointers of x after checking it matches ref's layout and shape."""
+    lx, re, im, sx = _unpack(x, name)
+    lr, _, _, sr = _unpack(ref, "q")
+    if lx != lr or sx != sr:
+        raise ValueError(f"{name} must match q's layout and shape")
+    return re, im
+
+
+def _bwd_outs(q, grads):
+    if grads is None:
+        grads = (_like(q), _like(q), _like(q))
+    dq, dk, dv = grads
+    return grads, [t for g, n in zip((dq, dk, dv), ("dq", "dk", "dv")) for t in _same(g, q, n)]
+
+
+def born_bwd(q, k, v, o, g, row_den, causal: bool = True, grads=None):
+    """Born-rule attention backward (cattn_born_bwd).
+
+    ``o`` and ``row_den`` come from the forward (``born_fwd(..., row_den=...)``);
+    ``g`` is dL/d(conj O) (or the real-pair gradient, which gives real-pair
+    gradients back).  Returns ``(dq, dk, dv)`` in the inputs' layout.
+    """
+    layout, ts, (B, H, T, d), _ = _prepare(q, k, v, _like(q))
+    ore, oim = _same(o, q, "o")
+    gre, gim = _same(g, q, "g")
+    if row_den is None or row_den.numel() != B * H * T or not row_den.is_contiguous():
+        raise ValueError("row_den must be the forward's contiguous float32 tensor of B*H*T elements")
+    grads, outs = _bwd_outs(q, grads)
+    s = lib().cattn_born_bwd(layout, *[_ptr(t) for t in ts[:6]], _ptr(ore), _ptr(oim), _ptr(gre), _ptr(gim),
+                             _ptr(row_den), *[_ptr(t) for t in outs], B, H, T, d, int(bool(causal)),
+                             _stream(ts[0]))
+    _check(s)
+    return grads
+
+
+def pct_bwd(q, k, v, g, causal: bool = False, bias: float = 0.0, grads=None, db_rows=None):
+    """Phase-coherent attention backward (cattn_pct_bwd).  Returns ``(dq, dk, dv)``;
+    ``db_rows`` (optional float32 [B*H*T]) receives the per-row bias gradient."""
+    layout, ts, (B, H, T, d), _ = _prepare(q, k, v, _like(q))
+    gre, gim = _same(g, q, "g")
+    if db_rows is not None and (db_rows.numel() != B * H * T or not db_rows.is_contiguous()):
+        raise ValueError("db_rows must be a contiguous float32 tensor of B*H*T elements")
+    grads, outs = _bwd_outs(q, grads)
+    s = lib().cattn_pct_bwd(layout, *[_ptr(t) for t in ts[:6]], _ptr(gre), _ptr(gim),
+                            *[_ptr(t) for t in outs], B, H, T, d, int(bool(causal)), float(bias),
+                            _ptr(db_rows), _stream(ts[0]))
+    _check(s)
+    return grads
 
 
 def default_pct_bias(T: int) -> float:

@@ -15,13 +15,24 @@ from .inputs import Inputs, bf16_bits_to_f64
 
 # Parity bars: fp32 arithmetic on complex64 inputs, bf16 products with fp32 accumulation.
 TOL = {"c64": 1e-4, "bf16": 2e-2}
+# Row-scale floor for gradient comparisons (fraction of the tensor's largest row scale).
+GRAD_FLOOR = 1e-3
 
 
-def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+def rowwise_rel_err(got: np.ndarray, ref: np.ndarray, floor: float = 0.0) -> float:
+    """Max over rows of max |got - ref| / max |ref| in the row.
+
+    ``floor`` > 0 raises each row's scale to at least ``floor`` times the
+    largest row scale of the tensor.  Gradients use it: some of their rows are
+    exactly zero in exact arithmetic (Born's first causal row of dQ), and those
+    are judged on their absolute error at the tensor's scale.
+    """
     got = np.asarray(got, dtype=np.complex128).reshape(-1, ref.shape[-1])
     ref = np.asarray(ref, dtype=np.complex128).reshape(-1, ref.shape[-1])
     diff = np.abs(got - ref).max(axis=1)
     scale = np.abs(ref).max(axis=1)
+    if floor > 0.0 and scale.size:
+        scale = np.maximum(scale, floor * scale.max())
     if np.any(~np.isfinite(diff)):
         return float("inf")
     zero = scale == 0.0
@@ -40,6 +51,15 @@ def to_device(inp: Inputs, device="cuda"):
                      for p in ("re", "im"))
         out.append(pair)
     return tuple(out)
+
+
+def grad_to_device(g, device="cuda"):
+    """Upload an incoming gradient (``inputs.Grad``) in its layout."""
+    import torch
+    if g.layout == "c64":
+        return torch.from_numpy(g.dev["g"]).to(device)
+    return tuple(torch.from_numpy(g.dev[f"g_{p}"].view(np.int16)).to(device).view(torch.bfloat16)
+                 for p in ("re", "im"))
 
 
 def from_device(o) -> np.ndarray:

@@ -97,6 +97,91 @@ cattn_status run(const Problem &p) {
     return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
+// Validates a backward call and fills `p` (same rules as the forward: layout,
+// sizes, NULLs, 16-byte alignment, and no output overlapping an input or
+// another output).
+cattn_status validate_bwd(int op, int layout, const void *const in_re[5], const void *const in_im[5],
+                          const float *row_den, void *const out_re[3], void *const out_im[3], float *db_rows,
+                          int64_t B, int64_t H, int64_t T, int64_t d_h, int causal, float bias, void *stream,
+                          cattn::BwdProblem *p, bool *empty) {
+    // in: q, k, v, o (Born only), g
+    if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
+    if (op == cattn::OP_PCT && !isfinite(bias)) return CATTN_E_ARG;
+    if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
+    if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
+    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    const int64_t BH = B * H;
+    if (BH > INT32_MAX) return CATTN_E_SHAPE;
+    const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
+    if (BH != 0 && T > (int64_t)(INT64_MAX / 16) / BH / d_h / elem) return CATTN_E_SHAPE;
+    *empty = BH == 0 || T == 0;
+    if (*empty) return CATTN_OK;
+
+    const bool born = op == cattn::OP_BORN;
+    const bool c64 = layout == CATTN_LAYOUT_C64;
+    for (int i = 0; i < 5; ++i) {
+        if (i == 3 && !born) continue;   // PCT takes no O
+        if (!in_re[i] || (c64 ? in_im[i] != nullptr : in_im[i] == nullptr)) return CATTN_E_NULL;
+    }
+    for (int i = 0; i < 3; ++i)
+        if (!out_re[i] || (c64 ? out_im[i] != nullptr : out_im[i] == nullptr)) return CATTN_E_NULL;
+    if (born && !row_den) return CATTN_E_NULL;
+
+    for (int i = 0; i < 5; ++i)
+        if ((in_re[i] && !aligned16(in_re[i])) || (in_im[i] && !aligned16(in_im[i]))) return CATTN_E_ALIGN;
+    for (int i = 0; i < 3; ++i)
+        if (!aligned16(out_re[i]) || (out_im[i] && !aligned16(out_im[i]))) return CATTN_E_ALIGN;
+    if ((row_den && !aligned16(row_den)) || (db_rows && !aligned16(db_rows))) return CATTN_E_ALIGN;
+
+    const uintptr_t bytes = (uintptr_t)(BH * T * d_h * elem);
+    const uintptr_t rbytes = (uintptr_t)(BH * T * 4);
+    Span ins[11];
+    int ni = 0;
+    for (int i = 0; i < 5; ++i) {
+        if (in_re[i]) ins[ni++] = Span{(uintptr_t)in_re[i], (uintptr_t)in_re[i] + bytes};
+        if (in_im[i]) ins[ni++] = Span{(uintptr_t)in_im[i], (uintptr_t)in_im[i] + bytes};
+    }
+    if (row_den) ins[ni++] = Span{(uintptr_t)row_den, (uintptr_t)row_den + rbytes};
+    Span outs[7];
+    int no = 0;
+    for (int i = 0; i < 3; ++i) {
+        outs[no++] = Span{(uintptr_t)out_re[i], (uintptr_t)out_re[i] + bytes};
+        if (out_im[i]) outs[no++] = Span{(uintptr_t)out_im[i], (uintptr_t)out_im[i] + bytes};
+    }
+    if (db_rows) outs[no++] = Span{(uintptr_t)db_rows, (uintptr_t)db_rows + rbytes};
+    for (int a = 0; a < no; ++a) {
+        for (int b = 0; b < ni; ++b)
+            if (overlaps(outs[a], ins[b])) return CATTN_E_ALIAS;
+        for (int b = a + 1; b < no; ++b)
+            if (overlaps(outs[a], outs[b])) return CATTN_E_ALIAS;
+    }
+
+    p->op = op;
+    p->layout = c64 ? cattn::LAYOUT_C64 : cattn::LAYOUT_BF16;
+    p->q_re = in_re[0]; p->q_im = in_im[0];
+    p->k_re = in_re[1]; p->k_im = in_im[1];
+    p->v_re = in_re[2]; p->v_im = in_im[2];
+    p->o_re = in_re[3]; p->o_im = in_im[3];
+    p->g_re = in_re[4]; p->g_im = in_im[4];
+    p->row_den = row_den;
+    p->dq_re = out_re[0]; p->dq_im = out_im[0];
+    p->dk_re = out_re[1]; p->dk_im = out_im[1];
+    p->dv_re = out_re[2]; p->dv_im = out_im[2];
+    p->db_rows = db_rows;
+    p->BH = (int)BH;
+    p->T = (int)T;
+    p->d = (int)d_h;
+    p->causal = causal != 0;
+    p->bias = bias;
+    p->stream = reinterpret_cast<hipStream_t>(stream);
+    return CATTN_OK;
+}
+
+cattn_status run_bwd(const cattn::BwdProblem &p) {
+    const hipError_t e = cattn::launch_bwd_generic(p);
+    return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,6 +208,39 @@ cattn_status cattn_pct_fwd(int layout, const void *q_re, const void *q_im, const
     return run(p);
 }
 
+cattn_status cattn_born_bwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
+                            const void *v_re, const void *v_im, const void *o_re, const void *o_im,
+                            const void *g_re, const void *g_im, const float *row_den, void *dq_re, void *dq_im,
+                            void *dk_re, void *dk_im, void *dv_re, void *dv_im, int64_t B, int64_t H, int64_t T,
+                            int64_t d_h, int causal, void *stream) {
+    const void *const in_re[5] = {q_re, k_re, v_re, o_re, g_re};
+    const void *const in_im[5] = {q_im, k_im, v_im, o_im, g_im};
+    void *const out_re[3] = {dq_re, dk_re, dv_re};
+    void *const out_im[3] = {dq_im, dk_im, dv_im};
+    cattn::BwdProblem p{};
+    bool empty = false;
+    const cattn_status s = validate_bwd(cattn::OP_BORN, layout, in_re, in_im, row_den, out_re, out_im, nullptr, B,
+                                        H, T, d_h, causal, 0.f, stream, &p, &empty);
+    if (s != CATTN_OK || empty) return s;
+    return run_bwd(p);
+}
+
+cattn_status cattn_pct_bwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
+                           const void *v_re, const void *v_im, const void *g_re, const void *g_im, void *dq_re,
+                           void *dq_im, void *dk_re, void *dk_im, void *dv_re, void *dv_im, int64_t B, int64_t H,
+                           int64_t T, int64_t d_h, int causal, float bias, float *db_rows, void *stream) {
+    const void *const in_re[5] = {q_re, k_re, v_re, nullptr, g_re};
+    const void *const in_im[5] = {q_im, k_im, v_im, nullptr, g_im};
+    void *const out_re[3] = {dq_re, dk_re, dv_re};
+    void *const out_im[3] = {dq_im, dk_im, dv_im};
+    cattn::BwdProblem p{};
+    bool empty = false;
+    const cattn_status s = validate_bwd(cattn::OP_PCT, layout, in_re, in_im, nullptr, out_re, out_im, db_rows, B, H,
+                                        T, d_h, causal, bias, stream, &p, &empty);
+    if (s != CATTN_OK || empty) return s;
+    return run_bwd(p);
+}
+
 const char *cattn_status_str(int status) {
     switch (status) {
         case CATTN_OK: return "ok";
@@ -130,7 +248,7 @@ const char *cattn_status_str(int status) {
         case CATTN_E_SHAPE: return "negative or too large size";
         case CATTN_E_LAYOUT: return "unknown layout";
         case CATTN_E_ALIGN: return "pointer not 16-byte aligned";
-        case CATTN_E_ALIAS: return "output overlaps an input or another output";
+        case CATTN_E_ALIAS: return "an output overlaps an input or another output";
         case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128";
         case CATTN_E_LAUNCH: return "HIP kernel launch failed";
         case CATTN_E_ARG: return "eps negative or not finite, or bias not finite";
@@ -138,6 +256,6 @@ const char *cattn_status_str(int status) {
     }
 }
 
-int cattn_abi_version(void) { return 1; }
+int cattn_abi_version(void) { return 2; }
 
 }  // extern "C"

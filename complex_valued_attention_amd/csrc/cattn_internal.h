@@ -39,4 +39,25 @@ hipError_t launch_born_bf16_mfma(const Problem &p);
 bool supports_f32_mfma(const Problem &p);
 hipError_t launch_f32_mfma(const Problem &p);
 
+// One validated backward call (same [BH, T, d] layout).  G = dL/d(conj O);
+// the outputs are dL/d(conj q), dL/d(conj k), dL/d(conj v).
+struct BwdProblem {
+    int op;
+    int layout;
+    const void *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
+    const void *o_re, *o_im;     // Born: the forward output
+    const void *g_re, *g_im;     // incoming gradient
+    const float *row_den;        // Born: the forward's row denominators
+    void *dq_re, *dq_im, *dk_re, *dk_im, *dv_re, *dv_im;
+    float *db_rows;              // PCT: per-row bias gradient, may be null
+    int BH;
+    int T;
+    int d;
+    int causal;
+    float bias;                  // PCT
+    hipStream_t stream;
+};
+
+hipError_t launch_bwd_generic(const BwdProblem &p);
+
 }  // namespace cattn

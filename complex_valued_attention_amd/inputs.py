@@ -28,7 +28,7 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "BENCH_WORKLOAD", "make_inputs", "random_qkv",
+    "Workload", "WORKLOADS", "BENCH_WORKLOAD", "make_inputs", "make_grad", "random_qkv",
     "round_to_bf16_bits", "bf16_bits_to_f64", "attention_flops",
 ]
 
@@ -167,3 +167,30 @@ def make_inputs(w: Workload | str, **override) -> Inputs:
     q, k, v = random_qkv(w.B, w.H, w.T, w.d_h, w.seed, qk_unit=w.qk_unit,
                          v_unit=w.v_unit, rotary=w.rotary)
     return round_inputs(q, k, v, w.layout)
+
+
+@dataclasses.dataclass
+class Grad:
+    """An incoming gradient G = dL/d(conj O) for the backward: ``g64`` (complex128,
+    the device values promoted) and ``dev`` (``g`` complex64, or ``g_re``/``g_im``
+    bf16 bit planes)."""
+    layout: str
+    g64: np.ndarray
+    dev: dict
+
+
+def make_grad(w: Workload | str, **override) -> Grad:
+    """CN(0, 1) incoming gradient of the workload's output shape, drawn from
+    PCG64(seed + 1000) (a stream apart from the inputs') and rounded like them."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if override:
+        w = dataclasses.replace(w, **override)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+    shape = (w.B, w.H, w.T, w.d_h)
+    g = (rng.standard_normal(shape) + 1j * rng.standard_normal(shape)) * np.sqrt(0.5)
+    if w.layout == "c64":
+        dev = {"g": np.ascontiguousarray(g.astype(np.complex64))}
+        return Grad(w.layout, dev["g"].astype(np.complex128), dev)
+    re, im = round_to_bf16_bits(g.real), round_to_bf16_bits(g.imag)
+    return Grad(w.layout, bf16_bits_to_f64(re) + 1j * bf16_bits_to_f64(im), {"g_re": re, "g_im": im})

@@ -1,6 +1,7 @@
 /*
- * cattn.h -- fused forward pass of complex-valued attention on AMD Instinct
- * gfx950 (CDNA4).  C ABI: plain pointers and sizes, no C++ or framework types.
+ * cattn.h -- fused forward and backward passes of complex-valued attention on
+ * AMD Instinct gfx950 (CDNA4).  C ABI: plain pointers and sizes, no C++ or
+ * framework types.
  *
  * Two operators, both ending in O = W V over complex values V:
  *
@@ -56,7 +57,7 @@ typedef enum {
     CATTN_E_SHAPE = 2,       /* a size is negative, or the byte size overflows int64 */
     CATTN_E_LAYOUT = 3,      /* unknown layout value */
     CATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
-    CATTN_E_ALIAS = 5,       /* O or row_den overlaps an input or each other */
+    CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
     CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
     CATTN_E_ARG = 8          /* eps negative or not finite, or bias not finite */
@@ -103,10 +104,70 @@ cattn_status cattn_pct_fwd(int layout,
                            int64_t B, int64_t H, int64_t T, int64_t d_h,
                            int causal, float bias, void *stream);
 
+/*
+ * Backward passes.  Gradients follow the Wirtinger convention of "CNet ..."
+ * (section 3, the accumulation rule (2) and the CModulus2 worked example):
+ * for a real loss L the caller passes G = dL/d(conj O) and receives
+ * dL/d(conj q), dL/d(conj k), dL/d(conj v).  The map is linear in G, so
+ * passing the real-pair gradient dL/dRe O + i dL/dIm O (the convention of
+ * torch's complex autograd) returns real-pair gradients.  The closed forms
+ * (derived from the forward definitions; section 11.2 of the same page states
+ * that Born attention's backward exists in closed form):
+ *
+ *   Born, with l = row_den, delta[k] = Re(G[k]^H O[k]) and, for j in J(k),
+ *   D[k,j] = (Re(G[k]^H V[j]) - delta[k]) / l[k]:
+ *       dV[j] = sum_k w[k,j] / l[k] G[k]
+ *       dQ[k] = sum_j 2 D[k,j] S[k,j] K[j]
+ *       dK[j] = sum_k 2 D[k,j] conj(S[k,j]) Q[k]
+ *   A row with l[k] == 0 contributes nothing.
+ *
+ *   PCT, with qh, kh the unit rows and ds[i,j] = Re(G[i]^H V[j]) w (1 - w):
+ *       dV[j] = sum_i w[i,j] G[i]
+ *       dq[i] = P(qh[i], sqrt(d_h) sum_j ds[i,j] kh[j]) / ||q[i]||
+ *       dk[j] = P(kh[j], sqrt(d_h) sum_i ds[i,j] qh[i]) / ||k[j]||
+ *   where P(u, x) = x - Re(x^H u) u; a zero-norm row gets gradient 0.
+ *
+ * Arguments as for the forward, plus:
+ *   o_*        Born: the forward output O (same layout).
+ *   g_*        the incoming gradient G (same layout).
+ *   row_den    Born: device float[B*H*T], the forward's row denominators
+ *              (sum_j w + eps), required.
+ *   dq_*, dk_*, dv_*  outputs (same layout), fully overwritten.
+ *   db_rows    PCT: optional (NULL allowed) device float[B*H*T], receives
+ *              sum_j ds[i,j] per query row; their sum is dL/d(bias).
+ * The outputs must not overlap any input or each other.  The arithmetic is
+ * fp32 for both layouts (bf16 inputs are widened, outputs rounded to bf16).
+ * Each call enqueues two kernels (key-side and query-side gradients); it
+ * allocates nothing, uses no atomics and is deterministic.
+ */
+cattn_status cattn_born_bwd(int layout,
+                            const void *q_re, const void *q_im,
+                            const void *k_re, const void *k_im,
+                            const void *v_re, const void *v_im,
+                            const void *o_re, const void *o_im,
+                            const void *g_re, const void *g_im,
+                            const float *row_den,
+                            void *dq_re, void *dq_im,
+                            void *dk_re, void *dk_im,
+                            void *dv_re, void *dv_im,
+                            int64_t B, int64_t H, int64_t T, int64_t d_h,
+                            int causal, void *stream);
+
+cattn_status cattn_pct_bwd(int layout,
+                           const void *q_re, const void *q_im,
+                           const void *k_re, const void *k_im,
+                           const void *v_re, const void *v_im,
+                           const void *g_re, const void *g_im,
+                           void *dq_re, void *dq_im,
+                           void *dk_re, void *dk_im,
+                           void *dv_re, void *dv_im,
+                           int64_t B, int64_t H, int64_t T, int64_t d_h,
+                           int causal, float bias, float *db_rows, void *stream);
+
 /* Static, NUL-terminated description of a status value (never NULL). */
 const char *cattn_status_str(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 had the forward entry points only). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -20,14 +20,15 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["cattn_abi_version", "cattn_born_fwd", "cattn_pct_fwd", "cattn_status_str"]
+    assert declared_functions() == ["cattn_abi_version", "cattn_born_bwd", "cattn_born_fwd", "cattn_pct_bwd",
+                                    "cattn_pct_fwd", "cattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 1
+    assert L.cattn_abi_version() == 2
 
 
 def test_status_strings():
@@ -112,3 +113,69 @@ def test_python_binding_rejects_bad_tensors():
         cattn.born_fwd(x, x, x)            # host tensors are refused before any call
     with pytest.raises(TypeError):
         cattn.born_fwd(x.real, x.real, x.real)
+
+
+# ---- backward entry points -------------------------------------------------
+Q = [0x100000 * (i + 20) for i in range(16)]
+
+
+def born_b(layout=0, ins=None, outs=None, row_den=Q[15], B=1, H=1, T=8, d=4, causal=1):
+    if ins is None:   # q, k, v, o, g as (re, im) pairs
+        ins = [(Q[i], None) for i in range(5)] if layout == 0 else [(Q[i], Q[i + 5]) for i in range(5)]
+    if outs is None:  # dq, dk, dv
+        outs = [(Q[10 + i], None if layout == 0 else 0x100000 * (41 + i)) for i in range(3)]
+    flat_in = [x for pair in ins for x in pair]
+    flat_out = [x for pair in outs for x in pair]
+    return cattn.lib().cattn_born_bwd(layout, *flat_in, row_den, *flat_out, B, H, T, d, causal, None)
+
+
+def pct_b(layout=0, ins=None, outs=None, db_rows=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0):
+    if ins is None:   # q, k, v, g
+        ins = [(Q[i], None) for i in range(4)] if layout == 0 else [(Q[i], Q[i + 5]) for i in range(4)]
+    if outs is None:
+        outs = [(Q[10 + i], None) for i in range(3)]
+    flat_in = [x for pair in ins for x in pair]
+    flat_out = [x for pair in outs for x in pair]
+    return cattn.lib().cattn_pct_bwd(layout, *flat_in, *flat_out, B, H, T, d, causal, bias, db_rows, None)
+
+
+def test_bwd_argument_errors():
+    assert born_b(layout=5) == 3
+    assert pct_b(d=0) == 6
+    assert born_b(T=-1) == 2
+    assert pct_b(bias=float("nan")) == 8
+    # Born needs O, G and row_den
+    assert born_b(row_den=None) == 1
+    ins = [(Q[i], None) for i in range(5)]
+    ins[3] = (None, None)
+    assert born_b(ins=ins) == 1
+    # PCT needs G
+    ins = [(Q[i], None) for i in range(4)]
+    ins[3] = (None, None)
+    assert pct_b(ins=ins) == 1
+    # complex64 carries no imaginary planes
+    outs = [(Q[10], Q[13]), (Q[11], None), (Q[12], None)]
+    assert pct_b(outs=outs) == 1
+    # alignment of an output and of db_rows
+    outs = [(Q[10] + 8, None), (Q[11], None), (Q[12], None)]
+    assert born_b(outs=outs) == 4
+    assert pct_b(db_rows=Q[14] + 4) == 4
+
+
+def test_bwd_aliasing():
+    # dq over k
+    outs = [(Q[1], None), (Q[11], None), (Q[12], None)]
+    assert born_b(outs=outs) == 5
+    # dk over dv
+    outs = [(Q[10], None), (Q[11], None), (Q[11] + 16, None)]
+    assert pct_b(outs=outs) == 5
+    # db_rows over an output
+    assert pct_b(db_rows=Q[12]) == 5
+    # an output over row_den
+    outs = [(Q[10], None), (Q[15], None), (Q[12], None)]
+    assert born_b(outs=outs) == 5
+
+
+def test_bwd_empty_problem_is_ok():
+    assert born_b(ins=[(None, None)] * 5, outs=[(None, None)] * 3, row_den=None, T=0) == 0
+    assert pct_b(ins=[(None, None)] * 4, outs=[(None, None)] * 3, B=0) == 0
