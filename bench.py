@@ -1,6 +1,7 @@
 """Benchmark: Born-rule attention forward, B8 H16 T4096 d_h 64, bf16 real/imag planes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--copy-probe MIB]
+    python bench.py --pass bwd [--workload NAME] ...      (the backward instead of the forward)
 
 One step = one call of the fused forward (score GEMM, weight map, Born
 denominator, value GEMM, epilogue: the whole hot path, one kernel launch)
@@ -14,6 +15,7 @@ timed on a bounded sample of whole heads on the host cores as a CPU baseline
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -72,6 +74,92 @@ def kernel_name(w) -> str:
     if w.layout == "c64" and w.d_h in (16, 32, 64):
         return "attn_f32_mfma_kernel"
     return "generic_fwd_kernel"
+
+
+def bwd_flops(w) -> float:
+    """Minimal backward flops: S, E = Re(G^H V), dV, dK and dQ once each -- Born
+    (8 + 4 + 4 + 8 + 8) d_h = 32 d_h per (query, key) pair, PCT (4 + 4 + 4 + 4 + 4)
+    d_h = 20 d_h (only Re S, real weights); halved when causal."""
+    per_pair = 32.0 if w.op == "born" else 20.0
+    f = per_pair * w.T * w.T * w.d_h * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def run_gpu_bwd(w, steps: int, warmup: int):
+    """Times the backward call alone; O and the row denominators come from one
+    forward call before the timed region."""
+    import torch
+    from complex_valued_attention_amd import cattn, inputs as gen
+    from complex_valued_attention_amd.check import from_device, grad_to_device, to_device
+
+    cattn.lib()
+    inp = gen.make_inputs(w)
+    grad = gen.make_grad(w)
+    q, k, v = to_device(inp)
+    g = grad_to_device(grad)
+    like = (lambda: torch.empty_like(q)) if w.layout == "c64" else (lambda: (torch.empty_like(q[0]),
+                                                                            torch.empty_like(q[0])))
+    grads = (like(), like(), like())
+    if w.op == "born":
+        den = torch.empty(w.B * w.H * w.T, dtype=torch.float32, device="cuda")
+        o = cattn.born_fwd(q, k, v, causal=w.causal, row_den=den)
+        step = lambda: cattn.born_bwd(q, k, v, o, g, den, causal=w.causal, grads=grads)
+    else:
+        step = lambda: cattn.pct_bwd(q, k, v, g, causal=w.causal, grads=grads)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return inp, grad, tuple(from_device(x) for x in grads), ev[0].elapsed_time(ev[-1]) / steps, per
+
+
+def main_bwd(args, w):
+    from complex_valued_attention_amd.check import rowwise_rel_err
+    inp, grad, got, ms, per = run_gpu_bwd(w, args.steps, args.warmup)
+    flops = bwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] bwd {w.name}: {ms:.4f} ms/step (median {np.median(per):.4f} ms), {tflops:.2f} TFLOP/s")
+    # which kernels the library dispatches: bf16 matrix cores for Born at d_h = 64, else fp32 vector code
+    mfma = w.op == "born" and w.layout == "bf16" and w.d_h == 64
+    peak = PEAK_TFLOPS["bf16"] if mfma else PEAK_TFLOPS["c64"]
+    kern = ("born_bf16_d64_bwd_dkdv_kernel + born_bf16_d64_bwd_dq_kernel" if mfma
+            else "bwd_dkdv_kernel + bwd_dq_kernel")
+    rec = {
+        "metric": f"{w.op} bwd real TFLOP/s ({w.name})",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if mfma else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "bwd", "op": w.op, "causal": w.causal, "B": w.B, "H": w.H,
+                   "T": w.T, "d_h": w.d_h, "layout": w.layout},
+        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None, "kernel": kern},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        t0 = time.perf_counter()
+        b, h = 0, 0
+        if w.op == "born":
+            ref = oracle.born_attention_bwd(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], grad.g64[b, h],
+                                            causal=w.causal)
+        else:
+            ref = oracle.pct_attention_bwd(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], grad.g64[b, h],
+                                           causal=w.causal)[:3]
+        t = time.perf_counter() - t0
+        one = dataclasses.replace(w, B=1, H=1)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        rec["cpu_baseline"] = {"value": bwd_flops(one) / t / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                               "kind": "oracle", "sample": f"1 of {w.B * w.H} heads (full T={w.T}), fp64 numpy, "
+                                                           f"{t:.1f} s",
+                               "gpu_rowwise_rel_err_dv": rowwise_rel_err(got[2][b, h], ref[2])}
+    print(json.dumps(rec), flush=True)
 
 
 def run_gpu(w, steps: int, warmup: int):
@@ -147,6 +235,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the bench, run a plain elementwise copy of MIB MiB (reads and writes MIB MiB "
                          "per launch) five times: the reference kernel for scaling HBM byte counters")
@@ -161,6 +250,9 @@ def main():
     name = args.workload or gen.BENCH_WORKLOAD
     w = gen.WORKLOADS[name]
 
+    if args.which == "bwd":
+        main_bwd(args, w)
+        return
     inp, got, ms, per, wall_ms = run_gpu(w, args.steps, args.warmup)
     flops = gen.attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
     alg = algorithmic_flops(w)

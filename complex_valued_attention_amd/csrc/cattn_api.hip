@@ -178,7 +178,13 @@ cattn_status validate_bwd(int op, int layout, const void *const in_re[5], const 
 }
 
 cattn_status run_bwd(const cattn::BwdProblem &p) {
-    const hipError_t e = cattn::launch_bwd_generic(p);
+    hipError_t e;
+    if (cattn::supports_born_bf16_d64_bwd(p)) {
+        e = cattn::launch_born_bf16_d64_bwd_dkdv(p);
+        if (e == hipSuccess) e = cattn::launch_born_bf16_d64_bwd_dq(p);
+    } else {
+        e = cattn::launch_bwd_generic(p);
+    }
     return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 

@@ -58,6 +58,12 @@ struct BwdProblem {
     hipStream_t stream;
 };
 
-hipError_t launch_bwd_generic(const BwdProblem &p);
+hipError_t launch_bwd_generic(const BwdProblem &p);        // both kernels
+hipError_t launch_bwd_generic_dkdv(const BwdProblem &p);   // key-side gradients only
+hipError_t launch_bwd_generic_dq(const BwdProblem &p);     // query-side gradients only
+
+bool supports_born_bf16_d64_bwd(const BwdProblem &p);
+hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p);
+hipError_t launch_born_bf16_d64_bwd_dkdv(const BwdProblem &p);
 
 }  // namespace cattn

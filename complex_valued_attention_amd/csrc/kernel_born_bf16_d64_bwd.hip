@@ -1,0 +1,548 @@
+// Born-rule attention backward, head width 64, bf16 real/imaginary planes,
+// gfx950 matrix cores (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
+//
+// Gradients ("CNet ...", section 3, the Wirtinger accumulation rule (2)):
+// given G = dL/d(conj O), the forward's output O and row denominators l, and
+// per query row delta = Re(G^H O), with E = Re(G V^H) and, on the causal
+// support, D2 = 2 (E - delta) / l and P = D2 o S (S = Q K^H):
+//     dV = (w / l)^T G,   dQ = P K,   dK = P^H Q.
+// Real forms used below, with a prime for the real width-128 row [Re | Im]:
+//     Re S = Q' . K',   Im S = Re Q . (-Im K) + Im Q . Re K,   E = G' . V'
+//     Re dQ = P_r K_r - P_i K_i,  Im dQ = P_r K_i + P_i K_r
+//     Re dK = P_r Q_r + P_i Q_i,  Im dK = P_r Q_i - P_i Q_r
+//     dV'   = (w / l) G'
+//
+// Two kernels share the forward's building blocks: swizzled 64-row stages of
+// one plane per 8 KiB region, staged straight from global memory into LDS,
+// A operands of row-major tiles read as 16-byte chunks, and the transposing
+// LDS read (ds_read_b64_tr_b16) for tiles used with their rows as the
+// contraction index.  A tile needed both ways is staged twice, once in each
+// swizzle, so every LDS read stays free of bank conflicts.  Products are
+// formed with the streamed rows along the MFMA's k-dimension's partner, so
+// each lane's 16 accumulator values are directly the bf16 B operand of the
+// next product (no shuffles).
+//
+//  * dQ kernel: a workgroup of 4 waves owns 128 queries (32 per wave, the
+//    wave's Q' and G' in registers) and streams K and V.  Per 32-key block:
+//    S^T and E^T (keys x queries), P^T, then dQ^T += K^T P^T.
+//  * dK/dV kernel: a workgroup owns 128 keys (K' and V' in registers) and
+//    streams Q and G with the per-query 2/l and 2 delta/l.  Per 32-query
+//    block: S and E (queries x keys), w/l and P, then dV^T += G^T (w/l) and
+//    dK^T += Q^T P.
+// Causal work is balanced by mirrored pairs of tiles, as in the forward.
+#include "cattn_internal.h"
+
+namespace cattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4v __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int D = 64;
+constexpr int NW = 4;                   // waves per workgroup, one per SIMD
+constexpr int NT = 64 * NW;
+constexpr int BT = 32 * NW;             // rows owned by a workgroup (queries or keys)
+constexpr int BS = 64;                  // streamed rows per LDS stage
+constexpr int ROWB = 2 * D;             // bytes per row of one plane
+constexpr int REGION = BS * ROWB;       // 8 KiB
+constexpr int CPT = REGION / 16 / NT;   // 16-byte chunks per thread per region
+static_assert(CPT * 16 * NT == REGION, "staging split");
+
+__device__ inline int swz_k(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+__device__ inline int swz_v(int row) { return (row & 3) << 1; }
+
+__device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ inline u32x2 ds_read_tr(const char *p) {
+    const bf16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes per lane from global memory (SGPR base + per-lane byte offset)
+// straight into LDS at lds + 16 * lane.  Completion is tracked by hand
+// (vmcnt(0) before the barrier that publishes a stage).
+__device__ inline void dma16(uint32_t lds, const void *base, uint32_t voff) {
+    __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// All of this wave's loads have landed; then workgroup barrier.
+__device__ inline void loads_done_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
+// Rows r0 .. r0 + 63 of one plane into one LDS region, chunk c of row r at
+// slot c ^ swz(r).  Rows past T repeat row T - 1 (they are masked later).
+__device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, bool vswz, int tid,
+                                    int wave) {
+    const int slot = tid & 7;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+        const int row = (tid >> 3) + (NT / 8) * e;
+        const int lc = slot ^ (vswz ? swz_v(row) : swz_k(row));
+        const int g = min(r0 + row, T - 1);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NT * 16 + wave * 1024));
+        dma16(dst, plane, (uint32_t)(g * ROWB + 16 * lc));
+    }
+}
+
+// B-operand rows: lane (row l32, half h) holds X'[row][16 kk + 8 h .. + 8] of
+// X' = [Re X | Im X]; zero for rows past T.
+__device__ inline void load_rows_b(const uint16_t *re, const uint16_t *im, int row, int T, int h, u32x4 (&x)[8]) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < T) v = *reinterpret_cast<const u32x4 *>((kk < 4 ? re : im) + (int64_t)row * D + 16 * (kk & 3) + 8 * h);
+        x[kk] = v;
+    }
+}
+
+// Per-lane LDS offsets (the forward's): the A operand of k-step kk of a
+// row-major tile (row l32, logical chunk 2 (kk % 4) + h), and the
+// transposing read of a tile whose rows are the contraction index.
+struct Offsets {
+    int koff[4];
+    int voff[2];
+};
+
+__device__ inline Offsets lane_offsets(int lane) {
+    Offsets o;
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.koff[j] = l32 * ROWB + (((2 * j + h) ^ swz_k(l32)) << 4);
+    const int G = lane >> 4, r = (lane >> 2) & 3, c4 = lane & 3;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+        const int lc = 4 * cc + 2 * (G & 1) + (c4 >> 1);
+        o.voff[cc] = (4 * h + r) * ROWB + ((lc ^ (r << 1)) << 4) + ((c4 & 1) << 3);
+    }
+    return o;
+}
+
+// 32 channels x 16 rows A operand through two transposing reads.
+__device__ inline bf16x8 tr_operand(const char *p) {
+    const u32x2 lo = ds_read_tr(p);
+    const u32x2 hi = ds_read_tr(p + 8 * ROWB);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Stores a (channels x rows) accumulator set as bf16 planes: acc[c], c < 2 real
+// plane, c >= 2 imaginary plane, channel tile c & 1; lane row = l32.
+__device__ inline void store_rows(uint16_t *re, uint16_t *im, int row, int h, const f32x16 (&acc)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int col = 32 * (c & 1) + 8 * g + 4 * h;
+            const u32x2 v = {pack_bf16x2(acc[c][4 * g], acc[c][4 * g + 1]),
+                             pack_bf16x2(acc[c][4 * g + 2], acc[c][4 * g + 3])};
+            *reinterpret_cast<u32x2 *>((c < 2 ? re : im) + (int64_t)row * D + col) = v;
+        }
+    }
+}
+
+__device__ inline void work_item(const BwdProblem &p, int nwork, int &bh, int &item) {
+    const int L = blockIdx.x;
+    if ((p.BH & 7) == 0) {   // all items of a head on one XCD
+        const int x = L & 7, j = L >> 3;
+        bh = x + 8 * (j / nwork);
+        item = j % nwork;
+    } else {
+        bh = L / nwork;
+        item = L % nwork;
+    }
+}
+
+// ---------------------------------------------------------------------------- dQ
+constexpr int QREG = 6;   // K re, K im, V re, V im (row-major swizzle), K re, K im (transposing swizzle)
+
+__global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
+    __shared__ __align__(16) char lds[2 * QREG * REGION];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int T = p.T;
+    int bh, item;
+    work_item(p, nwork, bh, item);
+
+    const int64_t head = (int64_t)bh * T * D;
+    auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + head; };
+    const uint16_t *stage_planes[QREG] = {plane(p.k_re), plane(p.k_im), plane(p.v_re),
+                                          plane(p.v_im), plane(p.k_re), plane(p.k_im)};
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char *)lds;
+    const Offsets off = lane_offsets(lane);
+
+    auto issue_stage = [&](int s) {
+        const uint32_t base = lds0 + (uint32_t)((s & 1) * QREG * REGION);
+#pragma unroll
+        for (int r = 0; r < QREG; ++r)
+            stage_region(base + r * REGION, stage_planes[r], s * BS, T, r >= 4, tid, wave);
+    };
+
+    const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const int rb = p.causal ? (blk == 0 ? nrb - 1 - item : item) : item;
+        const int m0 = rb * BT;
+        const int qt0 = m0 + 32 * wave;
+        const int q = qt0 + l32;
+
+        // Q' and G' of this lane's query as B operands; delta and 2/l
+        u32x4 x[8];
+        bf16x8 qb[8], qneg[4], gb[8];
+        load_rows_b(plane(p.q_re), plane(p.q_im), q, T, h, x);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            qb[kk] = as_bf16x8(x[kk]);
+            if (kk < 4) qneg[kk] = as_bf16x8(x[kk] ^ 0x80008000u);
+        }
+        load_rows_b(plane(p.g_re), plane(p.g_im), q, T, h, x);
+        u32x4 ox[8];
+        load_rows_b(plane(p.o_re), plane(p.o_im), q, T, h, ox);
+        float dl = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            gb[kk] = as_bf16x8(x[kk]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dl += bf_lo(x[kk][e]) * bf_lo(ox[kk][e]) + bf_hi(x[kk][e]) * bf_hi(ox[kk][e]);
+        }
+        dl += __shfl_xor(dl, 32);   // both lane halves hold this query
+        float inv2 = 0.f;
+        if (q < T) {
+            const float l = p.row_den[(int64_t)bh * T + q];
+            inv2 = l != 0.f ? 2.f / l : 0.f;   // a zero denominator: no gradient
+        }
+        const float dinv2 = dl * inv2;
+
+        f32x16 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+
+        auto key_block = [&](const char *st, int sb, bool masked, int lim) {
+            f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int o = (kk >> 2) * REGION + sb * 32 * ROWB + off.koff[kk & 3];
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(st + o);
+                sr = mfma(ak, qb[kk], sr);
+                si = mfma(ak, kk < 4 ? qb[kk + 4] : qneg[kk - 4], si);
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(st + 2 * REGION + o);
+                e = mfma(av, gb[kk], e);
+            }
+            // P^T = D2 S^T; register r of lane half h is key 8 (r/4) + 4 h + r % 4
+            uint32_t pr[8], pi[8];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float d0 = e[r] * inv2 - dinv2, d1 = e[r + 1] * inv2 - dinv2;
+                if (masked) {
+                    const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);
+                    d0 = key0 > lim ? 0.f : d0;
+                    d1 = key0 + 1 > lim ? 0.f : d1;
+                }
+                pr[r >> 1] = pack_bf16x2(d0 * sr[r], d1 * sr[r + 1]);
+                pi[r >> 1] = pack_bf16x2(d0 * si[r], d1 * si[r + 1]);
+            }
+            bf16x8 prb[2], pib[2], pnb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const u32x4 a = {pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3]};
+                const u32x4 b = {pi[4 * m], pi[4 * m + 1], pi[4 * m + 2], pi[4 * m + 3]};
+                prb[m] = as_bf16x8(a);
+                pib[m] = as_bf16x8(b);
+                pnb[m] = as_bf16x8(b ^ 0x80008000u);
+            }
+            // dQ^T += K^T P^T:  Re += K_r P_r - K_i P_i,  Im += K_i P_r + K_r P_i
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
+                    const bf16x8 krt = tr_operand(st + 4 * REGION + o);
+                    const bf16x8 kit = tr_operand(st + 5 * REGION + o);
+                    acc[ct] = mfma(krt, prb[m], acc[ct]);
+                    acc[ct] = mfma(kit, pnb[m], acc[ct]);
+                    acc[2 + ct] = mfma(kit, prb[m], acc[2 + ct]);
+                    acc[2 + ct] = mfma(krt, pib[m], acc[2 + ct]);
+                }
+            }
+        };
+
+        const int kend = p.causal ? min(T, m0 + BT) : T;
+        const int nstages = (kend + BS - 1) / BS;
+        const bool wave_live = qt0 < T;
+
+        loads_done_barrier();   // the previous row block is done with both buffers
+        issue_stage(0);
+        for (int s = 0; s < nstages; ++s) {
+            loads_done_barrier();
+            if (s + 1 < nstages) issue_stage(s + 1);
+            if (!wave_live) continue;
+            const char *st = lds + (s & 1) * QREG * REGION;
+#pragma unroll
+            for (int sb = 0; sb < BS / 32; ++sb) {
+                const int kb0 = s * BS + 32 * sb;
+                const bool skip = kb0 >= T || (p.causal && kb0 > qt0);
+                const bool full = (!p.causal || kb0 + 32 <= qt0) && kb0 + 32 <= T;
+                if (full)
+                    key_block(st, sb, false, 31);
+                else if (!skip)
+                    key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0));
+            }
+        }
+        if (q < T) store_rows(reinterpret_cast<uint16_t *>(p.dq_re) + head, reinterpret_cast<uint16_t *>(p.dq_im) + head,
+                              q, h, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------- dK, dV
+constexpr int KREG = 8;   // Q re, Q im, G re, G im (row-major), the same four (transposing)
+
+__global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p, int nkt, int nwork) {
+    __shared__ __align__(16) char lds[2 * KREG * REGION];
+    __shared__ __align__(16) float scal[2][2][BS];   // [buffer][2/l, 2 delta/l][query of the stage]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int T = p.T;
+    int bh, item;
+    work_item(p, nwork, bh, item);
+
+    const int64_t head = (int64_t)bh * T * D;
+    auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + head; };
+    const uint16_t *stage_planes[KREG] = {plane(p.q_re), plane(p.q_im), plane(p.g_re), plane(p.g_im),
+                                          plane(p.q_re), plane(p.q_im), plane(p.g_re), plane(p.g_im)};
+    const uint16_t *ore = plane(p.o_re), *oim = plane(p.o_im), *gre = plane(p.g_re), *gim = plane(p.g_im);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char *)lds;
+    const Offsets off = lane_offsets(lane);
+
+    // per-query scalars of a stage: thread -> query tid / 4, channels 16 (tid % 4) .. + 16
+    const int sq = tid >> 2, sp = tid & 3;
+    u32x4 sx[8];   // G re, G im, O re, O im: two 16-byte chunks each
+    auto scal_load = [&](int q0) {
+        const int q = q0 + sq;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint16_t *src = (i >> 1) == 0 ? gre : (i >> 1) == 1 ? gim : (i >> 1) == 2 ? ore : oim;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (q < T) v = *reinterpret_cast<const u32x4 *>(src + (int64_t)q * D + 16 * sp + 8 * (i & 1));
+            sx[i] = v;
+        }
+    };
+    auto scal_store = [&](int q0, int buf) {
+        float dl = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dl += bf_lo(sx[i][e]) * bf_lo(sx[4 + i][e]) + bf_hi(sx[i][e]) * bf_hi(sx[4 + i][e]) +
+                      bf_lo(sx[2 + i][e]) * bf_lo(sx[6 + i][e]) + bf_hi(sx[2 + i][e]) * bf_hi(sx[6 + i][e]);
+        dl += __shfl_xor(dl, 1);
+        dl += __shfl_xor(dl, 2);
+        if (sp == 0) {
+            const int q = q0 + sq;
+            float inv2 = 0.f;
+            if (q < T) {
+                const float l = p.row_den[(int64_t)bh * T + q];
+                inv2 = l != 0.f ? 2.f / l : 0.f;
+            }
+            scal[buf][0][sq] = inv2;
+            scal[buf][1][sq] = dl * inv2;
+        }
+    };
+
+    const int nblocks = p.causal && item != nkt - 1 - item ? 2 : 1;
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const int kt = p.causal ? (blk == 0 ? item : nkt - 1 - item) : item;   // long tile first
+        const int k0 = kt * BT;
+        const int kw0 = k0 + 32 * wave;
+        const int key = kw0 + l32;
+
+        // K' and V' of this lane's key as B operands
+        u32x4 x[8];
+        bf16x8 kb[8], kni[4], vb[8];
+        load_rows_b(plane(p.k_re), plane(p.k_im), key, T, h, x);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            kb[kk] = as_bf16x8(x[kk]);
+            if (kk >= 4) kni[kk - 4] = as_bf16x8(x[kk] ^ 0x80008000u);   // -Im K
+        }
+        load_rows_b(plane(p.v_re), plane(p.v_im), key, T, h, x);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) vb[kk] = as_bf16x8(x[kk]);
+
+        f32x16 dk[4], dv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dk[c] = dv[c] = f32x16{};
+
+        auto query_block = [&](const char *st, const float *sc_inv2, const float *sc_dinv2, int sb, bool masked,
+                               int lo, int hi) {
+            f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int o = (kk >> 2) * REGION + sb * 32 * ROWB + off.koff[kk & 3];
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(st + o);
+                sr = mfma(aq, kb[kk], sr);
+                si = mfma(aq, kk < 4 ? kni[kk] : kb[kk - 4], si);
+                const bf16x8 ag = *reinterpret_cast<const bf16x8 *>(st + 2 * REGION + o);
+                e = mfma(ag, vb[kk], e);
+            }
+            // register r of lane half h is query 8 (r/4) + 4 h + r % 4 of the block
+            uint32_t aw[8], pr[8], pi[8];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 i2 = *reinterpret_cast<const f32x4 *>(sc_inv2 + 32 * sb + 8 * g + 4 * h);
+                const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv2 + 32 * sb + 8 * g + 4 * h);
+                float a[4], d2[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * g + c;
+                    a[c] = 0.5f * i2[c] * (sr[r] * sr[r] + si[r] * si[r]);
+                    d2[c] = e[r] * i2[c] - di[c];
+                    if (masked) {
+                        const int qi = 8 * g + 4 * h + c;
+                        const bool ok = qi >= lo && qi <= hi;
+                        a[c] = ok ? a[c] : 0.f;
+                        d2[c] = ok ? d2[c] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 4; c += 2) {
+                    const int r = 4 * g + c;
+                    aw[r >> 1] = pack_bf16x2(a[c], a[c + 1]);
+                    pr[r >> 1] = pack_bf16x2(d2[c] * sr[r], d2[c + 1] * sr[r + 1]);
+                    pi[r >> 1] = pack_bf16x2(d2[c] * si[r], d2[c + 1] * si[r + 1]);
+                }
+            }
+            bf16x8 ab[2], prb[2], pib[2], pnb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const u32x4 w4 = {aw[4 * m], aw[4 * m + 1], aw[4 * m + 2], aw[4 * m + 3]};
+                const u32x4 a4 = {pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3]};
+                const u32x4 b4 = {pi[4 * m], pi[4 * m + 1], pi[4 * m + 2], pi[4 * m + 3]};
+                ab[m] = as_bf16x8(w4);
+                prb[m] = as_bf16x8(a4);
+                pib[m] = as_bf16x8(b4);
+                pnb[m] = as_bf16x8(b4 ^ 0x80008000u);
+            }
+            // dV^T += G'^T (w/l);  dK^T: Re += Q_r P_r + Q_i P_i,  Im += Q_i P_r - Q_r P_i
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
+                    const bf16x8 grt = tr_operand(st + 6 * REGION + o);
+                    const bf16x8 git = tr_operand(st + 7 * REGION + o);
+                    dv[ct] = mfma(grt, ab[m], dv[ct]);
+                    dv[2 + ct] = mfma(git, ab[m], dv[2 + ct]);
+                    const bf16x8 qrt = tr_operand(st + 4 * REGION + o);
+                    const bf16x8 qit = tr_operand(st + 5 * REGION + o);
+                    dk[ct] = mfma(qrt, prb[m], dk[ct]);
+                    dk[ct] = mfma(qit, pib[m], dk[ct]);
+                    dk[2 + ct] = mfma(qit, prb[m], dk[2 + ct]);
+                    dk[2 + ct] = mfma(qrt, pnb[m], dk[2 + ct]);
+                }
+            }
+        };
+
+        const int qs = p.causal ? k0 : 0;   // earlier queries see none of these keys
+        const int nstages = qs < T ? (T - qs + BS - 1) / BS : 0;
+        auto issue_stage = [&](int s) {
+            const uint32_t base = lds0 + (uint32_t)((s & 1) * KREG * REGION);
+#pragma unroll
+            for (int r = 0; r < KREG; ++r)
+                stage_region(base + r * REGION, stage_planes[r], qs + s * BS, T, r >= 4, tid, wave);
+        };
+
+        loads_done_barrier();   // the previous key tile is done with both buffers
+        if (nstages > 0) {
+            issue_stage(0);
+            scal_load(qs);
+            scal_store(qs, 0);
+        }
+        for (int s = 0; s < nstages; ++s) {
+            loads_done_barrier();   // stage s and its scalars are visible
+            const bool next = s + 1 < nstages;
+            if (next) {
+                issue_stage(s + 1);
+                scal_load(qs + (s + 1) * BS);
+            }
+            const char *st = lds + (s & 1) * KREG * REGION;
+            const float *si2 = scal[s & 1][0], *sdi = scal[s & 1][1];
+#pragma unroll
+            for (int sb = 0; sb < BS / 32; ++sb) {
+                const int qb0 = qs + s * BS + 32 * sb;
+                const bool skip = qb0 >= T || kw0 >= T || (p.causal && qb0 + 31 < kw0);
+                const bool full = (!p.causal || qb0 >= kw0 + 31) && qb0 + 32 <= T && kw0 + 32 <= T;
+                if (full) {
+                    query_block(st, si2, sdi, sb, false, 0, 31);
+                } else if (!skip) {
+                    const int lo = p.causal ? key - qb0 : 0;
+                    const int hi = key < T ? T - 1 - qb0 : -1;
+                    query_block(st, si2, sdi, sb, true, lo, hi);
+                }
+            }
+            if (next) scal_store(qs + (s + 1) * BS, (s + 1) & 1);
+        }
+        if (key < T) {
+            store_rows(reinterpret_cast<uint16_t *>(p.dk_re) + head, reinterpret_cast<uint16_t *>(p.dk_im) + head,
+                       key, h, dk);
+            store_rows(reinterpret_cast<uint16_t *>(p.dv_re) + head, reinterpret_cast<uint16_t *>(p.dv_im) + head,
+                       key, h, dv);
+        }
+    }
+}
+
+}  // namespace
+
+bool supports_born_bf16_d64_bwd(const BwdProblem &p) {
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D;
+}
+
+hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {
+    const int nrb = (p.T + BT - 1) / BT;
+    const int nwork = p.causal ? (nrb + 1) / 2 : nrb;
+    const int64_t blocks = (int64_t)p.BH * nwork;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(born_bf16_d64_bwd_dq_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nrb, nwork);
+    return hipGetLastError();
+}
+
+hipError_t launch_born_bf16_d64_bwd_dkdv(const BwdProblem &p) {
+    const int nkt = (p.T + BT - 1) / BT;
+    const int nwork = p.causal ? (nkt + 1) / 2 : nkt;
+    const int64_t blocks = (int64_t)p.BH * nwork;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(born_bf16_d64_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nkt, nwork);
+    return hipGetLastError();
+}
+
+}  // namespace cattn

@@ -363,25 +363,34 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdProblem p) {
 }
 
 template <int DP>
-hipError_t launch_dp(const BwdProblem &p) {
+hipError_t launch_dp(const BwdProblem &p, bool dkdv, bool dq) {
     constexpr int B = BwdTile<DP>::B;
     const int64_t nt = (p.T + B - 1) / B;
     const int64_t blocks = (int64_t)p.BH * nt;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<DP>, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel<DP>, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
-    return hipGetLastError();
+    if (dkdv) {
+        hipLaunchKernelGGL(bwd_dkdv_kernel<DP>, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (dq) {
+        hipLaunchKernelGGL(bwd_dq_kernel<DP>, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_parts(const BwdProblem &p, bool dkdv, bool dq) {
+    if (p.d <= 16) return launch_dp<16>(p, dkdv, dq);
+    if (p.d <= 32) return launch_dp<32>(p, dkdv, dq);
+    if (p.d <= 64) return launch_dp<64>(p, dkdv, dq);
+    return launch_dp<128>(p, dkdv, dq);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_generic(const BwdProblem &p) {
-    if (p.d <= 16) return launch_dp<16>(p);
-    if (p.d <= 32) return launch_dp<32>(p);
-    if (p.d <= 64) return launch_dp<64>(p);
-    return launch_dp<128>(p);
-}
+hipError_t launch_bwd_generic(const BwdProblem &p) { return launch_parts(p, true, true); }
+hipError_t launch_bwd_generic_dkdv(const BwdProblem &p) { return launch_parts(p, true, false); }
+hipError_t launch_bwd_generic_dq(const BwdProblem &p) { return launch_parts(p, false, true); }
 
 }  // namespace cattn

@@ -6,8 +6,10 @@ takes O and the row denominators from the HIP forward, as a caller would.
 Gradients are compared row by row (each query or key row of dQ, dK, dV).  A
 row's scale is the larger of its reference values and of the terms the
 computation subtracts to form it (`term_scales`): Born's dQ and dK are
-differences X - Y of two sums (the delta = Re(G^H O) term), and PCT's dq and
-dk remove a projection.  Where X and Y cancel -- exactly so in Born's first
+differences X - Y of two sums (the delta = Re(G^H O) term, whose own terms
+are counted by magnitude, sum_c |G_c| |O_c|, since delta is formed from the
+forward's output as the caller stores it), and PCT's dq and dk remove a
+projection.  Where X and Y cancel -- exactly so in Born's first
 causal row, whose gradient is identically 0 because O[0] = V[0] -- fp32
 arithmetic leaves rounding noise of the size of X and Y, which is what the
 tolerance is measured against there.  (An fp32 emulation of the same
@@ -81,9 +83,12 @@ def term_scales(op, q, k, v, g, causal, bias=0.0, eps=0.0):
         l = wgt.sum(-1) + eps
         inv = np.where(l > 0, 1.0 / np.where(l > 0, l, 1.0), 0.0)
         o = (wgt * inv[..., None]).astype(np.complex128) @ v
-        delta = np.sum((g.conj() * o).real, -1)
+        # delta = Re(G^H O) is itself a sum of cancelling terms, formed from the
+        # forward's output as stored (bf16 planes for that layout); its terms'
+        # magnitudes sum to sum_c |G_c| |O_c|, which is what O's rounding scales with
+        delta_abs = np.sum(np.abs(g) * np.abs(o), -1)
         X = (2 * E * S * inv[..., None]) * mask
-        Y = (2 * delta[..., None] * S * inv[..., None]) * mask
+        Y = (2 * delta_abs[..., None] * S * inv[..., None]) * mask
         sq = np.maximum(amax(X @ k), amax(Y @ k))
         sk = np.maximum(amax(tr(X.conj()) @ q), amax(tr(Y.conj()) @ q))
         sv = amax(tr(wgt * inv[..., None]).astype(np.complex128) @ g)
@@ -144,6 +149,14 @@ CASES = [
     ("born", "bf16", True, 1, 2, 300, 64, True),
     ("born", "bf16", False, 1, 1, 200, 16, False),
     ("born", "bf16", True, 1, 1, 150, 128, True),
+    # the bf16 head-width-64 matrix-core path: causal and not, T = 1, tile edges,
+    # B*H a multiple of 8 and not
+    ("born", "bf16", False, 2, 1, 333, 64, True),
+    ("born", "bf16", True, 1, 1, 1, 64, True),
+    ("born", "bf16", True, 1, 3, 64, 64, True),
+    ("born", "bf16", True, 2, 4, 129, 64, True),
+    ("born", "bf16", True, 1, 8, 520, 64, False),
+    ("born", "bf16", False, 1, 1, 127, 64, False),
     ("pct", "c64", True, 1, 2, 300, 64, False),
     ("pct", "c64", False, 1, 2, 65, 16, False),
     ("pct", "c64", True, 1, 1, 100, 17, False),
