@@ -10,7 +10,8 @@ to fp64) and computes the plain definitions in complex128:
   Learning Framework ...", section 11.2, paragraph "Closing it: Born-rule
   attention", and Figure 2).
 * :mod:`oracle.pct`   -- phase-coherent (PCT) attention ("Complex-valued
-  Phase-Coherent Transformers", section 1 and Appendix D.2).
+  Phase-Coherent Transformers", section 1 and Appendix D.2), and the family's
+  L2-softmax and screening gates (Appendix D.2).
 * :mod:`oracle.born_density` -- a second, independent formulation of Born
   attention through causal density-matrix prefix states ("The Quantum
   Shortcut", section 2, the Born rule as a linear functional of the density
@@ -25,14 +26,14 @@ Every function here is pinned by the CPU tests against closed forms,
 invariants, hand-derived worked examples and the second formulation.
 """
 from .born import born_attention, born_attention_rows
-from .pct import pct_attention, pct_attention_rows, pct_scores
+from .pct import pct_attention, pct_attention_rows, pct_scores, pct_screen_attention, pct_softmax_attention
 from .born_density import born_attention_density
 from .born_grad import born_attention_bwd
 from .pct_grad import pct_attention_bwd
 
 __all__ = [
     "born_attention", "born_attention_rows",
-    "pct_attention", "pct_attention_rows", "pct_scores",
+    "pct_attention", "pct_attention_rows", "pct_scores", "pct_softmax_attention", "pct_screen_attention",
     "born_attention_density",
     "born_attention_bwd", "pct_attention_bwd",
 ]

@@ -68,3 +68,37 @@ def pct_attention_rows(q, k, v, rows, causal: bool = False, bias: float = 0.0):
         w = _sigmoid(s + bias)
         out[i] = w @ np.asarray(v[b, h, :J], dtype=np.complex128)
     return out
+
+
+# ---------------------------------------------------------------------------- siblings
+# "Complex-valued Phase-Coherent Transformers", Appendix D.2 lists the family's
+# other members on the same scaled cosine score: the L2-softmax cell (the PCT
+# cell with the sigmoid replaced by a row softmax over j) and the complex
+# screening cell (gate r^2 relu(s - t)^2).  Only the weight map differs.  The
+# screening cell's TanhNorm of the aggregate and its modReLU Hadamard gate act
+# after the attention sum and are not part of it.
+
+
+def pct_softmax_attention(q, k, v, causal: bool = False):
+    """L2-softmax member: w[i, j] = exp(s[i, j]) / sum_{j' in J(i)} exp(s[i, j']).
+
+    The score is bounded by sqrt(d_h) (Cauchy-Schwarz), so exp(s) needs no
+    shift to stay finite; the definition is written as it reads.
+    """
+    v = np.asarray(v, dtype=np.complex128)
+    T = q.shape[-2]
+    e = np.exp(pct_scores(q, k))
+    if causal:
+        e = e * np.tril(np.ones((T, T)))
+    w = e / e.sum(axis=-1, keepdims=True)
+    return w.astype(np.complex128) @ v
+
+
+def pct_screen_attention(q, k, v, causal: bool = False, r: float = 1.0, t: float = 0.0):
+    """Screening gate core: w[i, j] = r^2 max(s[i, j] - t, 0)^2, no row normalisation."""
+    v = np.asarray(v, dtype=np.complex128)
+    T = q.shape[-2]
+    w = r * r * np.maximum(pct_scores(q, k) - t, 0.0) ** 2
+    if causal:
+        w = w * np.tril(np.ones((T, T)))
+    return w.astype(np.complex128) @ v
