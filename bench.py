@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--copy-probe MIB]
     python bench.py --pass bwd [--workload NAME] ...      (the backward instead of the forward)
+    python bench.py --workload NAME --gate softmax|screen  (a PCT workload with a sibling gate)
 
 One step = one call of the fused forward (score GEMM, weight map, Born
 denominator, value GEMM, epilogue: the whole hot path, one kernel launch)
@@ -162,7 +163,7 @@ def main_bwd(args, w):
     print(json.dumps(rec), flush=True)
 
 
-def run_gpu(w, steps: int, warmup: int):
+def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid"):
     import torch
     from complex_valued_attention_amd import cattn, inputs as gen
     from complex_valued_attention_amd.check import from_device, to_device
@@ -176,10 +177,12 @@ def run_gpu(w, steps: int, warmup: int):
         out = torch.empty_like(q)
     else:
         out = (torch.empty_like(q[0]), torch.empty_like(q[0]))
-    fn = cattn.born_fwd if w.op == "born" else cattn.pct_fwd
-
-    def step():
-        fn(q, k, v, causal=w.causal, out=out)
+    if w.op == "born":
+        step = lambda: cattn.born_fwd(q, k, v, causal=w.causal, out=out)
+    elif gate == "sigmoid":
+        step = lambda: cattn.pct_fwd(q, k, v, causal=w.causal, out=out)
+    else:   # screening with r = 1, t = 0.5 (a threshold inside the score range)
+        step = lambda: cattn.pct_gate_fwd(q, k, v, gate=gate, causal=w.causal, a=1.0, b=0.5, out=out)
 
     for _ in range(warmup):
         step()
@@ -236,6 +239,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
+    ap.add_argument("--gate", choices=["sigmoid", "softmax", "screen"], default="sigmoid",
+                    help="PCT workloads: the gate on the scaled cosine score")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the bench, run a plain elementwise copy of MIB MiB (reads and writes MIB MiB "
                          "per launch) five times: the reference kernel for scaling HBM byte counters")
@@ -253,7 +258,10 @@ def main():
     if args.which == "bwd":
         main_bwd(args, w)
         return
-    inp, got, ms, per, wall_ms = run_gpu(w, args.steps, args.warmup)
+    if args.gate != "sigmoid" and w.op != "pct":
+        print("--gate applies to PCT workloads only", file=sys.stderr)
+        sys.exit(2)
+    inp, got, ms, per, wall_ms = run_gpu(w, args.steps, args.warmup, args.gate)
     flops = gen.attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
     alg = algorithmic_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -264,7 +272,8 @@ def main():
         f"ms/step), {tflops:.1f} TFLOP/s")
 
     rec = {
-        "metric": METRIC if name == gen.BENCH_WORKLOAD else f"{w.op} fwd real TFLOP/s ({name})",
+        "metric": METRIC if name == gen.BENCH_WORKLOAD else
+        f"{w.op}{'' if args.gate == 'sigmoid' else '-' + args.gate} fwd real TFLOP/s ({name})",
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -277,13 +286,14 @@ def main():
         "dtype": "bf16" if w.layout == "bf16" else "f32",
         "data": "synthetic (seeded complex Gaussian, unit-norm rotary Q/K)" if w.rotary else "synthetic",
         "config": {"workload": name, "op": w.op, "causal": w.causal, "B": w.B, "H": w.H, "T": w.T,
-                   "d_h": w.d_h, "layout": w.layout, "seed": w.seed},
+                   "d_h": w.d_h, "layout": w.layout, "seed": w.seed,
+                   **({} if args.gate == "sigmoid" else {"gate": args.gate})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(name),
                      "kernel": kernel_name(w),
                      "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per))},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.gate == "sigmoid":
         rec["cpu_baseline"] = cpu_baseline(w, inp, got)
         log(f"[bench] cpu baseline {rec['cpu_baseline']}")
     print(json.dumps(rec), flush=True)

@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
     L.cattn_pct_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                 ctypes.c_int, ctypes.c_float, vp]
     L.cattn_pct_fwd.restype = ctypes.c_int
+    L.cattn_pct_gate_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float, vp]
+    L.cattn_pct_gate_fwd.restype = ctypes.c_int
     L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
     L.cattn_born_bwd.restype = ctypes.c_int
     L.cattn_pct_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [vp] * 6 + [i64] * 4 +
@@ -139,6 +142,21 @@ def pct_fwd(q, k, v, causal: bool = False, bias: float = 0.0, out=None):
     layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
     s = lib().cattn_pct_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, int(bool(causal)),
                             float(bias), _stream(ts[0]))
+    _check(s)
+    return out
+
+
+GATES = {"sigmoid": 0, "softmax": 1, "screen": 2}
+
+
+def pct_gate_fwd(q, k, v, gate: str = "softmax", causal: bool = False, a: float = 0.0, b: float = 0.0, out=None):
+    """PCT-family forward with a chosen gate (cattn_pct_gate_fwd): "sigmoid" (bias a),
+    "softmax" (the L2-softmax cell) or "screen" (a^2 max(s - b, 0)^2)."""
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}")
+    layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
+    s = lib().cattn_pct_gate_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, int(bool(causal)), GATES[gate],
+                                 float(a), float(b), _stream(ts[0]))
     _check(s)
     return out
 

@@ -23,10 +23,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 cattn_status validate(int op, int layout, const void *q_re, const void *q_im, const void *k_re,
                       const void *k_im, const void *v_re, const void *v_im, void *o_re, void *o_im,
                       int64_t B, int64_t H, int64_t T, int64_t d_h, int causal, float eps, float bias,
-                      float *row_den, void *stream, Problem *p, bool *empty) {
+                      float *row_den, void *stream, Problem *p, bool *empty, float gate_r = 0.f,
+                      float gate_t = 0.f) {
     if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
     if (op == cattn::OP_BORN && (!isfinite(eps) || eps < 0.f)) return CATTN_E_ARG;
     if (op == cattn::OP_PCT && !isfinite(bias)) return CATTN_E_ARG;
+    if (op == cattn::OP_PCT_SCREEN && (!isfinite(gate_r) || !isfinite(gate_t))) return CATTN_E_ARG;
     if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
     if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
     if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
@@ -80,6 +82,8 @@ cattn_status validate(int op, int layout, const void *q_re, const void *q_im, co
     p->causal = causal != 0;
     p->eps = eps;
     p->bias = bias;
+    p->gate_r = gate_r;
+    p->gate_t = gate_t;
     p->stream = reinterpret_cast<hipStream_t>(stream);
     return CATTN_OK;
 }
@@ -214,6 +218,26 @@ cattn_status cattn_pct_fwd(int layout, const void *q_re, const void *q_im, const
     return run(p);
 }
 
+cattn_status cattn_pct_gate_fwd(int layout, const void *q_re, const void *q_im, const void *k_re,
+                                const void *k_im, const void *v_re, const void *v_im, void *o_re, void *o_im,
+                                int64_t B, int64_t H, int64_t T, int64_t d_h, int causal, int gate, float a,
+                                float b, void *stream) {
+    int op;
+    switch (gate) {
+        case CATTN_GATE_SIGMOID: op = cattn::OP_PCT; break;
+        case CATTN_GATE_SOFTMAX: op = cattn::OP_PCT_SOFTMAX; break;
+        case CATTN_GATE_SCREEN: op = cattn::OP_PCT_SCREEN; break;
+        default: return CATTN_E_ARG;
+    }
+    Problem p{};
+    bool empty = false;
+    const cattn_status s = validate(op, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H, T, d_h, causal,
+                                    0.f, gate == CATTN_GATE_SIGMOID ? a : 0.f, nullptr, stream, &p, &empty,
+                                    gate == CATTN_GATE_SCREEN ? a : 0.f, gate == CATTN_GATE_SCREEN ? b : 0.f);
+    if (s != CATTN_OK || empty) return s;
+    return run(p);
+}
+
 cattn_status cattn_born_bwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
                             const void *v_re, const void *v_im, const void *o_re, const void *o_im,
                             const void *g_re, const void *g_im, const float *row_den, void *dq_re, void *dq_im,
@@ -257,11 +281,11 @@ const char *cattn_status_str(int status) {
         case CATTN_E_ALIAS: return "an output overlaps an input or another output";
         case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128";
         case CATTN_E_LAUNCH: return "HIP kernel launch failed";
-        case CATTN_E_ARG: return "eps negative or not finite, or bias not finite";
+        case CATTN_E_ARG: return "eps negative or not finite, a gate parameter not finite, or an unknown gate";
         default: return "unknown status";
     }
 }
 
-int cattn_abi_version(void) { return 2; }
+int cattn_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -6,7 +6,14 @@
 
 namespace cattn {
 
-enum Op : int { OP_BORN = 0, OP_PCT = 1 };
+// OP_PCT is the sigmoid cell; the two siblings share its scaled cosine score
+// ("Complex-valued Phase-Coherent Transformers", Appendix D.2): the
+// L2-softmax cell and the screening gate r^2 relu(s - t)^2.
+enum Op : int { OP_BORN = 0, OP_PCT = 1, OP_PCT_SOFTMAX = 2, OP_PCT_SCREEN = 3 };
+
+// Operators on the PCT score path, and operators whose weights are row-normalised.
+__host__ __device__ inline bool op_pct_score(int op) { return op != OP_BORN; }
+__host__ __device__ inline bool op_row_norm(int op) { return op == OP_BORN || op == OP_PCT_SOFTMAX; }
 enum Layout : int { LAYOUT_C64 = 0, LAYOUT_BF16 = 1 };
 
 // One validated forward call.  Pointers are device pointers; tensors are
@@ -22,7 +29,9 @@ struct Problem {
     int d;
     int causal;
     float eps;          // Born
-    float bias;         // PCT
+    float bias;         // PCT sigmoid cell
+    float gate_r;       // screening gate: r
+    float gate_t;       // screening gate: t
     hipStream_t stream;
 };
 

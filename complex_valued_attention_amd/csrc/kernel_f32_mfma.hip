@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma_kernel(Problem p, int nrb) {
         qb[j] = x;
     }
     float rq = 0.f;
-    if (OP == OP_PCT) {
+    if (OP != OP_BORN) {
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < C::KCH; ++j) ss += qb[j][0] * qb[j][0] + qb[j][1] * qb[j][1] + qb[j][2] * qb[j][2] +
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma_kernel(Problem p, int nrb) {
             *reinterpret_cast<f32x4 *>(ks + skey * C::KROW + 4 * (schunk + i)) = kreg[i];
             *reinterpret_cast<f32x4 *>(vs + skey * C::VROW + 4 * (schunk + i)) = vreg[i];
         }
-        if (OP == OP_PCT) {
+        if (OP != OP_BORN) {
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < C::CPT; ++i)
@@ -189,8 +189,15 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma_kernel(Problem p, int nrb) {
                     const f32x4 rkv = *reinterpret_cast<const f32x4 *>(rk + 8 * g + 4 * h);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float x = sr[4 * g + e] * rq * rkv[e] + p.bias;
-                        w[4 * g + e] = 1.f / (1.f + __expf(-x));
+                        const float x = sr[4 * g + e] * rq * rkv[e];   // sqrt(d_h) Re<qh, kh>
+                        if (OP == OP_PCT) {
+                            w[4 * g + e] = 1.f / (1.f + __expf(-(x + p.bias)));
+                        } else if (OP == OP_PCT_SOFTMAX) {
+                            w[4 * g + e] = __expf(x);   // |x| <= sqrt(d_h): no shift needed
+                        } else {
+                            const float y = fmaxf(x - p.gate_t, 0.f);
+                            w[4 * g + e] = p.gate_r * p.gate_r * y * y;
+                        }
                     }
                 }
             }
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma_kernel(Problem p, int nrb) {
                     if ((diag && key > l32) || k0 + key >= T) w[r] = 0.f;
                 }
             }
-            if (OP == OP_BORN) {
+            if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) rsum += w[r];
             }
@@ -226,8 +233,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma_kernel(Problem p, int nrb) {
     // epilogue: rows of O'^T come out interleaved (re, im, re, im) in groups of 4
     float scale = 1.f;
     float den = 0.f;
-    if (OP == OP_BORN) {
-        den = rsum + __shfl_xor(rsum, 32) + p.eps;
+    if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) {
+        den = rsum + __shfl_xor(rsum, 32) + (OP == OP_BORN ? p.eps : 0.f);
         scale = den != 0.f ? 1.f / den : 0.f;
     }
     if (qrow >= T) return;
@@ -264,7 +271,12 @@ hipError_t launch_cfg(const Problem &p) {
 
 template <int D>
 hipError_t launch_d(const Problem &p) {
-    return p.op == OP_BORN ? launch_cfg<D, OP_BORN>(p) : launch_cfg<D, OP_PCT>(p);
+    switch (p.op) {
+        case OP_BORN: return launch_cfg<D, OP_BORN>(p);
+        case OP_PCT: return launch_cfg<D, OP_PCT>(p);
+        case OP_PCT_SOFTMAX: return launch_cfg<D, OP_PCT_SOFTMAX>(p);
+        default: return launch_cfg<D, OP_PCT_SCREEN>(p);
+    }
 }
 
 }  // namespace

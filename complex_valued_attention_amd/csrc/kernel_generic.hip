@@ -63,7 +63,8 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
     const int bh = blockIdx.x / nqb;
     const int q0 = (blockIdx.x % nqb) * BQ;
     const int64_t base = (int64_t)bh * p.T * d;
-    const bool pct = p.op == OP_PCT;
+    const bool pct = op_pct_score(p.op);
+    const bool norm = op_row_norm(p.op);
 
     for (int i = tid; i < BQ * DP; i += NT) {
         const int r = i / DP, m = i % DP;
@@ -121,8 +122,15 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
             if (!pct) {
                 w = sr * sr + si * si;
             } else {
-                const float x = sr * rq[r] * rk[c] + p.bias;
-                w = 1.f / (1.f + __expf(-x));
+                const float x = sr * rq[r] * rk[c];   // sqrt(d_h) Re<qh, kh>, |x| <= sqrt(d_h)
+                if (p.op == OP_PCT) {
+                    w = 1.f / (1.f + __expf(-(x + p.bias)));
+                } else if (p.op == OP_PCT_SOFTMAX) {
+                    w = __expf(x);                    // bounded by e^sqrt(d_h): no shift needed
+                } else {
+                    const float y = fmaxf(x - p.gate_t, 0.f);
+                    w = p.gate_r * p.gate_r * y * y;
+                }
             }
             Ws[r][c] = valid ? w : 0.f;
         }
@@ -147,13 +155,13 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
     const int qi = q0 + oq;
     if (qi >= p.T) return;
     const float D = dens[oq];
-    const float inv = (!pct && D != 0.f) ? 1.f / D : 0.f;
+    const float inv = (norm && D != 0.f) ? 1.f / D : 0.f;
 #pragma unroll
     for (int ci = 0; ci < NC; ++ci) {
         const int c = og + ci * NG;
         if (c < d) {
             float2 o = acc[ci];
-            if (!pct) o = make_float2(o.x * inv, o.y * inv);
+            if (norm) o = make_float2(o.x * inv, o.y * inv);
             store_c(p.layout, p.o_re, p.o_im, base + (int64_t)qi * d + c, o);
         }
     }

@@ -60,8 +60,16 @@ typedef enum {
     CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
     CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
-    CATTN_E_ARG = 8          /* eps negative or not finite, or bias not finite */
+    CATTN_E_ARG = 8          /* eps negative or not finite, a gate parameter not finite, or an unknown gate */
 } cattn_status;
+
+/* Gates on the PCT score path ("Complex-valued Phase-Coherent Transformers",
+ * Appendix D.2, the family's cells). */
+typedef enum {
+    CATTN_GATE_SIGMOID = 0,  /* w = sigmoid(s + a): the PCT cell (as cattn_pct_fwd, bias a) */
+    CATTN_GATE_SOFTMAX = 1,  /* w = exp(s) / sum_{j in J(i)} exp(s): the L2-softmax cell */
+    CATTN_GATE_SCREEN = 2    /* w = a^2 max(s - b, 0)^2: the screening gate (r = a, t = b) */
+} cattn_gate;
 
 typedef enum {
     CATTN_LAYOUT_C64 = 0,
@@ -103,6 +111,26 @@ cattn_status cattn_pct_fwd(int layout,
                            void *o_re, void *o_im,
                            int64_t B, int64_t H, int64_t T, int64_t d_h,
                            int causal, float bias, void *stream);
+
+/*
+ * PCT-family forward with a choice of gate on the same scaled cosine score
+ * s[i,j] = sqrt(d_h) Re < q_i/||q_i||, k_j/||k_j|| >  (|s| <= sqrt(d_h)):
+ *   gate CATTN_GATE_SIGMOID  O[i] = sum_j sigmoid(s[i,j] + a) V[j]
+ *   gate CATTN_GATE_SOFTMAX  O[i] = sum_j exp(s[i,j]) V[j] / sum_j exp(s[i,j])
+ *                            (a and b unused; the score bound keeps exp finite)
+ *   gate CATTN_GATE_SCREEN   O[i] = sum_j a^2 max(s[i,j] - b, 0)^2 V[j]
+ * with j over J(i).  The screening cell's TanhNorm of the aggregate and its
+ * modReLU gate act after this sum and are not part of it.  Other arguments
+ * as for cattn_pct_fwd; a and b must be finite where used; an unknown gate
+ * is CATTN_E_ARG.
+ */
+cattn_status cattn_pct_gate_fwd(int layout,
+                                const void *q_re, const void *q_im,
+                                const void *k_re, const void *k_im,
+                                const void *v_re, const void *v_im,
+                                void *o_re, void *o_im,
+                                int64_t B, int64_t H, int64_t T, int64_t d_h,
+                                int causal, int gate, float a, float b, void *stream);
 
 /*
  * Backward passes.  Gradients follow the Wirtinger convention of "CNet ..."
@@ -167,7 +195,7 @@ cattn_status cattn_pct_bwd(int layout,
 /* Static, NUL-terminated description of a status value (never NULL). */
 const char *cattn_status_str(int status);
 
-/* ABI version of this header: 2 (1 had the forward entry points only). */
+/* ABI version of this header: 3 (2 added the backward, 3 the PCT gates). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

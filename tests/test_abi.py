@@ -21,14 +21,14 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["cattn_abi_version", "cattn_born_bwd", "cattn_born_fwd", "cattn_pct_bwd",
-                                    "cattn_pct_fwd", "cattn_status_str"]
+                                    "cattn_pct_fwd", "cattn_pct_gate_fwd", "cattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 2
+    assert L.cattn_abi_version() == 3
 
 
 def test_status_strings():
@@ -179,3 +179,19 @@ def test_bwd_aliasing():
 def test_bwd_empty_problem_is_ok():
     assert born_b(ins=[(None, None)] * 5, outs=[(None, None)] * 3, row_den=None, T=0) == 0
     assert pct_b(ins=[(None, None)] * 4, outs=[(None, None)] * 3, B=0) == 0
+
+
+def gate_fwd(gate, a=0.0, b=0.0, layout=0, T=8, misalign=0):
+    # every call must fail validation: a misaligned O stops the ones whose gate arguments pass
+    q = [P[0], None, P[1], None, P[2], None, P[3] + misalign, None] if layout == 0 else P
+    return cattn.lib().cattn_pct_gate_fwd(layout, *q, 1, 1, T, 4, 1, gate, a, b, None)
+
+
+def test_gate_arguments():
+    assert gate_fwd(3) == 8                    # unknown gate
+    assert gate_fwd(-1) == 8
+    assert gate_fwd(0, a=float("nan")) == 8    # sigmoid bias
+    assert gate_fwd(2, a=float("inf")) == 8    # screening r
+    assert gate_fwd(2, b=float("nan")) == 8    # screening t
+    assert gate_fwd(1, a=float("nan"), misalign=8) == 4   # the softmax gate ignores a and b
+    assert gate_fwd(1, T=0) == 0
