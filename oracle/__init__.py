@@ -21,6 +21,8 @@ to fp64) and computes the plain definitions in complex128:
   operators in closed form (gradients dL/d(conj z) as in "CNet ...", section 3,
   rule (2)), derived from the forward definitions and pinned by finite
   differences.
+* :mod:`oracle.rotary` -- the rotary phase embedding ("Show HN: CNET",
+  RotaryEmbed).
 
 Every function here is pinned by the CPU tests against closed forms,
 invariants, hand-derived worked examples and the second formulation.
@@ -30,10 +32,12 @@ from .pct import pct_attention, pct_attention_rows, pct_scores, pct_screen_atten
 from .born_density import born_attention_density
 from .born_grad import born_attention_bwd
 from .pct_grad import pct_attention_bwd
+from .rotary import rotary
 
 __all__ = [
     "born_attention", "born_attention_rows",
     "pct_attention", "pct_attention_rows", "pct_scores", "pct_softmax_attention", "pct_screen_attention",
     "born_attention_density",
     "born_attention_bwd", "pct_attention_bwd",
+    "rotary",
 ]
