@@ -163,6 +163,40 @@ def main_bwd(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def main_rotary(args, w):
+    """The rotary pass over one [B, H, T, d_h] operand of the workload (out of place):
+    HBM-bound, bytes = the operand read once + written once."""
+    import torch
+    from complex_valued_attention_amd import cattn
+    from complex_valued_attention_amd.check import to_device
+    cattn.lib()
+    inp = __import__("complex_valued_attention_amd.inputs", fromlist=["make_inputs"]).make_inputs(w)
+    x = to_device(inp)[0]
+    out = cattn.rotary(x)
+    for _ in range(args.warmup):
+        cattn.rotary(x, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        cattn.rotary(x, out=out)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    nbytes = 2 * w.B * w.H * w.T * w.d_h * (8 if w.layout == "c64" else 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] rotary {w.name}: {ms:.4f} ms/step, {gbs:.0f} GB/s")
+    rec = {"metric": f"rotary GB/s ({w.name})", "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32" if w.layout == "c64" else "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "pass": "rotary", "B": w.B, "H": w.H, "T": w.T, "d_h": w.d_h,
+                      "layout": w.layout},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "rotary_kernel"}}
+    print(json.dumps(rec), flush=True)
+
+
 def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid"):
     import torch
     from complex_valued_attention_amd import cattn, inputs as gen
@@ -238,7 +272,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "rotary"], default="fwd")
     ap.add_argument("--gate", choices=["sigmoid", "softmax", "screen"], default="sigmoid",
                     help="PCT workloads: the gate on the scaled cosine score")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -257,6 +291,9 @@ def main():
 
     if args.which == "bwd":
         main_bwd(args, w)
+        return
+    if args.which == "rotary":
+        main_rotary(args, w)
         return
     if args.gate != "sigmoid" and w.op != "pct":
         print("--gate applies to PCT workloads only", file=sys.stderr)

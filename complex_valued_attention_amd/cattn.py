@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.cattn_pct_gate_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float, vp]
     L.cattn_pct_gate_fwd.restype = ctypes.c_int
+    L.cattn_rotary.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
+    L.cattn_rotary.restype = ctypes.c_int
     L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
     L.cattn_born_bwd.restype = ctypes.c_int
     L.cattn_pct_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [vp] * 6 + [i64] * 4 +
@@ -157,6 +159,24 @@ def pct_gate_fwd(q, k, v, gate: str = "softmax", causal: bool = False, a: float 
     layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
     s = lib().cattn_pct_gate_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, int(bool(causal)), GATES[gate],
                                  float(a), float(b), _stream(ts[0]))
+    _check(s)
+    return out
+
+
+def rotary(x, pos0: int = 0, base: float = 10000.0, out=None):
+    """Rotary phase embedding (cattn_rotary): x[..., t, m] * exp(i (pos0 + t) base^(-m/d_h)).
+    ``out=x`` rotates in place.  Returns the output tensor(s)."""
+    layout, re, im, shape = _unpack(x, "x")
+    if len(shape) != 4:
+        raise ValueError(f"x must be [B, H, T, d_h]; got {shape}")
+    if out is None:
+        out = _like(x)
+    lo, ore, oim, so = _unpack(out, "out")
+    if lo != layout or so != shape:
+        raise ValueError("out must match x's layout and shape")
+    B, H, T, d = shape
+    s = lib().cattn_rotary(layout, _ptr(re), _ptr(im), _ptr(ore), _ptr(oim), B, H, T, d, int(pos0), float(base),
+                           _stream(re))
     _check(s)
     return out
 

@@ -271,6 +271,45 @@ cattn_status cattn_pct_bwd(int layout, const void *q_re, const void *q_im, const
     return run_bwd(p);
 }
 
+cattn_status cattn_rotary(int layout, const void *x_re, const void *x_im, void *y_re, void *y_im, int64_t B,
+                          int64_t H, int64_t T, int64_t d_h, int64_t pos0, float base, void *stream) {
+    if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
+    if (!isfinite(base) || !(base > 0.f)) return CATTN_E_ARG;
+    if (pos0 < 0 || pos0 > ((int64_t)1 << 40)) return CATTN_E_ARG;
+    if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
+    if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
+    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    const int64_t BH = B * H;
+    const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
+    if (BH != 0 && T > (int64_t)(INT64_MAX / 16) / BH / d_h / elem) return CATTN_E_SHAPE;
+    if (BH == 0 || T == 0) return CATTN_OK;
+    const bool c64 = layout == CATTN_LAYOUT_C64;
+    if (!x_re || !y_re || (c64 ? (x_im || y_im) : (!x_im || !y_im))) return CATTN_E_NULL;
+    for (const void *q : {(const void *)x_re, (const void *)x_im, (const void *)y_re, (const void *)y_im})
+        if (q && !aligned16(q)) return CATTN_E_ALIGN;
+    // the output either is the input (in place, plane by plane) or overlaps nothing
+    const uintptr_t bytes = (uintptr_t)(BH * T * d_h * elem);
+    auto span = [bytes](const void *q) { return Span{(uintptr_t)q, (uintptr_t)q + bytes}; };
+    const void *xs[2] = {x_re, x_im};
+    const void *ys[2] = {y_re, y_im};
+    for (int a = 0; a < 2; ++a) {
+        if (!ys[a]) continue;
+        for (int b = 0; b < 2; ++b)
+            if (xs[b] && overlaps(span(ys[a]), span(xs[b])) && !(a == b && ys[a] == xs[b])) return CATTN_E_ALIAS;
+    }
+    if (y_im && overlaps(span(y_re), span(y_im))) return CATTN_E_ALIAS;
+    cattn::RotaryProblem p{};
+    p.layout = c64 ? cattn::LAYOUT_C64 : cattn::LAYOUT_BF16;
+    p.x_re = x_re; p.x_im = x_im; p.y_re = y_re; p.y_im = y_im;
+    p.rows = BH * T;
+    p.T = (int)T;
+    p.d = (int)d_h;
+    p.pos0 = pos0;
+    p.log_base = log((double)base);
+    p.stream = reinterpret_cast<hipStream_t>(stream);
+    return cattn::launch_rotary(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+}
+
 const char *cattn_status_str(int status) {
     switch (status) {
         case CATTN_OK: return "ok";
@@ -281,11 +320,11 @@ const char *cattn_status_str(int status) {
         case CATTN_E_ALIAS: return "an output overlaps an input or another output";
         case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128";
         case CATTN_E_LAUNCH: return "HIP kernel launch failed";
-        case CATTN_E_ARG: return "eps negative or not finite, a gate parameter not finite, or an unknown gate";
+        case CATTN_E_ARG: return "a scalar argument out of range (eps, bias, gate parameters, rotary base or position) or an unknown gate";
         default: return "unknown status";
     }
 }
 
-int cattn_abi_version(void) { return 3; }
+int cattn_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -75,4 +75,19 @@ bool supports_born_bf16_d64_bwd(const BwdProblem &p);
 hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p);
 hipError_t launch_born_bf16_d64_bwd_dkdv(const BwdProblem &p);
 
+// One validated rotary call over rows = B*H*T rows of d complex channels.
+struct RotaryProblem {
+    int layout;
+    const void *x_re, *x_im;
+    void *y_re, *y_im;
+    int64_t rows;
+    int T;
+    int d;
+    int64_t pos0;
+    double log_base;
+    hipStream_t stream;
+};
+
+hipError_t launch_rotary(const RotaryProblem &p);
+
 }  // namespace cattn

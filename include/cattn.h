@@ -60,7 +60,7 @@ typedef enum {
     CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
     CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
-    CATTN_E_ARG = 8          /* eps negative or not finite, a gate parameter not finite, or an unknown gate */
+    CATTN_E_ARG = 8          /* a scalar out of range: eps, bias, a gate parameter, rotary base or position; or an unknown gate */
 } cattn_status;
 
 /* Gates on the PCT score path ("Complex-valued Phase-Coherent Transformers",
@@ -192,10 +192,27 @@ cattn_status cattn_pct_bwd(int layout,
                            int64_t B, int64_t H, int64_t T, int64_t d_h,
                            int causal, float bias, float *db_rows, void *stream);
 
+/*
+ * Rotary phase embedding ("Show HN: CNET", the RotaryEmbed layer: position
+ * as a complex phase rotation, base 10000, an absolute position for the
+ * one-token step mode):
+ *     y[b,h,t,m] = x[b,h,t,m] * exp(i (pos0 + t) theta_m),  theta_m = base^(-m/d_h)
+ * over [B, H, T, d_h] tensors in either layout.  y may be x itself (in
+ * place, same pointers) or must not overlap it.  base > 0 and finite;
+ * 0 <= pos0 <= 2^40.  The angle is reduced modulo 2 pi in fp64, so long
+ * positions keep full fp32 accuracy.  Allocates nothing; asynchronous on
+ * stream.
+ */
+cattn_status cattn_rotary(int layout,
+                          const void *x_re, const void *x_im,
+                          void *y_re, void *y_im,
+                          int64_t B, int64_t H, int64_t T, int64_t d_h,
+                          int64_t pos0, float base, void *stream);
+
 /* Static, NUL-terminated description of a status value (never NULL). */
 const char *cattn_status_str(int status);
 
-/* ABI version of this header: 3 (2 added the backward, 3 the PCT gates). */
+/* ABI version of this header: 4 (2 added the backward, 3 the PCT gates, 4 rotary). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

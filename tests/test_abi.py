@@ -21,14 +21,14 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["cattn_abi_version", "cattn_born_bwd", "cattn_born_fwd", "cattn_pct_bwd",
-                                    "cattn_pct_fwd", "cattn_pct_gate_fwd", "cattn_status_str"]
+                                    "cattn_pct_fwd", "cattn_pct_gate_fwd", "cattn_rotary", "cattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 3
+    assert L.cattn_abi_version() == 4
 
 
 def test_status_strings():
@@ -195,3 +195,25 @@ def test_gate_arguments():
     assert gate_fwd(2, b=float("nan")) == 8    # screening t
     assert gate_fwd(1, a=float("nan"), misalign=8) == 4   # the softmax gate ignores a and b
     assert gate_fwd(1, T=0) == 0
+
+
+def rot(layout=0, ptrs=None, B=1, H=1, T=8, d=4, pos0=0, base=10000.0):
+    xs = ptrs if ptrs is not None else ([P[0], None, P[1], None] if layout == 0 else [P[0], P[1], P[2], P[3]])
+    return cattn.lib().cattn_rotary(layout, *xs, B, H, T, d, pos0, base, None)
+
+
+def test_rotary_argument_errors():
+    # every call fails validation (or is empty): none reaches a launch
+    assert rot(layout=9) == 3
+    assert rot(base=0.0) == 8
+    assert rot(base=float("nan")) == 8
+    assert rot(pos0=-1) == 8
+    assert rot(pos0=2 ** 41) == 8
+    assert rot(d=0) == 6
+    assert rot(T=-2) == 2
+    assert rot(T=0) == 0
+    assert rot(ptrs=[P[0], P[4], P[1], None]) == 1          # complex64 takes no imaginary plane
+    assert rot(layout=1, ptrs=[P[0], None, P[2], P[3]]) == 1
+    assert rot(ptrs=[P[0], None, P[1] + 8, None]) == 4
+    assert rot(ptrs=[P[0], None, P[0] + 16, None]) == 5     # partial overlap of input and output
+    assert rot(layout=1, ptrs=[P[0], P[1], P[1], P[2]]) == 5   # output real plane over the input imaginary plane
