@@ -23,6 +23,9 @@ to fp64) and computes the plain definitions in complex128:
   differences.
 * :mod:`oracle.rotary` -- the rotary phase embedding ("Show HN: CNET",
   RotaryEmbed).
+* :mod:`oracle.born_linear` -- Born attention with a carried density state:
+  state build, prefill with an incoming state, and the one-token step
+  ("Show HN: CNET", BornAttention's linear and step modes).
 
 Every function here is pinned by the CPU tests against closed forms,
 invariants, hand-derived worked examples and the second formulation.
@@ -33,11 +36,12 @@ from .born_density import born_attention_density
 from .born_grad import born_attention_bwd
 from .pct_grad import pct_attention_bwd
 from .rotary import rotary
+from .born_linear import born_prefill, born_state, born_step
 
 __all__ = [
     "born_attention", "born_attention_rows",
     "pct_attention", "pct_attention_rows", "pct_scores", "pct_softmax_attention", "pct_screen_attention",
     "born_attention_density",
     "born_attention_bwd", "pct_attention_bwd",
-    "rotary",
+    "rotary", "born_state", "born_step", "born_prefill",
 ]

@@ -1,0 +1,63 @@
+"""Born attention with a carried density state: state build, prefill with an
+incoming state, and the one-token step (test infrastructure only).
+
+"Show HN: CNET", BornAttention: the linear mode lifts each key to its outer
+product and carries a running state, giving O(N) memory, an exact result (the
+feature map is finite) and constant-memory autoregressive decoding in step
+mode ("one token in, one token out, the state updated in place");
+"The Quantum Shortcut", section 2: the Born rule as the linear functional
+q^H rho q of the density matrix rho = k k^H.  Per head:
+
+    Z      = sum_j k_j k_j^H                   (d x d, the normaliser state)
+    M[c]   = sum_j V[j, c] k_j k_j^H            (d x d for each value channel c)
+    O[t, c] = q_t^H M_t[c] q_t / (q_t^H Z_t q_t + eps)
+
+where the states at token t hold every key j <= t (the carried state plus the
+tokens of the current call up to t).  Arrays here are per head: q, k, v
+[T, d]; Z [d, d]; M [d, d, d] indexed M[c, a, b].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _c(x):
+    return np.asarray(x, dtype=np.complex128)
+
+
+def born_state(k, v, Z0=None, M0=None):
+    """(Z, M) after adding every token of k, v [T, d] to the state (Z0, M0) (zero if None)."""
+    k, v = _c(k), _c(v)
+    d = k.shape[-1]
+    Z = np.zeros((d, d), np.complex128) if Z0 is None else _c(Z0).copy()
+    M = np.zeros((d, d, d), np.complex128) if M0 is None else _c(M0).copy()
+    for j in range(k.shape[0]):
+        rho = np.outer(k[j], k[j].conj())
+        Z += rho
+        M += v[j][:, None, None] * rho[None, :, :]
+    return Z, M
+
+
+def born_step(q, k, v, Z, M, eps: float = 0.0):
+    """One token: add (k, v) to the state, then read out q.  q, k, v [d].
+    Returns (o [d], Z', M'); o = 0 when the denominator is 0."""
+    q = _c(q)
+    Z, M = born_state(_c(k)[None, :], _c(v)[None, :], Z, M)
+    den = (q.conj() @ Z @ q).real + eps
+    if den == 0.0:
+        return np.zeros(q.shape[-1], np.complex128), Z, M
+    num = np.einsum("a,cab,b->c", q.conj(), M, q)
+    return num / den, Z, M
+
+
+def born_prefill(q, k, v, Z0=None, M0=None, eps: float = 0.0):
+    """Causal Born over a sequence whose keys before token 0 are summarised by
+    the state (Z0, M0): each token is one step.  Returns (O [T, d], Z, M)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    d = q.shape[-1]
+    Z = np.zeros((d, d), np.complex128) if Z0 is None else _c(Z0)
+    M = np.zeros((d, d, d), np.complex128) if M0 is None else _c(M0)
+    out = np.zeros(q.shape, np.complex128)
+    for t in range(q.shape[0]):
+        out[t], Z, M = born_step(q[t], k[t], v[t], Z, M, eps)
+    return out, Z, M
