@@ -310,6 +310,125 @@ cattn_status cattn_rotary(int layout, const void *x_re, const void *x_im, void *
     return cattn::launch_rotary(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
+namespace {
+
+// Shared checks of the carried-state calls: layout, sizes (d_h <= 64), the
+// complex operands (NULL and alignment rules of the forward), the state and
+// row_den buffers, and that no written buffer overlaps another buffer.
+struct Buf {
+    const void *p;
+    uintptr_t bytes;
+    bool written;
+};
+
+cattn_status check_linear(int layout, int64_t B, int64_t H, int64_t T, int64_t d_h, const void *const *cre,
+                          const void *const *cim, const bool *cwritten, int nc, const Buf *extra, int ne,
+                          cattn::LinearProblem *p, bool *empty) {
+    if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
+    if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
+    if (d_h < 1 || d_h > CATTN_LIN_MAXD) return CATTN_E_UNSUPPORTED;
+    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    const int64_t BH = B * H;
+    if (BH > INT32_MAX) return CATTN_E_SHAPE;
+    const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
+    if (BH != 0 && T > (int64_t)(INT64_MAX / 16) / BH / d_h / elem) return CATTN_E_SHAPE;
+    *empty = BH == 0 || T == 0;
+    if (*empty) return CATTN_OK;
+    const bool c64 = layout == CATTN_LAYOUT_C64;
+    Buf all[16];
+    int n = 0;
+    for (int i = 0; i < nc; ++i) {
+        if (!cre[i] || (c64 ? cim[i] != nullptr : cim[i] == nullptr)) return CATTN_E_NULL;
+        if (!aligned16(cre[i]) || (cim[i] && !aligned16(cim[i]))) return CATTN_E_ALIGN;
+        const uintptr_t bytes = (uintptr_t)(BH * T * d_h * elem);
+        all[n++] = Buf{cre[i], bytes, cwritten[i]};
+        if (cim[i]) all[n++] = Buf{cim[i], bytes, cwritten[i]};
+    }
+    for (int i = 0; i < ne; ++i) {
+        if (!extra[i].p) return CATTN_E_NULL;
+        if (!aligned16(extra[i].p)) return CATTN_E_ALIGN;
+        all[n++] = extra[i];
+    }
+    for (int a = 0; a < n; ++a)
+        for (int b = a + 1; b < n; ++b)
+            if ((all[a].written || all[b].written) &&
+                overlaps(Span{(uintptr_t)all[a].p, (uintptr_t)all[a].p + all[a].bytes},
+                         Span{(uintptr_t)all[b].p, (uintptr_t)all[b].p + all[b].bytes}))
+                return CATTN_E_ALIAS;
+    p->layout = c64 ? cattn::LAYOUT_C64 : cattn::LAYOUT_BF16;
+    p->BH = (int)BH;
+    p->T = (int)T;
+    p->d = (int)d_h;
+    return CATTN_OK;
+}
+
+uintptr_t z_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * d * d * 8); }
+uintptr_t m_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * d * d * d * 8); }
+
+}  // namespace
+
+cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, const void *v_re, const void *v_im,
+                              int64_t B, int64_t H, int64_t T, int64_t d_h, float *Z, float *M, int accumulate,
+                              void *stream) {
+    const void *cre[2] = {k_re, v_re}, *cim[2] = {k_im, v_im};
+    const bool cw[2] = {false, false};
+    const Buf extra[2] = {{Z, z_bytes(B, H, d_h), true}, {M, m_bytes(B, H, d_h), true}};
+    cattn::LinearProblem p{};
+    bool empty = false;
+    if (T == 0 && !accumulate) {
+        // no tokens, overwrite: the state becomes zero (k and v are not read)
+        const cattn_status s = check_linear(layout, B, H, 1, d_h, nullptr, nullptr, nullptr, 0, extra, 2, &p, &empty);
+        if (s != CATTN_OK || empty) return s;
+        p.T = 0;
+    } else {
+        const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 2, &p, &empty);
+        if (s != CATTN_OK || empty) return s;
+    }
+    p.k_re = k_re; p.k_im = k_im; p.v_re = v_re; p.v_im = v_im;
+    p.Z = Z; p.M = M;
+    p.accumulate = accumulate != 0;
+    p.stream = reinterpret_cast<hipStream_t>(stream);
+    return cattn::launch_born_state(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+}
+
+cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, const float *Z, const float *M,
+                              void *o_re, void *o_im, float *row_den, int64_t B, int64_t H, int64_t T, int64_t d_h,
+                              void *stream) {
+    const void *cre[2] = {q_re, o_re}, *cim[2] = {q_im, o_im};
+    const bool cw[2] = {false, true};
+    const Buf extra[3] = {{Z, z_bytes(B, H, d_h), false}, {M, m_bytes(B, H, d_h), false},
+                          {row_den, (uintptr_t)(B * H * T * 4), true}};
+    cattn::LinearProblem p{};
+    bool empty = false;
+    const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 3, &p, &empty);
+    if (s != CATTN_OK || empty) return s;
+    p.q_re = q_re; p.q_im = q_im; p.o_re = o_re; p.o_im = o_im;
+    p.Z = const_cast<float *>(Z); p.M = const_cast<float *>(M);   // read only in this call
+    p.row_den = row_den;
+    p.stream = reinterpret_cast<hipStream_t>(stream);
+    return cattn::launch_born_merge(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+}
+
+cattn_status cattn_born_step(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
+                             const void *v_re, const void *v_im, void *o_re, void *o_im, float *Z, float *M,
+                             float *row_den, int64_t B, int64_t H, int64_t d_h, float eps, void *stream) {
+    if (!isfinite(eps) || eps < 0.f) return CATTN_E_ARG;
+    const void *cre[4] = {q_re, k_re, v_re, o_re}, *cim[4] = {q_im, k_im, v_im, o_im};
+    const bool cw[4] = {false, false, false, true};
+    const Buf extra[3] = {{Z, z_bytes(B, H, d_h), true}, {M, m_bytes(B, H, d_h), true},
+                          {row_den, (uintptr_t)(B * H * 4), true}};
+    cattn::LinearProblem p{};
+    bool empty = false;
+    const cattn_status s = check_linear(layout, B, H, 1, d_h, cre, cim, cw, 4, extra, 3, &p, &empty);
+    if (s != CATTN_OK || empty) return s;
+    p.q_re = q_re; p.q_im = q_im; p.k_re = k_re; p.k_im = k_im; p.v_re = v_re; p.v_im = v_im;
+    p.o_re = o_re; p.o_im = o_im;
+    p.Z = Z; p.M = M; p.row_den = row_den;
+    p.eps = eps;
+    p.stream = reinterpret_cast<hipStream_t>(stream);
+    return cattn::launch_born_step(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+}
+
 const char *cattn_status_str(int status) {
     switch (status) {
         case CATTN_OK: return "ok";
@@ -318,13 +437,13 @@ const char *cattn_status_str(int status) {
         case CATTN_E_LAYOUT: return "unknown layout";
         case CATTN_E_ALIGN: return "pointer not 16-byte aligned";
         case CATTN_E_ALIAS: return "an output overlaps an input or another output";
-        case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128";
+        case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128 (1..64 for the carried-state calls)";
         case CATTN_E_LAUNCH: return "HIP kernel launch failed";
         case CATTN_E_ARG: return "a scalar argument out of range (eps, bias, gate parameters, rotary base or position) or an unknown gate";
         default: return "unknown status";
     }
 }
 
-int cattn_abi_version(void) { return 4; }
+int cattn_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -90,4 +90,25 @@ struct RotaryProblem {
 
 hipError_t launch_rotary(const RotaryProblem &p);
 
+// Born attention with a carried density state (state build, merge, step).
+#define CATTN_LIN_MAXD 64
+struct LinearProblem {
+    int layout;
+    const void *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
+    void *o_re, *o_im;
+    float *Z;          // [BH, d, d] complex64 (interleaved)
+    float *M;          // [BH, d, d, d] complex64, M[c][a][b]
+    float *row_den;    // merge: [BH * T] in/out; step: [BH] out
+    int BH;
+    int T;
+    int d;
+    int accumulate;    // state build: add to the state instead of overwriting it
+    float eps;         // step
+    hipStream_t stream;
+};
+
+hipError_t launch_born_state(const LinearProblem &p);
+hipError_t launch_born_merge(const LinearProblem &p);
+hipError_t launch_born_step(const LinearProblem &p);
+
 }  // namespace cattn

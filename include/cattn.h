@@ -58,7 +58,7 @@ typedef enum {
     CATTN_E_LAYOUT = 3,      /* unknown layout value */
     CATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
-    CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 */
+    CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 (1..64 for the carried-state calls) */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
     CATTN_E_ARG = 8          /* a scalar out of range: eps, bias, a gate parameter, rotary base or position; or an unknown gate */
 } cattn_status;
@@ -209,10 +209,61 @@ cattn_status cattn_rotary(int layout,
                           int64_t B, int64_t H, int64_t T, int64_t d_h,
                           int64_t pos0, float base, void *stream);
 
+/*
+ * Born attention with a carried density state ("Show HN: CNET",
+ * BornAttention's linear and step modes: each key lifted to its outer
+ * product, a running state, constant-memory decoding; "The Quantum Shortcut",
+ * section 2: the Born rule as q^H rho q with rho = k k^H).  Per head:
+ *     Z    = sum_j k_j k_j^H            (d_h x d_h)
+ *     M[c] = sum_j V[j,c] k_j k_j^H      (d_h x d_h per value channel c)
+ *     O[t,c] = q_t^H M_t[c] q_t / (q_t^H Z_t q_t + eps)
+ * where the states at token t hold the carried keys and every key of the
+ * sequence up to t.  This is exactly Born attention (the feature map is
+ * finite), with O(1) memory per decoded token.
+ *
+ * State buffers (device, caller-owned, interleaved complex64):
+ *     Z [B, H, d_h, d_h]        M [B, H, d_h, d_h, d_h]  (M[c][a][b])
+ * The carried-state calls take 1 <= d_h <= 64 (the state is d_h^3 complex
+ * values per head: 2 MiB at 64).
+ *
+ * cattn_born_state: Z, M over the T tokens of k, v; accumulate != 0 adds to
+ *     the buffers' contents, 0 overwrites them (T = 0 then zeroes the state,
+ *     and k, v may be NULL).
+ * cattn_born_merge: prefill with an incoming state.  Given the output O and
+ *     row denominators l of cattn_born_fwd (causal) over this call's tokens,
+ *     folds in the incoming state (Z, M):
+ *         O <- (O l + q^H M q) / (l + q^H Z q),   l <- l + q^H Z q.
+ *     Then cattn_born_state(accumulate = 1) carries the call's own tokens out.
+ * cattn_born_step: one token per head (q, k, v, o are [B, H, 1, d_h]): adds
+ *     (k, v) to the state in place, then writes o and row_den[b*H + h] =
+ *     q^H Z q + eps.  For bf16 the numerator is rounded once to bf16 before
+ *     the division (a second rounding of o).
+ * Written buffers must not overlap any other buffer of the call.
+ */
+cattn_status cattn_born_state(int layout,
+                              const void *k_re, const void *k_im,
+                              const void *v_re, const void *v_im,
+                              int64_t B, int64_t H, int64_t T, int64_t d_h,
+                              float *Z, float *M, int accumulate, void *stream);
+
+cattn_status cattn_born_merge(int layout,
+                              const void *q_re, const void *q_im,
+                              const float *Z, const float *M,
+                              void *o_re, void *o_im, float *row_den,
+                              int64_t B, int64_t H, int64_t T, int64_t d_h, void *stream);
+
+cattn_status cattn_born_step(int layout,
+                             const void *q_re, const void *q_im,
+                             const void *k_re, const void *k_im,
+                             const void *v_re, const void *v_im,
+                             void *o_re, void *o_im,
+                             float *Z, float *M, float *row_den,
+                             int64_t B, int64_t H, int64_t d_h, float eps, void *stream);
+
 /* Static, NUL-terminated description of a status value (never NULL). */
 const char *cattn_status_str(int status);
 
-/* ABI version of this header: 4 (2 added the backward, 3 the PCT gates, 4 rotary). */
+/* ABI version of this header: 5 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus
