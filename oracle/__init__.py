@@ -36,7 +36,8 @@ from .born_density import born_attention_density
 from .born_grad import born_attention_bwd
 from .pct_grad import pct_attention_bwd
 from .rotary import rotary
-from .born_linear import born_prefill, born_state, born_step
+from .born_linear import (born_prefill, born_state, born_step, pack_hermitian, pack_state,
+                          unpack_hermitian, unpack_state)
 
 __all__ = [
     "born_attention", "born_attention_rows",
@@ -44,4 +45,5 @@ __all__ = [
     "born_attention_density",
     "born_attention_bwd", "pct_attention_bwd",
     "rotary", "born_state", "born_step", "born_prefill",
+    "pack_hermitian", "unpack_hermitian", "pack_state", "unpack_state",
 ]

@@ -15,6 +15,15 @@ q^H rho q of the density matrix rho = k k^H.  Per head:
 where the states at token t hold every key j <= t (the carried state plus the
 tokens of the current call up to t).  Arrays here are per head: q, k, v
 [T, d]; Z [d, d]; M [d, d, d] indexed M[c, a, b].
+
+Packed real form of the state (the layout the device library carries).  Z is
+Hermitian and each M[c] splits into two Hermitian parts,
+M[c] = X_c + i X_{d+c} with X_c = (M[c] + M[c]^H) / 2 and
+X_{d+c} = (M[c] - M[c]^H) / (2i) (the sums of k k^H weighted by Re V[:, c] and
+by Im V[:, c]); X_{2d} = Z.  A Hermitian d x d matrix X has d^2 real degrees
+of freedom, stored as a real d x d matrix P with P[a, b] = Re X[a, b] for
+a <= b and P[a, b] = Im X[b, a] for a > b.  The packed state is S[n] = P(X_n)
+for n = 0 .. 2d, shape [2d + 1, d, d].
 """
 from __future__ import annotations
 
@@ -61,3 +70,44 @@ def born_prefill(q, k, v, Z0=None, M0=None, eps: float = 0.0):
     for t in range(q.shape[0]):
         out[t], Z, M = born_step(q[t], k[t], v[t], Z, M, eps)
     return out, Z, M
+
+
+def pack_hermitian(X):
+    """P(X) for a Hermitian X [d, d]: Re on and above the diagonal, Im of the
+    transposed entry below it."""
+    X = _c(X)
+    up = np.triu(np.ones(X.shape, bool))
+    return np.where(up, X.real, X.T.imag)
+
+
+def unpack_hermitian(P):
+    """The Hermitian X whose packed form is P."""
+    P = np.asarray(P, dtype=np.float64)
+    d = P.shape[-1]
+    X = np.zeros((d, d), np.complex128)
+    for a in range(d):
+        X[a, a] = P[a, a]
+        for b in range(a + 1, d):
+            X[a, b] = P[a, b] + 1j * P[b, a]
+            X[b, a] = np.conj(X[a, b])
+    return X
+
+
+def pack_state(Z, M):
+    """Packed real state S [2d + 1, d, d] of (Z, M)."""
+    Z, M = _c(Z), _c(M)
+    d = Z.shape[-1]
+    S = np.zeros((2 * d + 1, d, d))
+    for c in range(d):
+        S[c] = pack_hermitian((M[c] + M[c].conj().T) / 2)
+        S[d + c] = pack_hermitian((M[c] - M[c].conj().T) / 2j)
+    S[2 * d] = pack_hermitian(Z)
+    return S
+
+
+def unpack_state(S):
+    """(Z, M) of a packed state S [2d + 1, d, d]."""
+    S = np.asarray(S, dtype=np.float64)
+    d = S.shape[-1]
+    M = np.stack([unpack_hermitian(S[c]) + 1j * unpack_hermitian(S[d + c]) for c in range(d)])
+    return unpack_hermitian(S[2 * d]), M

@@ -6,7 +6,8 @@ trace = sum |k|^2, M[c] is the v-weighted sum); planted mistakes fail."""
 import numpy as np
 import pytest
 
-from oracle import born_attention, born_prefill, born_state, born_step
+from oracle import (born_attention, born_prefill, born_state, born_step, pack_hermitian, pack_state,
+                    unpack_hermitian, unpack_state)
 
 
 def crandn(rng, *shape):
@@ -75,3 +76,60 @@ def test_planted_mistakes_fail():
     # the outer product unconjugated (k k^T)
     Z2 = sum(np.outer(k[j], k[j]) for j in range(T))
     assert not np.allclose(q[-1].conj() @ Z2 @ q[-1], q[-1].conj() @ born_state(k, v)[0] @ q[-1])
+
+
+def test_packed_hermitian_hand_example():
+    # k = (1, i): k k^H = [[1, -i], [i, 1]]; Re above and on the diagonal, Im of the upper entry below
+    X = np.outer([1, 1j], np.conj([1, 1j]))
+    np.testing.assert_array_equal(X, [[1, -1j], [1j, 1]])
+    np.testing.assert_array_equal(pack_hermitian(X), [[1.0, 0.0], [-1.0, 1.0]])
+    np.testing.assert_array_equal(unpack_hermitian([[1.0, 0.0], [-1.0, 1.0]]), X)
+
+
+def test_packed_state_round_trip_and_parts():
+    rng = np.random.default_rng(75)
+    T, d = 20, 5
+    k, v = crandn(rng, T, d), crandn(rng, T, d)
+    Z, M = born_state(k, v)
+    S = pack_state(Z, M)
+    assert S.shape == (2 * d + 1, d, d) and S.dtype == np.float64
+    Z2, M2 = unpack_state(S)
+    np.testing.assert_allclose(Z2, Z, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(M2, M, rtol=0, atol=1e-12)
+    # the parts are the real- and imaginary-V-weighted sums of outer products
+    ZR, MR = born_state(k, v.real.astype(complex))
+    ZI, MI = born_state(k, v.imag.astype(complex))
+    for c in range(d):
+        np.testing.assert_allclose(S[c], pack_hermitian(MR[c]), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(S[d + c], pack_hermitian(MI[c]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S[2 * d], pack_hermitian(Z), rtol=0, atol=1e-12)
+
+
+def test_packed_form_carries_the_quadratic_form():
+    """q^H X q = sum_a |q_a|^2 P[a, a] + 2 sum_{a != b} phi_ab(q) P[a, b] with
+    phi_ab(q) = Re(q_a conj q_b) for a < b and Im(q_b conj q_a) for a > b: the
+    identity a packed-state readout relies on."""
+    rng = np.random.default_rng(76)
+    d = 7
+    k = crandn(rng, 9, d)
+    X = sum(np.outer(kj, kj.conj()) * w for kj, w in zip(k, rng.standard_normal(9)))
+    P = pack_hermitian(X)
+    for _ in range(5):
+        q = crandn(rng, d)
+        phi = np.empty((d, d))
+        for a in range(d):
+            for b in range(d):
+                phi[a, b] = (q[a] * np.conj(q[b])).real if a <= b else (q[b] * np.conj(q[a])).imag
+        weight = np.where(np.eye(d, dtype=bool), 1.0, 2.0)
+        np.testing.assert_allclose((weight * phi * P).sum(), (q.conj() @ X @ q).real, rtol=1e-12)
+        # and the packed outer product is phi itself: P(q q^H) = phi(q)
+        np.testing.assert_allclose(pack_hermitian(np.outer(q, q.conj())), phi, rtol=0, atol=1e-14)
+
+
+def test_planted_packing_mistake_fails():
+    # storing the lower triangle as +Im of the lower entry (the transpose's sign) breaks the round trip
+    rng = np.random.default_rng(77)
+    q = crandn(rng, 4)
+    X = np.outer(q, q.conj())
+    wrong = np.where(np.triu(np.ones((4, 4), bool)), X.real, X.imag)
+    assert np.abs(unpack_hermitian(wrong) - X).max() > 1e-3
