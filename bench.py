@@ -3,6 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--copy-probe MIB]
     python bench.py --pass bwd [--workload NAME] ...      (the backward instead of the forward)
     python bench.py --workload NAME --gate softmax|screen  (a PCT workload with a sibling gate)
+    python bench.py --pass step [--workload NAME]        (one-token decoding with a carried Born state)
+    python bench.py --pass linear [--workload NAME] [--chunk C]
+                                   (a whole causal Born sequence in chunks with a carried state, beside
+                                    the quadratic kernel on the same inputs)
 
 One step = one call of the fused forward (score GEMM, weight map, Born
 denominator, value GEMM, epilogue: the whole hot path, one kernel launch)
@@ -197,6 +201,221 @@ def main_rotary(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def _chunk(x, t0, t1):
+    """[B, H, t0:t1, d] as a fresh contiguous allocation (complex64 tensor or bf16 plane pair)."""
+    import torch
+    if isinstance(x, tuple):
+        return tuple(p[:, :, t0:t1].clone(memory_format=torch.contiguous_format) for p in x)
+    return x[:, :, t0:t1].clone(memory_format=torch.contiguous_format)
+
+
+def state_flops(T: int, d: int, heads: int) -> float:
+    """Real flops of building (or reading out) the carried state over T tokens:
+    2d + 1 packed real d x d matrices per head, one multiply-add per entry and
+    token (forming the d^2 lifted features of a token is not counted)."""
+    return 2.0 * T * (2 * d + 1) * d * d * heads
+
+
+def state_bytes(d: int, heads: int) -> int:
+    """Bytes of the packed carried state (fp32)."""
+    return (2 * d + 1) * d * d * 4 * heads
+
+
+def main_step(args, w):
+    """One-token decoding with a carried Born state: the state of the workload's
+    T tokens is built once (untimed), then each step adds one token and reads
+    the state out.  HBM-bound: the state is read and written once per step."""
+    import oracle
+    import torch
+    from complex_valued_attention_amd import cattn, inputs as gen
+    from complex_valued_attention_amd.check import TOL, from_device, rowwise_rel_err, to_device
+    from threadpoolctl import threadpool_info
+    if w.op != "born" or w.d_h > 64:
+        print("--pass step needs a Born workload with d_h <= 64", file=sys.stderr)
+        sys.exit(2)
+    cattn.lib()
+    inp = gen.make_inputs(w)
+    q, k, v = to_device(inp)
+    B, H, T, d = w.B, w.H, w.T, w.d_h
+    n = args.warmup + args.steps
+    if n > T:
+        print(f"--warmup + --steps must not exceed T = {T}", file=sys.stderr)
+        sys.exit(2)
+    S = cattn.born_state_buffer(B, H, d)
+    cattn.born_state(k, v, S)
+    # the new tokens: the workload's first n tokens again, one fresh [B, H, 1, d] tensor each
+    toks = [tuple(_chunk(x, t, t + 1) for x in (q, k, v)) for t in range(n)]
+    outs = [cattn._like(toks[0][0]) for _ in range(n)]
+    dens = torch.empty(n, B * H, dtype=torch.float32, device="cuda")
+    for i in range(args.warmup):
+        cattn.born_step(*toks[i], S, out=outs[i], row_den=dens[i])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.warmup, n):
+        cattn.born_step(*toks[i], S, out=outs[i], row_den=dens[i])
+        ev[i - args.warmup + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    heads = B * H
+    elem = 8 if w.layout == "c64" else 4
+    nbytes = 2 * state_bytes(d, heads) + 4 * heads * d * elem + 4 * heads   # state in and out, q k v o, row_den
+    gbs = nbytes / (float(np.mean(per)) * 1e-3) / 1e9
+    log(f"[bench] step {w.name}: {ms:.4f} ms/step ({heads} heads, state {state_bytes(d, heads) / 2**20:.0f} MiB), "
+        f"{gbs:.0f} GB/s")
+    # oracle: head (0, 0) through the same T-token prefix and every step (its
+    # outputs compared with the device's); then more steps on the workload's
+    # tokens until about 12 s of host time, the CPU baseline
+    b, h = 0, 0
+    Zo, Mo = oracle.born_state(inp.k64[b, h], inp.v64[b, h])
+    t_used, err, n_cpu = 0.0, 0.0, 0
+    while n_cpu < n or (t_used < 12.0 and n_cpu < T):
+        t0 = time.perf_counter()
+        o_ref, Zo, Mo = oracle.born_step(inp.q64[b, h, n_cpu], inp.k64[b, h, n_cpu], inp.v64[b, h, n_cpu], Zo, Mo)
+        t_used += time.perf_counter() - t0
+        if n_cpu < n:
+            err = max(err, rowwise_rel_err(from_device(outs[n_cpu])[b, h], o_ref[None]))
+        n_cpu += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    rec = {"metric": f"Born carried-state decode tokens/s ({w.name} state)", "value": heads / (ms * 1e-3),
+           "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic (the workload's tokens as prefix and as new tokens)",
+           "config": {"workload": w.name, "pass": "step", "B": B, "H": H, "prefix_T": T, "d_h": d,
+                      "layout": w.layout, "state_MiB": state_bytes(d, heads) / 2**20},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "born_step_kernel",
+                        "bytes_per_step": nbytes, "kernel_ms_mean": float(np.mean(per)),
+                        "kernel_ms_median": float(np.median(per))},
+           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads), "kind": "oracle",
+                            "sample": f"head (0,0), {n_cpu} steps after the {T}-token prefix, fp64 numpy, "
+                                      f"{t_used:.1f} s", "gpu_rowwise_rel_err": err,
+                            "gpu_parity_pass": bool(err <= TOL[w.layout])}}
+    print(json.dumps(rec), flush=True)
+
+
+def main_linear(args, w):
+    """A whole causal Born sequence in chunks of C tokens with a carried state:
+    per chunk the quadratic kernel over the chunk, the merge of the incoming
+    state, and the state update; beside it the quadratic kernel over the whole
+    sequence on the same inputs."""
+    import oracle
+    import torch
+    from complex_valued_attention_amd import cattn, inputs as gen
+    from complex_valued_attention_amd.check import TOL, from_device, rowwise_rel_err, sample_rows, to_device
+    from threadpoolctl import threadpool_info
+    if w.op != "born" or not w.causal or w.d_h > 64:
+        print("--pass linear needs a causal Born workload with d_h <= 64", file=sys.stderr)
+        sys.exit(2)
+    cattn.lib()
+    inp = gen.make_inputs(w)
+    q, k, v = to_device(inp)
+    B, H, T, d, C = w.B, w.H, w.T, w.d_h, args.chunk
+    nc = (T + C - 1) // C
+    chunks = [tuple(_chunk(x, i * C, min(T, (i + 1) * C)) for x in (q, k, v)) for i in range(nc)]
+    outs = [cattn._like(c[0]) for c in chunks]
+    dens = [torch.empty(B * H * min(C, T - i * C), dtype=torch.float32, device="cuda") for i in range(nc)]
+    S = cattn.born_state_buffer(B, H, d)
+    stream = torch.cuda.current_stream()
+    kinds = ("fwd", "merge", "state")
+
+    def chunked(evs=None):
+        for i, (qc, kc, vc) in enumerate(chunks):
+            marks = []
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+            cattn.born_fwd(qc, kc, vc, causal=True, out=outs[i], row_den=dens[i])
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+            if i:
+                cattn.born_merge(qc, S, outs[i], dens[i])
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+            if i + 1 < nc:
+                cattn.born_state(kc, vc, S, accumulate=i > 0)
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+                evs.append(marks)
+
+    full_out = cattn._like(q)
+    quad = lambda: cattn.born_fwd(q, k, v, causal=True, out=full_out)
+    for _ in range(args.warmup):
+        chunked()
+        quad()
+    torch.cuda.synchronize()
+    # the chunked form, whole passes timed
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        chunked()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    # per-kind kernel time (a separate pass with events between the launches)
+    evs = []
+    chunked(evs)
+    torch.cuda.synchronize()
+    part = {kd: sum(m[j].elapsed_time(m[j + 1]) for m in evs) for j, kd in enumerate(kinds)}
+    # the quadratic kernel over the whole sequence
+    eq = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    eq[0].record(stream)
+    for i in range(args.steps):
+        quad()
+        eq[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_quad = eq[0].elapsed_time(eq[-1]) / args.steps
+    heads = B * H
+    tok_s = heads * T / (ms * 1e-3)
+    log(f"[bench] linear {w.name} chunk {C}: {ms:.3f} ms/pass ({tok_s / 1e6:.2f} M head-tokens/s); "
+        f"quadratic {ms_quad:.3f} ms; parts {part}")
+    # parity: the chunked output against the quadratic kernel's on every row,
+    # and sampled rows against the oracle
+    got = np.concatenate([from_device(o) for o in outs], axis=2)
+    quad_got = from_device(full_out)
+    err_quad = rowwise_rel_err(got, quad_got)
+    rows = sample_rows(B, H, T, 32, seed=w.seed, tile=C)
+    t0 = time.perf_counter()
+    ref = oracle.born_attention_rows(inp.q64, inp.k64, inp.v64, rows, causal=True)
+    t_rows = time.perf_counter() - t0
+    err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
+    # CPU baseline: the oracle's own carried-state recursion on the first tokens of head (0, 0)
+    n_cpu, t_used = 0, 0.0
+    Zo, Mo = np.zeros((d, d), complex), np.zeros((d, d, d), complex)
+    while t_used < 12.0 and n_cpu < T:
+        t0 = time.perf_counter()
+        _, Zo, Mo = oracle.born_step(inp.q64[0, 0, n_cpu], inp.k64[0, 0, n_cpu], inp.v64[0, 0, n_cpu], Zo, Mo)
+        t_used += time.perf_counter() - t0
+        n_cpu += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    dom = max(("merge", "state"), key=lambda kd: part[kd])
+    n_launch = nc - 1
+    dom_ms = part[dom] / n_launch
+    dom_flops = state_flops(C, d, heads)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    rec = {"metric": f"Born chunked carried-state prefill head-tokens/s ({w.name}, chunk {C})",
+           "value": tok_s, "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.layout == "bf16" else "f32",
+           "data": "synthetic (seeded complex Gaussian, unit-norm rotary Q/K)" if w.rotary else "synthetic",
+           "config": {"workload": w.name, "pass": "linear", "B": B, "H": H, "T": T, "d_h": d, "layout": w.layout,
+                      "chunk": C, "chunks": nc},
+           "quadratic_ms": ms_quad, "speedup_vs_quadratic": ms_quad / ms,
+           "parts_ms": part,
+           "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_TFLOPS["c64"], "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_TFLOPS["c64"], "traffic": None,
+                        "kernel": f"born_{dom}_kernel", "kernel_ms_mean": dom_ms},
+           "gpu_vs_quadratic_rowwise_rel_err": err_quad,
+           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads),
+                            "kind": "oracle",
+                            "sample": f"head (0,0), first {n_cpu} tokens by the oracle's step recursion, "
+                                      f"fp64 numpy, {t_used:.1f} s; {len(rows)} sampled rows by the quadratic "
+                                      f"definition in {t_rows:.1f} s",
+                            "gpu_rowwise_rel_err": err, "gpu_parity_pass": bool(err <= TOL[w.layout])}}
+    print(json.dumps(rec), flush=True)
+
+
 def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid"):
     import torch
     from complex_valued_attention_amd import cattn, inputs as gen
@@ -272,7 +491,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "rotary"], default="fwd")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "rotary", "step", "linear"], default="fwd")
+    ap.add_argument("--chunk", type=int, default=4096, help="--pass linear: tokens per chunk")
     ap.add_argument("--gate", choices=["sigmoid", "softmax", "screen"], default="sigmoid",
                     help="PCT workloads: the gate on the scaled cosine score")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -294,6 +514,14 @@ def main():
         return
     if args.which == "rotary":
         main_rotary(args, w)
+        return
+    if args.which == "step":
+        main_step(args, w)
+        return
+    if args.which == "linear":
+        if args.workload is None:
+            w = gen.WORKLOADS["born_causal_bf16_b1h16t32768d64_rotary"]
+        main_linear(args, w)
         return
     if args.gate != "sigmoid" and w.op != "pct":
         print("--gate applies to PCT workloads only", file=sys.stderr)

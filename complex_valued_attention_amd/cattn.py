@@ -57,11 +57,11 @@ def lib() -> ctypes.CDLL:
     L.cattn_pct_gate_fwd.restype = ctypes.c_int
     L.cattn_rotary.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
     L.cattn_rotary.restype = ctypes.c_int
-    L.cattn_born_state.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_int, vp]
+    L.cattn_born_state.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp]
     L.cattn_born_state.restype = ctypes.c_int
-    L.cattn_born_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.cattn_born_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.cattn_born_merge.restype = ctypes.c_int
-    L.cattn_born_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+    L.cattn_born_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                   ctypes.c_float, vp]
     L.cattn_born_step.restype = ctypes.c_int
     L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
@@ -188,61 +188,55 @@ def rotary(x, pos0: int = 0, base: float = 10000.0, out=None):
     return out
 
 
-def born_state_buffers(B: int, H: int, d: int, device="cuda"):
-    """Zeroed carried-state buffers (Z, M) as complex64 tensors [B, H, d, d] and [B, H, d, d, d]."""
+def born_state_buffer(B: int, H: int, d: int, device="cuda"):
+    """A zeroed packed carried state: float32 [B, H, 2d + 1, d, d]."""
     import torch
-    return (torch.zeros(B, H, d, d, dtype=torch.complex64, device=device),
-            torch.zeros(B, H, d, d, d, dtype=torch.complex64, device=device))
+    return torch.zeros(B, H, 2 * d + 1, d, d, dtype=torch.float32, device=device)
 
 
-def _state_ptrs(Z, M, B, H, d):
+def _state_ptr(S, B, H, d):
     import torch
-    if Z.dtype != torch.complex64 or M.dtype != torch.complex64 or not (Z.is_contiguous() and M.is_contiguous()):
-        raise ValueError("Z and M must be contiguous complex64 tensors")
-    if tuple(Z.shape) != (B, H, d, d) or tuple(M.shape) != (B, H, d, d, d):
-        raise ValueError("Z must be [B, H, d, d] and M [B, H, d, d, d]")
-    return _ptr(Z), _ptr(M)
+    if S.dtype != torch.float32 or not S.is_contiguous() or tuple(S.shape) != (B, H, 2 * d + 1, d, d):
+        raise ValueError("the state must be a contiguous float32 tensor [B, H, 2d + 1, d, d]")
+    return _ptr(S)
 
 
-def born_state(k, v, Z, M, accumulate: bool = False):
-    """cattn_born_state: Z, M over the tokens of k, v (added to their contents if accumulate)."""
+def born_state(k, v, S, accumulate: bool = False):
+    """cattn_born_state: the packed state of the tokens of k, v (added to S's contents if accumulate)."""
     lk, kre, kim, shape = _unpack(k, "k")
     lv, vre, vim, sv = _unpack(v, "v")
     if lk != lv or shape != sv or len(shape) != 4:
         raise ValueError("k and v must share a layout and a [B, H, T, d] shape")
     B, H, T, d = shape
-    zp, mp = _state_ptrs(Z, M, B, H, d)
-    _check(lib().cattn_born_state(lk, _ptr(kre), _ptr(kim), _ptr(vre), _ptr(vim), B, H, T, d, zp, mp,
-                                  int(bool(accumulate)), _stream(kre)))
-    return Z, M
+    _check(lib().cattn_born_state(lk, _ptr(kre), _ptr(kim), _ptr(vre), _ptr(vim), B, H, T, d,
+                                  _state_ptr(S, B, H, d), int(bool(accumulate)), _stream(kre)))
+    return S
 
 
-def born_merge(q, Z, M, o, row_den):
-    """cattn_born_merge: fold the incoming state (Z, M) into a causal forward's o and row_den, in place."""
+def born_merge(q, S, o, row_den):
+    """cattn_born_merge: fold the incoming state S into a causal forward's o and row_den, in place."""
     lq, qre, qim, shape = _unpack(q, "q")
     lo, ore, oim, so = _unpack(o, "o")
     if lq != lo or shape != so or len(shape) != 4:
         raise ValueError("q and o must share a layout and a [B, H, T, d] shape")
     B, H, T, d = shape
-    zp, mp = _state_ptrs(Z, M, B, H, d)
     if row_den.numel() != B * H * T or not row_den.is_contiguous():
         raise ValueError("row_den must be the forward's contiguous float32 tensor of B*H*T elements")
-    _check(lib().cattn_born_merge(lq, _ptr(qre), _ptr(qim), zp, mp, _ptr(ore), _ptr(oim), _ptr(row_den),
-                                  B, H, T, d, _stream(qre)))
+    _check(lib().cattn_born_merge(lq, _ptr(qre), _ptr(qim), _state_ptr(S, B, H, d), _ptr(ore), _ptr(oim),
+                                  _ptr(row_den), B, H, T, d, _stream(qre)))
     return o, row_den
 
 
-def born_step(q, k, v, Z, M, eps: float = 0.0, out=None, row_den=None):
-    """cattn_born_step: one token per head ([B, H, 1, d]); updates Z, M in place, returns (o, row_den)."""
+def born_step(q, k, v, S, eps: float = 0.0, out=None, row_den=None):
+    """cattn_born_step: one token per head ([B, H, 1, d]); updates S in place, returns (o, row_den)."""
     import torch
     layout, ts, (B, H, T, d), out = _prepare(q, k, v, out)
     if T != 1:
         raise ValueError("born_step takes one token per head: [B, H, 1, d]")
-    zp, mp = _state_ptrs(Z, M, B, H, d)
     if row_den is None:
         row_den = torch.empty(B * H, dtype=torch.float32, device=ts[0].device)
-    _check(lib().cattn_born_step(layout, *[_ptr(t) for t in ts], zp, mp, _ptr(row_den), B, H, d, float(eps),
-                                 _stream(ts[0])))
+    _check(lib().cattn_born_step(layout, *[_ptr(t) for t in ts], _state_ptr(S, B, H, d), _ptr(row_den), B, H, d,
+                                 float(eps), _stream(ts[0])))
     return out, row_den
 
 

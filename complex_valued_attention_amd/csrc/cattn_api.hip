@@ -362,68 +362,64 @@ cattn_status check_linear(int layout, int64_t B, int64_t H, int64_t T, int64_t d
     return CATTN_OK;
 }
 
-uintptr_t z_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * d * d * 8); }
-uintptr_t m_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * d * d * d * 8); }
+uintptr_t s_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * (2 * d + 1) * d * d * 4); }
 
 }  // namespace
 
 cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, const void *v_re, const void *v_im,
-                              int64_t B, int64_t H, int64_t T, int64_t d_h, float *Z, float *M, int accumulate,
-                              void *stream) {
+                              int64_t B, int64_t H, int64_t T, int64_t d_h, float *S, int accumulate, void *stream) {
     const void *cre[2] = {k_re, v_re}, *cim[2] = {k_im, v_im};
     const bool cw[2] = {false, false};
-    const Buf extra[2] = {{Z, z_bytes(B, H, d_h), true}, {M, m_bytes(B, H, d_h), true}};
+    const Buf extra[1] = {{S, s_bytes(B, H, d_h), true}};
     cattn::LinearProblem p{};
     bool empty = false;
     if (T == 0 && !accumulate) {
         // no tokens, overwrite: the state becomes zero (k and v are not read)
-        const cattn_status s = check_linear(layout, B, H, 1, d_h, nullptr, nullptr, nullptr, 0, extra, 2, &p, &empty);
+        const cattn_status s = check_linear(layout, B, H, 1, d_h, nullptr, nullptr, nullptr, 0, extra, 1, &p, &empty);
         if (s != CATTN_OK || empty) return s;
         p.T = 0;
     } else {
-        const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 2, &p, &empty);
+        const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 1, &p, &empty);
         if (s != CATTN_OK || empty) return s;
     }
     p.k_re = k_re; p.k_im = k_im; p.v_re = v_re; p.v_im = v_im;
-    p.Z = Z; p.M = M;
+    p.S = S;
     p.accumulate = accumulate != 0;
     p.stream = reinterpret_cast<hipStream_t>(stream);
     return cattn::launch_born_state(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
-cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, const float *Z, const float *M,
-                              void *o_re, void *o_im, float *row_den, int64_t B, int64_t H, int64_t T, int64_t d_h,
+cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, const float *S, void *o_re,
+                              void *o_im, float *row_den, int64_t B, int64_t H, int64_t T, int64_t d_h,
                               void *stream) {
     const void *cre[2] = {q_re, o_re}, *cim[2] = {q_im, o_im};
     const bool cw[2] = {false, true};
-    const Buf extra[3] = {{Z, z_bytes(B, H, d_h), false}, {M, m_bytes(B, H, d_h), false},
-                          {row_den, (uintptr_t)(B * H * T * 4), true}};
+    const Buf extra[2] = {{S, s_bytes(B, H, d_h), false}, {row_den, (uintptr_t)(B * H * T * 4), true}};
     cattn::LinearProblem p{};
     bool empty = false;
-    const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 3, &p, &empty);
+    const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 2, &p, &empty);
     if (s != CATTN_OK || empty) return s;
     p.q_re = q_re; p.q_im = q_im; p.o_re = o_re; p.o_im = o_im;
-    p.Z = const_cast<float *>(Z); p.M = const_cast<float *>(M);   // read only in this call
+    p.S = const_cast<float *>(S);   // read only in this call
     p.row_den = row_den;
     p.stream = reinterpret_cast<hipStream_t>(stream);
     return cattn::launch_born_merge(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
 cattn_status cattn_born_step(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
-                             const void *v_re, const void *v_im, void *o_re, void *o_im, float *Z, float *M,
+                             const void *v_re, const void *v_im, void *o_re, void *o_im, float *S,
                              float *row_den, int64_t B, int64_t H, int64_t d_h, float eps, void *stream) {
     if (!isfinite(eps) || eps < 0.f) return CATTN_E_ARG;
     const void *cre[4] = {q_re, k_re, v_re, o_re}, *cim[4] = {q_im, k_im, v_im, o_im};
     const bool cw[4] = {false, false, false, true};
-    const Buf extra[3] = {{Z, z_bytes(B, H, d_h), true}, {M, m_bytes(B, H, d_h), true},
-                          {row_den, (uintptr_t)(B * H * 4), true}};
+    const Buf extra[2] = {{S, s_bytes(B, H, d_h), true}, {row_den, (uintptr_t)(B * H * 4), true}};
     cattn::LinearProblem p{};
     bool empty = false;
-    const cattn_status s = check_linear(layout, B, H, 1, d_h, cre, cim, cw, 4, extra, 3, &p, &empty);
+    const cattn_status s = check_linear(layout, B, H, 1, d_h, cre, cim, cw, 4, extra, 2, &p, &empty);
     if (s != CATTN_OK || empty) return s;
     p.q_re = q_re; p.q_im = q_im; p.k_re = k_re; p.k_im = k_im; p.v_re = v_re; p.v_im = v_im;
     p.o_re = o_re; p.o_im = o_im;
-    p.Z = Z; p.M = M; p.row_den = row_den;
+    p.S = S; p.row_den = row_den;
     p.eps = eps;
     p.stream = reinterpret_cast<hipStream_t>(stream);
     return cattn::launch_born_step(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
@@ -444,6 +440,6 @@ const char *cattn_status_str(int status) {
     }
 }
 
-int cattn_abi_version(void) { return 5; }
+int cattn_abi_version(void) { return 6; }
 
 }  // extern "C"

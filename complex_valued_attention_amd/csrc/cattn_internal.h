@@ -96,8 +96,7 @@ struct LinearProblem {
     int layout;
     const void *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
     void *o_re, *o_im;
-    float *Z;          // [BH, d, d] complex64 (interleaved)
-    float *M;          // [BH, d, d, d] complex64, M[c][a][b]
+    float *S;          // packed state [BH, 2d + 1, d, d] fp32
     float *row_den;    // merge: [BH * T] in/out; step: [BH] out
     int BH;
     int T;

@@ -221,17 +221,22 @@ cattn_status cattn_rotary(int layout,
  * sequence up to t.  This is exactly Born attention (the feature map is
  * finite), with O(1) memory per decoded token.
  *
- * State buffers (device, caller-owned, interleaved complex64):
- *     Z [B, H, d_h, d_h]        M [B, H, d_h, d_h, d_h]  (M[c][a][b])
- * The carried-state calls take 1 <= d_h <= 64 (the state is d_h^3 complex
- * values per head: 2 MiB at 64).
+ * State layout (device, caller-owned, fp32): S [B, H, 2 d_h + 1, d_h, d_h],
+ * 2 d_h + 1 real matrices per head, each the packed form of a Hermitian
+ * matrix X_n:
+ *     X_c        = sum_j Re V[j,c] k_j k_j^H     (n = c < d_h)
+ *     X_{d_h+c}  = sum_j Im V[j,c] k_j k_j^H     (so M[c] = X_c + i X_{d_h+c})
+ *     X_{2 d_h}  = Z
+ * packed as S[n][a][b] = Re X_n[a][b] for a <= b and Im X_n[b][a] for a > b.
+ * The state is (2 d_h + 1) d_h^2 floats per head: 2.02 MiB at d_h = 64.
+ * The carried-state calls take 1 <= d_h <= 64.
  *
- * cattn_born_state: Z, M over the T tokens of k, v; accumulate != 0 adds to
- *     the buffers' contents, 0 overwrites them (T = 0 then zeroes the state,
- *     and k, v may be NULL).
+ * cattn_born_state: S over the T tokens of k, v; accumulate != 0 adds to the
+ *     buffer's contents, 0 overwrites it (T = 0 then zeroes the state, and
+ *     k, v may be NULL).
  * cattn_born_merge: prefill with an incoming state.  Given the output O and
  *     row denominators l of cattn_born_fwd (causal) over this call's tokens,
- *     folds in the incoming state (Z, M):
+ *     folds in the incoming state:
  *         O <- (O l + q^H M q) / (l + q^H Z q),   l <- l + q^H Z q.
  *     Then cattn_born_state(accumulate = 1) carries the call's own tokens out.
  * cattn_born_step: one token per head (q, k, v, o are [B, H, 1, d_h]): adds
@@ -244,11 +249,11 @@ cattn_status cattn_born_state(int layout,
                               const void *k_re, const void *k_im,
                               const void *v_re, const void *v_im,
                               int64_t B, int64_t H, int64_t T, int64_t d_h,
-                              float *Z, float *M, int accumulate, void *stream);
+                              float *S, int accumulate, void *stream);
 
 cattn_status cattn_born_merge(int layout,
                               const void *q_re, const void *q_im,
-                              const float *Z, const float *M,
+                              const float *S,
                               void *o_re, void *o_im, float *row_den,
                               int64_t B, int64_t H, int64_t T, int64_t d_h, void *stream);
 
@@ -257,13 +262,14 @@ cattn_status cattn_born_step(int layout,
                              const void *k_re, const void *k_im,
                              const void *v_re, const void *v_im,
                              void *o_re, void *o_im,
-                             float *Z, float *M, float *row_den,
+                             float *S, float *row_den,
                              int64_t B, int64_t H, int64_t d_h, float eps, void *stream);
 
 /* Static, NUL-terminated description of a status value (never NULL). */
 const char *cattn_status_str(int status);
 
-/* ABI version of this header: 5 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state). */
+/* ABI version of this header: 6 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state,
+   6 its packed real layout). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 5
+    assert L.cattn_abi_version() == 6
 
 
 def test_status_strings():
@@ -226,20 +226,20 @@ S = [0x1000000 * (i + 2) for i in range(10)]   # far apart: state buffers are la
 def test_linear_argument_errors():
     L = cattn.lib()
     # state build: d_h above 64 is unsupported for the carried state
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 65, S[2], S[3], 0, None) == 6
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, None, S[3], 0, None) == 1
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[2] + 8, S[3], 0, None) == 4
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[2], S[2] + 16, 0, None) == 5   # Z over M
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 0, 4, None, None, 1, None) == 0       # empty
-    assert L.cattn_born_state(0, None, None, None, None, 1, 1, 0, 4, None, S[3], 0, None) == 1       # zeroing needs Z
-    assert L.cattn_born_state(0, None, None, None, None, 0, 1, 0, 4, None, None, 0, None) == 0       # no heads
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 65, S[2], 0, None) == 6
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, None, 0, None) == 1
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[2] + 8, 0, None) == 4
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[0] + 16, 0, None) == 5   # state over k
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 0, 4, None, 1, None) == 0        # empty
+    assert L.cattn_born_state(0, None, None, None, None, 1, 1, 0, 4, None, 0, None) == 1        # zeroing needs S
+    assert L.cattn_born_state(0, None, None, None, None, 0, 1, 0, 4, None, 0, None) == 0        # no heads
     # merge: the written output and row_den must not overlap the state
-    assert L.cattn_born_merge(0, S[0], None, S[1], S[2], S[1], None, S[4], 1, 1, 8, 4, None) == 5
-    assert L.cattn_born_merge(0, S[0], None, S[1], S[2], S[3], None, None, 1, 1, 8, 4, None) == 1
+    assert L.cattn_born_merge(0, S[0], None, S[1], S[1], None, S[4], 1, 1, 8, 4, None) == 5
+    assert L.cattn_born_merge(0, S[0], None, S[1], S[3], None, None, 1, 1, 8, 4, None) == 1
     # step: eps checked first; o over q
-    assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[3], None, S[4], S[5], S[6], 1, 1, 4,
+    assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[3], None, S[4], S[6], 1, 1, 4,
                              -1.0, None) == 8
-    assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[0], None, S[4], S[5], S[6], 1, 1, 4,
+    assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[0], None, S[4], S[6], 1, 1, 4,
                              0.0, None) == 5
-    assert L.cattn_born_step(1, S[0], None, S[1], S[7], S[2], S[8], S[3], S[9], S[4], S[5], S[6], 1, 1, 4,
+    assert L.cattn_born_step(1, S[0], None, S[1], S[7], S[2], S[8], S[3], S[9], S[4], S[6], 1, 1, 4,
                              0.0, None) == 1   # bf16 needs both planes of q

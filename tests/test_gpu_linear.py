@@ -2,7 +2,9 @@
 BornAttention's linear and step modes) against the fp64 oracle, through the C
 ABI: the state build (overwrite and accumulate), a sequence split over two
 calls with the first part carried as a state, token-by-token decoding, and the
-zero-denominator case.  States are complex64 in both layouts (fp32 sums)."""
+zero-denominator case.  The device state is the packed real form of the
+oracle's (Z, M) (fp32 in both layouts); it is compared with the oracle's state
+after packing (``oracle.pack_state``)."""
 import numpy as np
 import pytest
 
@@ -32,19 +34,19 @@ def _slice(x, t0, t1):
 
 
 def _oracle_state(inp, B, H, t0, t1):
+    """The oracle's packed state [B, H, 2d + 1, d, d] of tokens t0 .. t1 - 1."""
     import oracle
-    Z = np.zeros((B, H) + (inp.k64.shape[-1],) * 2, np.complex128)
-    M = np.zeros((B, H) + (inp.k64.shape[-1],) * 3, np.complex128)
+    d = inp.k64.shape[-1]
+    S = np.zeros((B, H, 2 * d + 1, d, d))
     for b in range(B):
         for h in range(H):
-            Z[b, h], M[b, h] = oracle.born_state(inp.k64[b, h, t0:t1], inp.v64[b, h, t0:t1])
-    return Z, M
+            S[b, h] = oracle.pack_state(*oracle.born_state(inp.k64[b, h, t0:t1], inp.v64[b, h, t0:t1]))
+    return S
 
 
-def _state_err(Zg, Mg, Z, M):
-    ez = rowwise_rel_err(Zg.cpu().numpy(), Z, floor=GRAD_FLOOR)
-    em = rowwise_rel_err(Mg.cpu().numpy(), M, floor=GRAD_FLOOR)
-    return max(ez, em)
+def _state_err(Sg, S):
+    """Row-wise error of each packed matrix (rows of d features), scaled per tensor."""
+    return rowwise_rel_err(Sg.cpu().numpy().astype(np.float64), S, floor=GRAD_FLOOR)
 
 
 STATE_CASES = [
@@ -66,22 +68,21 @@ def test_state_build_and_accumulate(layout, B, H, T, d):
     inp = gen.make_inputs(w)
     _, k, v = to_device(inp)
     say(f"state {layout} B{B} H{H} T{T} d{d}")
-    Z, M = cattn.born_state_buffers(B, H, d)
-    Z.fill_(float("nan"))   # overwrite mode ignores the old contents
-    M.fill_(float("nan"))
-    cattn.born_state(k, v, Z, M)
+    S = cattn.born_state_buffer(B, H, d)
+    S.fill_(float("nan"))   # overwrite mode ignores the old contents
+    cattn.born_state(k, v, S)
     torch.cuda.synchronize()
-    Zr, Mr = _oracle_state(inp, B, H, 0, T)
-    err = _state_err(Z, M, Zr, Mr)
+    Sr = _oracle_state(inp, B, H, 0, T)
+    err = _state_err(S, Sr)
     say(f"  full: {err:.3e}")
     assert err <= STATE_TOL
     # the same state in two calls: overwrite (an empty first part zeroes the
     # state), then accumulate
     t1 = T // 3
-    cattn.born_state(_slice(k, 0, t1), _slice(v, 0, t1), Z, M)
-    cattn.born_state(_slice(k, t1, T), _slice(v, t1, T), Z, M, accumulate=True)
+    cattn.born_state(_slice(k, 0, t1), _slice(v, 0, t1), S)
+    cattn.born_state(_slice(k, t1, T), _slice(v, t1, T), S, accumulate=True)
     torch.cuda.synchronize()
-    err = _state_err(Z, M, Zr, Mr)
+    err = _state_err(S, Sr)
     say(f"  split at {t1}: {err:.3e}")
     assert err <= STATE_TOL
 
@@ -107,29 +108,28 @@ def test_prefill_with_carried_state(layout, B, H, T, T1, d, eps):
     inp = gen.make_inputs(w)
     q, k, v = to_device(inp)
     say(f"carry {layout} B{B} H{H} T{T} split {T1} d{d} eps {eps}")
-    Z, M = cattn.born_state_buffers(B, H, d)
-    cattn.born_state(_slice(k, 0, T1), _slice(v, 0, T1), Z, M)
+    S = cattn.born_state_buffer(B, H, d)
+    cattn.born_state(_slice(k, 0, T1), _slice(v, 0, T1), S)
     q2, k2, v2 = (_slice(x, T1, T) for x in (q, k, v))
     row_den = torch.empty(B * H * (T - T1), dtype=torch.float32, device="cuda")
     o2 = cattn.born_fwd(q2, k2, v2, causal=True, eps=eps, row_den=row_den)
-    cattn.born_merge(q2, Z, M, o2, row_den)
-    cattn.born_state(k2, v2, Z, M, accumulate=True)
+    cattn.born_merge(q2, S, o2, row_den)
+    cattn.born_state(k2, v2, S, accumulate=True)
     torch.cuda.synchronize()
     ref = oracle.born_attention(inp.q64, inp.k64, inp.v64, causal=True, eps=eps)[:, :, T1:]
     err = rowwise_rel_err(from_device(o2), ref)
     say(f"  output: {err:.3e}")
     assert err <= TOL[layout]
     # merged row denominators are the full sequence's l = sum_j w + eps
-    S = np.einsum("bhtm,bhjm->bhtj", inp.q64, inp.k64.conj())
-    w_ = np.abs(S) ** 2
+    scores = np.einsum("bhtm,bhjm->bhtj", inp.q64, inp.k64.conj())
+    w_ = np.abs(scores) ** 2
     l_ref = np.array([[[w_[b, h, t, : t + 1].sum() for t in range(T1, T)] for h in range(H)] for b in range(B)])
     l_ref = l_ref + eps
     l_got = row_den.cpu().numpy().reshape(B, H, T - T1)
     den_err = np.max(np.abs(l_got - l_ref) / l_ref)
     say(f"  row_den: {den_err:.3e}")
     assert den_err <= DEN_TOL[layout]
-    Zr, Mr = _oracle_state(inp, B, H, 0, T)
-    assert _state_err(Z, M, Zr, Mr) <= STATE_TOL
+    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= STATE_TOL
 
 
 STEP_CASES = [
@@ -153,12 +153,12 @@ def test_step_decoding(layout, B, H, T0, n, d, eps):
     inp = gen.make_inputs(w)
     q, k, v = to_device(inp)
     say(f"step {layout} B{B} H{H} prefix {T0} steps {n} d{d} eps {eps}")
-    Z, M = cattn.born_state_buffers(B, H, d)
+    S = cattn.born_state_buffer(B, H, d)
     if T0:
-        cattn.born_state(_slice(k, 0, T0), _slice(v, 0, T0), Z, M)
+        cattn.born_state(_slice(k, 0, T0), _slice(v, 0, T0), S)
     outs, dens = [], []
     for t in range(T0, T):
-        o, den = cattn.born_step(*(_slice(x, t, t + 1) for x in (q, k, v)), Z, M, eps=eps)
+        o, den = cattn.born_step(*(_slice(x, t, t + 1) for x in (q, k, v)), S, eps=eps)
         outs.append(from_device(o))
         dens.append(den.cpu().numpy().reshape(B, H))
     torch.cuda.synchronize()
@@ -175,8 +175,7 @@ def test_step_decoding(layout, B, H, T0, n, d, eps):
             q_last = inp.q64[b, h, T - 1]
             den_ref = (q_last.conj() @ Zb @ q_last).real + eps
             assert abs(dens[-1][b, h] - den_ref) <= 1e-4 * den_ref
-    Zr, Mr = _oracle_state(inp, B, H, 0, T)
-    assert _state_err(Z, M, Zr, Mr) <= STATE_TOL
+    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= STATE_TOL
 
 
 def test_step_zero_query_gives_zero():
@@ -188,8 +187,8 @@ def test_step_zero_query_gives_zero():
     inp = gen.make_inputs(w)
     _, k, v = to_device(inp)
     q = torch.zeros_like(k)
-    Z, M = cattn.born_state_buffers(B, H, d)
-    o, den = cattn.born_step(q, k, v, Z, M, eps=0.0)
+    S = cattn.born_state_buffer(B, H, d)
+    o, den = cattn.born_step(q, k, v, S, eps=0.0)
     torch.cuda.synchronize()
     assert torch.all(den == 0)
     assert torch.all(o == 0)
@@ -205,16 +204,16 @@ def test_step_at_full_head_count_sampled():
     inp = gen.make_inputs(w)
     q, k, v = to_device(inp)
     say(f"step full size B{B} H{H} prefix {T0} d{d} bf16")
-    Z, M = cattn.born_state_buffers(B, H, d)
-    cattn.born_state(_slice(k, 0, T0), _slice(v, 0, T0), Z, M)
-    o, den = cattn.born_step(*(_slice(x, T0, T0 + 1) for x in (q, k, v)), Z, M)
+    S = cattn.born_state_buffer(B, H, d)
+    cattn.born_state(_slice(k, 0, T0), _slice(v, 0, T0), S)
+    o, den = cattn.born_step(*(_slice(x, T0, T0 + 1) for x in (q, k, v)), S)
     torch.cuda.synchronize()
     got = from_device(o)
     for b, h in [(0, 0), (5, 11), (7, 15)]:
         Zb, Mb = oracle.born_state(inp.k64[b, h, :T0], inp.v64[b, h, :T0])
         ob, Zb, Mb = oracle.born_step(inp.q64[b, h, T0], inp.k64[b, h, T0], inp.v64[b, h, T0], Zb, Mb)
         err = rowwise_rel_err(got[b, h, 0][None], ob[None])
-        es = _state_err(Z[b, h], M[b, h], Zb, Mb)
+        es = _state_err(S[b, h], oracle.pack_state(Zb, Mb))
         say(f"  head ({b},{h}): out {err:.3e} state {es:.3e}")
         assert err <= TOL["bf16"]
         assert es <= STATE_TOL
