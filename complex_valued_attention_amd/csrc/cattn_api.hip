@@ -386,7 +386,9 @@ cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, co
     p.S = S;
     p.accumulate = accumulate != 0;
     p.stream = reinterpret_cast<hipStream_t>(stream);
-    return cattn::launch_born_state(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+    const hipError_t e = cattn::supports_born_linear_bf16_d64(p) ? cattn::launch_born_state_bf16_d64(p)
+                                                                  : cattn::launch_born_state(p);
+    return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
 cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, const float *S, void *o_re,
@@ -403,7 +405,9 @@ cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, co
     p.S = const_cast<float *>(S);   // read only in this call
     p.row_den = row_den;
     p.stream = reinterpret_cast<hipStream_t>(stream);
-    return cattn::launch_born_merge(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
+    const hipError_t e = cattn::supports_born_linear_bf16_d64(p) ? cattn::launch_born_merge_bf16_d64(p)
+                                                                  : cattn::launch_born_merge(p);
+    return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
 cattn_status cattn_born_step(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,

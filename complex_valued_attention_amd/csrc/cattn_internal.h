@@ -109,5 +109,9 @@ struct LinearProblem {
 hipError_t launch_born_state(const LinearProblem &p);
 hipError_t launch_born_merge(const LinearProblem &p);
 hipError_t launch_born_step(const LinearProblem &p);
+// matrix-core versions for bf16 planes at head width 64
+bool supports_born_linear_bf16_d64(const LinearProblem &p);
+hipError_t launch_born_merge_bf16_d64(const LinearProblem &p);
+hipError_t launch_born_state_bf16_d64(const LinearProblem &p);
 
 }  // namespace cattn

@@ -15,7 +15,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-STATE_TOL = 1e-4   # fp32 sums of rounded inputs, both layouts
+def state_tol(layout, d):
+    """fp32 sums of the rounded inputs: 1e-4.  bf16 planes at width 64 run on
+    the matrix cores, which round every lifted feature Re/Im(k_a conj k_b) to
+    bf16 (2^-9 relative per term) before the fp32 sum: the output bar."""
+    return TOL["bf16"] if (layout == "bf16" and d == 64) else 1e-4
 # Row denominators: the bf16 forward sums the bf16-rounded weights it applies
 # to V (each within 2^-9 relative, all positive, so the sum is too).
 DEN_TOL = {"c64": 1e-5, "bf16": 2.0 ** -8}
@@ -58,6 +62,10 @@ STATE_CASES = [
     ("bf16", 1, 2, 200, 64),
     ("bf16", 1, 1, 77, 20),
     ("c64", 1, 1, 1, 8),
+    # bf16 at width 64 runs on the matrix cores: several heads, ragged stages
+    ("bf16", 2, 3, 333, 64),
+    ("bf16", 1, 1, 65, 64),
+    ("bf16", 1, 2, 1, 64),
 ]
 
 
@@ -75,7 +83,7 @@ def test_state_build_and_accumulate(layout, B, H, T, d):
     Sr = _oracle_state(inp, B, H, 0, T)
     err = _state_err(S, Sr)
     say(f"  full: {err:.3e}")
-    assert err <= STATE_TOL
+    assert err <= state_tol(layout, d)
     # the same state in two calls: overwrite (an empty first part zeroes the
     # state), then accumulate
     t1 = T // 3
@@ -84,7 +92,7 @@ def test_state_build_and_accumulate(layout, B, H, T, d):
     torch.cuda.synchronize()
     err = _state_err(S, Sr)
     say(f"  split at {t1}: {err:.3e}")
-    assert err <= STATE_TOL
+    assert err <= state_tol(layout, d)
 
 
 CARRY_CASES = [
@@ -95,6 +103,10 @@ CARRY_CASES = [
     ("bf16", 1, 2, 300, 100, 64, 0.0),
     ("bf16", 1, 1, 90, 1, 32, 0.0),
     ("c64", 1, 1, 65, 64, 64, 0.0),     # one-token second call
+    # bf16 at width 64 runs on the matrix cores: several 256-token tiles with
+    # ragged tails; 24 workgroups (the XCD-grouped order) and 3 (plain order)
+    ("bf16", 2, 3, 1100, 300, 64, 0.0),
+    ("bf16", 1, 1, 700, 129, 64, 0.25),
 ]
 
 
@@ -129,7 +141,7 @@ def test_prefill_with_carried_state(layout, B, H, T, T1, d, eps):
     den_err = np.max(np.abs(l_got - l_ref) / l_ref)
     say(f"  row_den: {den_err:.3e}")
     assert den_err <= DEN_TOL[layout]
-    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= STATE_TOL
+    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= state_tol(layout, d)
 
 
 STEP_CASES = [
@@ -175,7 +187,7 @@ def test_step_decoding(layout, B, H, T0, n, d, eps):
             q_last = inp.q64[b, h, T - 1]
             den_ref = (q_last.conj() @ Zb @ q_last).real + eps
             assert abs(dens[-1][b, h] - den_ref) <= 1e-4 * den_ref
-    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= STATE_TOL
+    assert _state_err(S, _oracle_state(inp, B, H, 0, T)) <= state_tol(layout, d)
 
 
 def test_step_zero_query_gives_zero():
@@ -216,4 +228,4 @@ def test_step_at_full_head_count_sampled():
         es = _state_err(S[b, h], oracle.pack_state(Zb, Mb))
         say(f"  head ({b},{h}): out {err:.3e} state {es:.3e}")
         assert err <= TOL["bf16"]
-        assert es <= STATE_TOL
+        assert es <= state_tol("bf16", d)
