@@ -11,20 +11,22 @@
 // with fp32 accumulation.  MFMA rows are the state matrices (five tiles of 32:
 // Re V, Im V, and Z with zero rows), columns are tokens, the reduction runs
 // over features.  The state operand is staged per feature row a (64 features)
-// from fp32 to bf16 in LDS, the factor 2 of off-diagonal features folded in
-// (exact).  The token operand is formed in registers: lane (token t, half h)
+// from fp32 to bf16 in LDS; the factor 2 of off-diagonal features is put on
+// the token side (the doubled pairs of q_b, the diagonal feature halved).  The token operand is formed in registers: lane (token t, half h)
 // holds the (Re, Im) bf16 pairs of the 32 channels b = 16 m + 8 h + e it ever
 // needs, and per feature row a one pair q_a from LDS; each feature is one
 // v_dot2_f32_bf16:
 //     phi_ab = Re(q_a conj q_b) = dot((Re q_a, Im q_a), (Re q_b, Im q_b))   (a <= b)
 //            = Im(q_b conj q_a) = dot((-Im q_a, Re q_a), (Re q_b, Im q_b))  (a > b).
-// Workgroup: 4 waves, 64 tokens per wave (two column tiles), one head.
+// Workgroup: 8 waves (two per SIMD, so one wave's feature formation overlaps
+// the other's matrix products), 32 tokens per wave, one head.
 //
 // State build: S[n][f] (+)= sum_j W[j][n] phi_f(k_j) with W[j] = (Re V[j],
 // Im V[j], 1), a real product [129 x T] x [T x 4096] per head.  MFMA rows are
 // the state matrices (the Z tile takes a constant operand: ones in row 128),
 // columns are features, the reduction runs over tokens.  Per 64-token stage
-// the values are staged transposed (VT[n][token], bf16) and the keys as
+// the value planes are copied token-major into LDS (LDS-direct loads) and read
+// as the row operand through the transposing LDS read; the keys are staged as
 // transposed (Re, Im) pairs (KT[channel][token]), with the rotated pairs
 // (-Im, Re) of the workgroup's four feature rows for the features below the
 // diagonal.  Workgroup: 4 waves, wave w owns feature row a = 4 g + w (64
@@ -42,14 +44,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 64;
 constexpr int NM = 2 * D + 1;           // packed matrices per head
-constexpr int NW = 4;                   // waves per workgroup
+constexpr int NW = 4;                   // waves per workgroup (state build)
 constexpr int NT = 64 * NW;
-constexpr int TPW = 2;                  // 32-token column tiles per wave
-constexpr int TOK = 32 * TPW * NW;      // tokens per workgroup
+constexpr int MNW = 8;                  // waves per workgroup (readout): two per SIMD
+constexpr int MNT = 64 * MNW;
+constexpr int TPW = 1;                  // 32-token column tiles per wave (readout)
+constexpr int TOK = 32 * TPW * MNW;     // tokens per workgroup (readout)
 constexpr int NTILE = 5;                // 32-row tiles of state matrices (129 rows used)
 constexpr int SROW = 72;                // bf16 per staged state row (64 + 8: conflict-free 16-byte reads)
 constexpr int QROW = D + 1;             // dwords per staged token row
-constexpr int SLOADS = (NM * D / 4 + NT - 1) / NT;   // float4 state loads per thread per feature row
+constexpr int SLOADS = (NM * D / 4 + MNT - 1) / MNT;   // float4 state loads per thread per feature row
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -69,7 +73,7 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(NT) void born_merge_bf16_d64_kernel(LinearProblem p, int ntile_t) {
+__global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem p, int ntile_t) {
     __shared__ __align__(16) uint16_t Sb[2][NM][SROW];   // staged state rows (bf16), double buffered
     __shared__ uint32_t Qs[TOK][QROW];                   // (Re, Im) bf16 pairs of the tile's tokens
 
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(NT) void born_merge_bf16_d64_kernel(LinearProblem p
     const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im);
 
     // ---- stage the tile's queries as (Re, Im) pairs; rows past T are zero
-    for (int i = tid; i < TOK * (D / 8); i += NT) {
+    for (int i = tid; i < TOK * (D / 8); i += MNT) {
         const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
         u32x4 re = {0, 0, 0, 0}, im = {0, 0, 0, 0};
         if (t0 + r < T) {
@@ -106,49 +110,52 @@ __global__ __launch_bounds__(NT) void born_merge_bf16_d64_kernel(LinearProblem p
         }
     }
 
-    // ---- state staging: feature row a of all 129 matrices, fp32 -> bf16, x2 off the diagonal
+    // ---- state staging: feature row a of all 129 matrices, fp32 -> bf16
     float4 sreg[SLOADS];
+    // 2064 float4 per row: four full passes of the workgroup and a 16-thread tail
+    static_assert(NM * D / 4 == (SLOADS - 1) * MNT + 16, "state row split");
     auto load_rows = [&](int a) {
 #pragma unroll
         for (int i = 0; i < SLOADS; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < NM * D / 4) {
-                const int n = idx / (D / 4), q4 = idx % (D / 4);
+            const int idx = tid + i * MNT;
+            const int n = idx / (D / 4), q4 = idx % (D / 4);
+            if (i < SLOADS - 1 || tid < 16)
                 sreg[i] = *reinterpret_cast<const float4 *>(S + ((int64_t)n * D + a) * D + 4 * q4);
-            }
         }
     };
-    auto store_rows = [&](int a, int buf) {
+    auto store_rows = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < SLOADS; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < NM * D / 4) {
-                const int n = idx / (D / 4), q4 = idx % (D / 4);
-                const int b = 4 * q4;
-                const float4 v = sreg[i];
-                const float w0 = b + 0 == a ? 1.f : 2.f, w1 = b + 1 == a ? 1.f : 2.f;
-                const float w2 = b + 2 == a ? 1.f : 2.f, w3 = b + 3 == a ? 1.f : 2.f;
-                uint2 pk;
-                pk.x = pack_bf16x2(v.x * w0, v.y * w1);
-                pk.y = pack_bf16x2(v.z * w2, v.w * w3);
-                *reinterpret_cast<uint2 *>(&Sb[buf][n][b]) = pk;
-            }
+            const int idx = tid + i * MNT;
+            const int n = idx / (D / 4), q4 = idx % (D / 4);
+            const float4 v = sreg[i];
+            uint2 pk;
+            pk.x = pack_bf16x2(v.x, v.y);
+            pk.y = pack_bf16x2(v.z, v.w);
+            if (i < SLOADS - 1 || tid < 16) *reinterpret_cast<uint2 *>(&Sb[buf][n][4 * q4]) = pk;
         }
     };
     load_rows(0);
-    store_rows(0, 0);
+    store_rows(0);
     __syncthreads();
 
-    // ---- this lane's token pairs for the channels b = 16 m + 8 h + e
+    // ---- this lane's token pairs for the channels b = 16 m + 8 h + e, doubled by
+    // one on the exponent (psi = 2 phi off the diagonal; exact for normal values;
+    // zero, subnormal, infinite and NaN halves are left as they are)
     int tl[TPW];
     uint32_t qb[TPW][32];
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
-        tl[s] = 64 * wave + 32 * s + l32;
+        tl[s] = 32 * TPW * wave + 32 * s + l32;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qb[s][8 * m + e] = Qs[tl[s]][16 * m + 8 * h + e];
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t x = Qs[tl[s]][16 * m + 8 * h + e];
+                const uint32_t lo = x & 0x7f80u, hi = x & 0x7f800000u;   // exponent fields
+                qb[s][8 * m + e] = x + (lo != 0u && lo != 0x7f80u ? 0x0080u : 0u)
+                                     + (hi != 0u && hi != 0x7f800000u ? 0x00800000u : 0u);
+            }
     }
 
     f32x16 acc[TPW][NTILE];
@@ -178,22 +185,37 @@ __global__ __launch_bounds__(NT) void born_merge_bf16_d64_kernel(LinearProblem p
                 sa[ti] = *reinterpret_cast<const bf16x8 *>(&Sb[buf][32 * ti + l32][16 * m + 8 * h]);
             sa[NTILE - 1] = l32 == 0 ? *reinterpret_cast<const bf16x8 *>(&Sb[buf][2 * D][16 * m + 8 * h])
                                      : as_bf16x8(zero4);
-            const int b0 = 16 * m + 8 * h;   // this lane's first channel of the step
+            // steps wholly above (a < 16 m) or below (a > 16 m + 15) the diagonal take one
+            // operand for all their features; in the step holding the diagonal (at position
+            // rd = a - 16 m) the lane's feature 8 h + e lies above it when 8 h + e > rd, and
+            // the diagonal feature itself takes half the upper value (q_b is doubled)
+            const int rd = a - 16 * m;
+            const bool mixed = rd >= 0 && rd <= 15;
 #pragma unroll
             for (int s = 0; s < TPW; ++s) {
+                float f[8];
+                if (!mixed) {
+                    const uint32_t xs = rd < 0 ? qa[s] : qr[s];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] = dot2(xs, qb[s][8 * m + e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float up = dot2(qa[s], qb[s][8 * m + e]);
+                        const float lo = dot2(qr[s], qb[s][8 * m + e]);
+                        f[e] = 8 * h + e > rd ? up : lo;
+                        if (e == (rd & 7)) f[e] = h == (rd >> 3) ? 0.5f * up : f[e];
+                    }
+                }
                 uint32_t pk[4];
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t x0 = a <= b0 + e ? qa[s] : qr[s];
-                    const uint32_t x1 = a <= b0 + e + 1 ? qa[s] : qr[s];
-                    pk[e >> 1] = pack_bf16x2(dot2(x0, qb[s][8 * m + e]), dot2(x1, qb[s][8 * m + e + 1]));
-                }
+                for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(f[e], f[e + 1]);
                 const bf16x8 fq = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
                 for (int ti = 0; ti < NTILE; ++ti) acc[s][ti] = mfma(sa[ti], fq, acc[s][ti]);
             }
         }
-        if (a + 1 < D) store_rows(a + 1, buf ^ 1);
+        if (a + 1 < D) store_rows(buf ^ 1);
         __syncthreads();
     }
 
@@ -237,14 +259,37 @@ __global__ __launch_bounds__(NT) void born_merge_bf16_d64_kernel(LinearProblem p
 
 constexpr int ST_TOK = 64;               // tokens per stage
 constexpr int KROW = ST_TOK + 4;         // dwords per staged key row (16-byte aligned, offset banks)
-constexpr int VROW = ST_TOK + 8;         // bf16 per staged value row
 constexpr int ROWS_PER_WG = NW;          // feature rows per workgroup
+constexpr int VROWB = 2 * D;             // bytes per token row of a value plane
+constexpr int VREGION = ST_TOK * VROWB;  // 8 KiB per plane and stage
+constexpr int VRPT = VREGION / 16 / NT;  // 16-byte LDS-direct loads per thread per plane
+static_assert(VRPT * 16 * NT == VREGION, "value staging split");
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+typedef __bf16 bf16x4v __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct StateStage {
     uint32_t KT[D][KROW];                // (Re k, Im k) pairs, [channel][token]
     uint32_t KR[ROWS_PER_WG][KROW];      // (-Im k, Re k) of this workgroup's feature rows
-    uint16_t VT[2 * D][VROW];            // Re V channels then Im V channels, [n][token]
+    char V[2][VREGION];                  // value planes, token-major, 16-byte chunks swizzled by token
 };
+
+__device__ inline int swz_v(int row) { return (row & 3) << 1; }
+
+__device__ inline u32x2 ds_read_tr(const char *p) {
+    const bf16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// All of this wave's LDS-direct loads have landed; then workgroup barrier.
+__device__ inline void loads_done_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
 
 __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p) {
     __shared__ __align__(16) StateStage st[2];
@@ -264,35 +309,26 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
     const int a0 = (lin % GROUPS) * ROWS_PER_WG;
     const int a = a0 + wave;                  // this wave's feature row
     const int64_t base = bh * (int64_t)T * D;
-    const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re);
-    const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im);
-    const uint16_t *vre = reinterpret_cast<const uint16_t *>(p.v_re);
-    const uint16_t *vim = reinterpret_cast<const uint16_t *>(p.v_im);
+    const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re) + base;
+    const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im) + base;
+    const uint16_t *vpl[2] = {reinterpret_cast<const uint16_t *>(p.v_re) + base,
+                              reinterpret_cast<const uint16_t *>(p.v_im) + base};
 
-    // staging: thread -> (token, 8-channel group); two K groups and four V groups per stage
-    u32x4 kr_reg[2], ki_reg[2], v_reg[4];
-    auto load_stage = [&](int t0) {
+    // keys through registers (interleaved to pairs, transposed); thread -> (token, 8 channels), twice
+    u32x4 kr_reg[2], ki_reg[2];
+    auto load_keys = [&](int t0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int g = tid + i * NT;                 // 512 (token, channel group) of K
+            const int g = tid + i * NT;
             const int r = g / (D / 8), c8 = (g % (D / 8)) * 8;
             kr_reg[i] = ki_reg[i] = u32x4{0, 0, 0, 0};
             if (t0 + r < T) {
-                kr_reg[i] = *reinterpret_cast<const u32x4 *>(kre + base + (int64_t)(t0 + r) * D + c8);
-                ki_reg[i] = *reinterpret_cast<const u32x4 *>(kim + base + (int64_t)(t0 + r) * D + c8);
+                kr_reg[i] = *reinterpret_cast<const u32x4 *>(kre + (int64_t)(t0 + r) * D + c8);
+                ki_reg[i] = *reinterpret_cast<const u32x4 *>(kim + (int64_t)(t0 + r) * D + c8);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = tid + i * NT;                 // 1024 (plane, token, channel group) of V
-            const int pl = g / (ST_TOK * D / 8), rem = g % (ST_TOK * D / 8);
-            const int r = rem / (D / 8), c8 = (rem % (D / 8)) * 8;
-            v_reg[i] = u32x4{0, 0, 0, 0};
-            if (t0 + r < T)
-                v_reg[i] = *reinterpret_cast<const u32x4 *>((pl ? vim : vre) + base + (int64_t)(t0 + r) * D + c8);
-        }
     };
-    auto store_stage = [&](StateStage &S_) {
+    auto store_keys = [&](StateStage &S_) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int g = tid + i * NT;
@@ -308,18 +344,32 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 if (c0 + 1 >= 0 && c0 + 1 < ROWS_PER_WG) S_.KR[c0 + 1][r] = rot_pair(p1);
             }
         }
+    };
+    // values straight to LDS: chunk NT e + tid is token tid / 8 + 32 e, physical slot tid % 8,
+    // holding logical chunk slot ^ swz(token); tokens past T repeat the last one (their keys are zero)
+    const int srow = tid >> 3, sslot = tid & 7;
+    const int lcv = sslot ^ swz_v(srow);
+    auto issue_values = [&](int t0, StateStage &S_) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = tid + i * NT;
-            const int pl = g / (ST_TOK * D / 8), rem = g % (ST_TOK * D / 8);
-            const int r = rem / (D / 8), c8 = (rem % (D / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                S_.VT[pl * D + c8 + 2 * e][r] = (uint16_t)(v_reg[i][e] & 0xffffu);
-                S_.VT[pl * D + c8 + 2 * e + 1][r] = (uint16_t)(v_reg[i][e] >> 16);
-            }
+        for (int i = 0; i < 2 * VRPT; ++i) {
+            const int pl = i / VRPT, e = i % VRPT;
+            const int row = min(t0 + srow + (NT / 8) * e, T - 1);
+            __builtin_amdgcn_global_load_lds((GLB_AS void *)(vpl[pl] + (int64_t)row * D + 8 * lcv),
+                                             (LDS_AS void *)(S_.V[pl] + e * (NT * 16) + wave * 1024), 16, 0, 0);
         }
     };
+    // V^T operand through the transposing read (k-step of 16 tokens): lane 16 G + 4 r + c4
+    // points at token 4 h + r, channels 16 (G & 1) + 4 c4 of the 32-channel tile; its
+    // element e then belongs to token 8 (e / 4) + 4 h + e % 4 of the step.
+    int voff[2];
+    {
+        const int G = lane >> 4, r = (lane >> 2) & 3, c4 = lane & 3;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int lc = 4 * cc + 2 * (G & 1) + (c4 >> 1);
+            voff[cc] = (4 * h + r) * VROWB + ((lc ^ (r << 1)) << 4) + ((c4 & 1) << 3);
+        }
+    }
 
     f32x16 acc[2][NTILE];
 #pragma unroll
@@ -332,38 +382,48 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
     // the Z tile's row operand: ones in row 128 (lane 0 of each half), zero elsewhere
     const uint32_t one2 = 0x3f803f80u;
     const bf16x8 zrow = l32 == 0 ? as_bf16x8(u32x4{one2, one2, one2, one2}) : as_bf16x8(u32x4{0, 0, 0, 0});
-    // features of column tile ft: (a, b = 32 ft + l32); on or above the diagonal reads KT[a], below KR
-    bool upper[2];
+    // column tile ft holds features (a, b = 32 ft + l32): on or above the diagonal the
+    // first operand is the pair of k_a (KT row a), below it the rotated pair (KR row)
+    int xoff[2], boff[2];
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) upper[ft] = a <= 32 * ft + l32;
+    for (int ft = 0; ft < 2; ++ft) {
+        const int b = 32 * ft + l32;
+        xoff[ft] = a <= b ? (int)offsetof(StateStage, KT) + a * KROW * 4 : (int)offsetof(StateStage, KR) + wave * KROW * 4;
+        boff[ft] = (int)offsetof(StateStage, KT) + b * KROW * 4;
+    }
 
     const int nst = (T + ST_TOK - 1) / ST_TOK;
     if (nst > 0) {
-        load_stage(0);
-        store_stage(st[0]);
+        issue_values(0, st[0]);
+        load_keys(0);
+        store_keys(st[0]);
     }
-    __syncthreads();
+    loads_done_barrier();
     for (int s = 0; s < nst; ++s) {
         StateStage &cur = st[s & 1];
-        if (s + 1 < nst) load_stage((s + 1) * ST_TOK);
+        const char *cb = reinterpret_cast<const char *>(&cur);
+        if (s + 1 < nst) {
+            issue_values((s + 1) * ST_TOK, st[(s + 1) & 1]);
+            load_keys((s + 1) * ST_TOK);
+        }
 #pragma unroll
         for (int ks = 0; ks < ST_TOK / 16; ++ks) {
-            const int tk = 16 * ks + 8 * h;   // this lane's first token of the step
             bf16x8 wa[NTILE];
 #pragma unroll
-            for (int ti = 0; ti < NTILE - 1; ++ti)
-                wa[ti] = *reinterpret_cast<const bf16x8 *>(&cur.VT[32 * ti + l32][tk]);
+            for (int c = 0; c < 4; ++c) {
+                const char *vb = cur.V[c >> 1] + 16 * ks * VROWB + voff[c & 1];
+                const u32x2 lo = ds_read_tr(vb);
+                const u32x2 hi = ds_read_tr(vb + 8 * VROWB);
+                wa[c] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
             wa[NTILE - 1] = zrow;
-            const u32x4 ka0 = *reinterpret_cast<const u32x4 *>(&cur.KT[a][tk]);
-            const u32x4 ka1 = *reinterpret_cast<const u32x4 *>(&cur.KT[a][tk + 4]);
-            const u32x4 kq0 = *reinterpret_cast<const u32x4 *>(&cur.KR[wave][tk]);
-            const u32x4 kq1 = *reinterpret_cast<const u32x4 *>(&cur.KR[wave][tk + 4]);
+            const int tb = (16 * ks + 4 * h) * 4;   // byte offset of this lane's first token in a key row
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {
-                const int b = 32 * ft + l32;
-                const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(&cur.KT[b][tk]);
-                const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(&cur.KT[b][tk + 4]);
-                const u32x4 x0 = upper[ft] ? ka0 : kq0, x1 = upper[ft] ? ka1 : kq1;
+                const u32x4 x0 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb);
+                const u32x4 x1 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb + 32);
+                const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb);
+                const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb + 32);
                 uint32_t pk[4];
                 pk[0] = pack_bf16x2(dot2(x0[0], kb0[0]), dot2(x0[1], kb0[1]));
                 pk[1] = pack_bf16x2(dot2(x0[2], kb0[2]), dot2(x0[3], kb0[3]));
@@ -374,8 +434,8 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 for (int ti = 0; ti < NTILE; ++ti) acc[ft][ti] = mfma(wa[ti], fk, acc[ft][ti]);
             }
         }
-        if (s + 1 < nst) store_stage(st[(s + 1) & 1]);
-        __syncthreads();
+        if (s + 1 < nst) store_keys(st[(s + 1) & 1]);
+        loads_done_barrier();
     }
 
     // write S[n][a * 64 + b]: lane (column b = 32 ft + l32, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4
@@ -403,7 +463,7 @@ hipError_t launch_born_merge_bf16_d64(const LinearProblem &p) {
     const int ntile_t = (p.T + TOK - 1) / TOK;
     const int64_t blocks = (int64_t)p.BH * ntile_t;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_merge_bf16_d64_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, ntile_t);
+    hipLaunchKernelGGL(born_merge_bf16_d64_kernel, dim3((unsigned)blocks), dim3(MNT), 0, p.stream, p, ntile_t);
     return hipGetLastError();
 }
 
