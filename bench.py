@@ -47,6 +47,18 @@ MEASURED_TRAFFIC = {
         "sha256": "1ea06ab789c9db176c51489e8839f1ee6cad3e1863445d4fac4248dcb78e7f02",
         "bytes": 882.4e6,   # read 748.1 MB + write 134.2 MB
     },
+    # one-token step with the carried state: born_step_kernel
+    "step:born_causal_bf16_b8h16t4096d64_rotary": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_linear.hip",
+        "sha256": "ea5dde56a44f154b865254f447d35d310cf03233ba5974324f701c40b4ece0c2",
+        "bytes": 542.3e6,   # read 271.5 MB + write 270.8 MB
+    },
+    # chunked prefill, chunk 4096: the state build born_state_bf16_d64_kernel
+    "linear:born_causal_bf16_b1h16t32768d64_rotary:4096": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
+        "sha256": "05a9bef9bc7a44946ab989f67027b8b00deccdcbae36c23bf6f21a6dd4570a1a",
+        "bytes": 96.6e6,    # read 62.8 MB + write 33.8 MB
+    },
 }
 
 
@@ -286,7 +298,8 @@ def main_step(args, w):
            "config": {"workload": w.name, "pass": "step", "B": B, "H": H, "prefix_T": T, "d_h": d,
                       "layout": w.layout, "state_MiB": state_bytes(d, heads) / 2**20},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "born_step_kernel",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(f"step:{w.name}"),
+                        "kernel": "born_step_kernel",
                         "bytes_per_step": nbytes, "kernel_ms_mean": float(np.mean(per)),
                         "kernel_ms_median": float(np.median(per))},
            "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads), "kind": "oracle",
@@ -394,6 +407,11 @@ def main_linear(args, w):
     dom_ms = part[dom] / n_launch
     dom_flops = state_flops(C, d, heads)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    # bf16 planes at width 64 run the state kernels on the matrix cores; otherwise fp32 vector ALU
+    mfma = w.layout == "bf16" and d == 64
+    bound, peak = ("mfma", PEAK_TFLOPS["bf16"]) if mfma else ("alu", PEAK_TFLOPS["c64"])
+    kname = {"merge": "born_merge_bf16_d64_kernel" if mfma else "born_merge_kernel",
+             "state": "born_state_bf16_d64_kernel" if mfma else "born_state_kernel"}[dom]
     rec = {"metric": f"Born chunked carried-state prefill head-tokens/s ({w.name}, chunk {C})",
            "value": tok_s, "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -403,9 +421,11 @@ def main_linear(args, w):
                       "chunk": C, "chunks": nc},
            "quadratic_ms": ms_quad, "speedup_vs_quadratic": ms_quad / ms,
            "parts_ms": part,
-           "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_TFLOPS["c64"], "unit": "TFLOP/s",
-                        "frac": achieved / PEAK_TFLOPS["c64"], "traffic": None,
-                        "kernel": f"born_{dom}_kernel", "kernel_ms_mean": dom_ms},
+           "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                        "frac": achieved / peak,
+                        "traffic": measured_traffic(f"linear:{w.name}:{C}") if dom == "state" else None,
+                        "kernel": kname, "kernel_ms_mean": dom_ms,
+                        "flops_per_launch": dom_flops},
            "gpu_vs_quadratic_rowwise_rel_err": err_quad,
            "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads),
                             "kind": "oracle",
@@ -517,11 +537,15 @@ def main():
         return
     if args.which == "step":
         main_step(args, w)
+        if args.copy_probe:
+            copy_probe(args.copy_probe)
         return
     if args.which == "linear":
         if args.workload is None:
             w = gen.WORKLOADS["born_causal_bf16_b1h16t32768d64_rotary"]
         main_linear(args, w)
+        if args.copy_probe:
+            copy_probe(args.copy_probe)
         return
     if args.gate != "sigmoid" and w.op != "pct":
         print("--gate applies to PCT workloads only", file=sys.stderr)
