@@ -203,6 +203,29 @@ def main_rotary(args, w):
     nbytes = 2 * w.B * w.H * w.T * w.d_h * (8 if w.layout == "c64" else 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] rotary {w.name}: {ms:.4f} ms/step, {gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        from complex_valued_attention_amd.check import TOL, from_device, rowwise_rel_err
+        got = from_device(out)
+        done, t_used, err = 0, 0.0, 0.0
+        for b in range(w.B):
+            for h in range(w.H):
+                t0 = time.perf_counter()
+                ref = oracle.rotary(inp.q64[b, h][None, None])[0, 0]
+                t_used += time.perf_counter() - t0
+                err = max(err, rowwise_rel_err(got[b, h], ref))
+                done += 1
+                if t_used >= 12.0:
+                    break
+            if t_used >= 12.0:
+                break
+        per_head = 2 * w.T * w.d_h * (8 if w.layout == "c64" else 4)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": done * per_head / t_used / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"{done} of {w.B * w.H} heads of Q (full T={w.T}), fp64 numpy, {t_used:.1f} s",
+               "gpu_rowwise_rel_err": err, "gpu_parity_pass": bool(err <= TOL[w.layout])}
     rec = {"metric": f"rotary GB/s ({w.name})", "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if w.layout == "c64" else "bf16", "data": "synthetic",
@@ -210,6 +233,8 @@ def main_rotary(args, w):
                       "layout": w.layout},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "rotary_kernel"}}
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 
@@ -475,7 +500,7 @@ def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid"):
     return inp, from_device(out), total_ms / steps, per, wall_ms
 
 
-def cpu_baseline(w, inp, got, budget_s: float = 12.0):
+def cpu_baseline(w, inp, got, budget_s: float = 12.0, gate: str = "sigmoid"):
     """The fp64 oracle on whole heads of the same inputs, as many heads as fit the budget.
 
     The heads it computes are also compared with the GPU output of the timed
@@ -486,7 +511,14 @@ def cpu_baseline(w, inp, got, budget_s: float = 12.0):
     from complex_valued_attention_amd.check import TOL, rowwise_rel_err
     from complex_valued_attention_amd.inputs import attention_flops
 
-    fn = oracle.born_attention if w.op == "born" else oracle.pct_attention
+    if w.op == "born":
+        fn = oracle.born_attention
+    elif gate == "softmax":
+        fn = oracle.pct_softmax_attention
+    elif gate == "screen":   # the bench's screening parameters: r = 1, t = 0.5
+        fn = lambda q, k, v, causal: oracle.pct_screen_attention(q, k, v, causal=causal, r=1.0, t=0.5)
+    else:
+        fn = oracle.pct_attention
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done, t_used, err = 0, 0.0, 0.0
     for b, h in heads:
@@ -582,8 +614,8 @@ def main():
                      "kernel": kernel_name(w),
                      "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per))},
     }
-    if not args.no_cpu_baseline and args.gate == "sigmoid":
-        rec["cpu_baseline"] = cpu_baseline(w, inp, got)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, got, gate=args.gate)
         log(f"[bench] cpu baseline {rec['cpu_baseline']}")
     print(json.dumps(rec), flush=True)
     if args.copy_probe:
