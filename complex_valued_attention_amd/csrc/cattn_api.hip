@@ -302,6 +302,7 @@ cattn_status cattn_rotary(int layout, const void *x_re, const void *x_im, void *
     p.layout = c64 ? cattn::LAYOUT_C64 : cattn::LAYOUT_BF16;
     p.x_re = x_re; p.x_im = x_im; p.y_re = y_re; p.y_im = y_im;
     p.rows = BH * T;
+    p.BH = BH;
     p.T = (int)T;
     p.d = (int)d_h;
     p.pos0 = pos0;

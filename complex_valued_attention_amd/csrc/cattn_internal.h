@@ -80,7 +80,8 @@ struct RotaryProblem {
     int layout;
     const void *x_re, *x_im;
     void *y_re, *y_im;
-    int64_t rows;
+    int64_t rows;      // BH * T
+    int64_t BH;
     int T;
     int d;
     int64_t pos0;
