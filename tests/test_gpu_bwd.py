@@ -163,6 +163,14 @@ CASES = [
     ("pct", "bf16", True, 1, 2, 200, 64, False),
     ("pct", "c64", False, 1, 1, 300, 128, False),
     ("pct", "c64", True, 1, 1, 1, 64, False),
+    # complex64 at widths 16/32/64 runs on the fp32 matrix cores: several
+    # 128-row blocks, ragged tails, 8 heads (the XCD-grouped block order)
+    ("born", "c64", True, 1, 2, 300, 64, True),
+    ("born", "c64", False, 1, 3, 260, 32, False),
+    ("born", "c64", True, 2, 4, 200, 16, False),
+    ("pct", "c64", True, 2, 1, 520, 32, False),
+    ("pct", "c64", False, 1, 8, 190, 64, False),
+    ("pct", "c64", True, 1, 8, 300, 16, False),
 ]
 
 
