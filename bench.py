@@ -143,10 +143,13 @@ def main_bwd(args, w):
     flops = bwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] bwd {w.name}: {ms:.4f} ms/step (median {np.median(per):.4f} ms), {tflops:.2f} TFLOP/s")
-    # which kernels the library dispatches: bf16 matrix cores for Born at d_h = 64, else fp32 vector code
+    # which kernels the library dispatches: bf16 matrix cores for Born at d_h = 64, fp32 matrix
+    # cores for complex64 at d_h 16/32/64, else fp32 vector code
     mfma = w.op == "born" and w.layout == "bf16" and w.d_h == 64
+    mfma32 = w.layout == "c64" and w.d_h in (16, 32, 64)
     peak = PEAK_TFLOPS["bf16"] if mfma else PEAK_TFLOPS["c64"]
     kern = ("born_bf16_d64_bwd_dkdv_kernel + born_bf16_d64_bwd_dq_kernel" if mfma
+            else "bwd_dkdv_f32_kernel + bwd_dq_f32_kernel" if mfma32
             else "bwd_dkdv_kernel + bwd_dq_kernel")
     rec = {
         "metric": f"{w.op} bwd real TFLOP/s ({w.name})",
@@ -155,7 +158,7 @@ def main_bwd(args, w):
         "dtype": "bf16" if mfma else "f32", "data": "synthetic",
         "config": {"workload": w.name, "pass": "bwd", "op": w.op, "causal": w.causal, "B": w.B, "H": w.H,
                    "T": w.T, "d_h": w.d_h, "layout": w.layout},
-        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma" if (mfma or mfma32) else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": tflops / peak, "traffic": None, "kernel": kern},
     }
     if not args.no_cpu_baseline:
