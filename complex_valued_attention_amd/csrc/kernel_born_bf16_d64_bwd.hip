@@ -80,7 +80,13 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset)
 // straight into LDS at lds + 16 * lane.  Completion is tracked by hand
-// (vmcnt(0) before the barrier that publishes a stage).
+// (vmcnt(0) before the barrier that publishes a stage).  M0 is a reserved
+// register: the compiler does not honour it as a clobber, so this form is
+// sound only while the compiler itself keeps no value in M0 across these
+// statements.  In these two kernels it emits no M0 use at all (checked in
+// their assembly: the only writes to M0 are the ones below); the SGPR-base
+// form saves the 64-bit per-lane addresses of the builtin's form, which
+// these kernels, at 512 registers, do not have room for.
 __device__ inline void dma16(uint32_t lds, const void *base, uint32_t voff) {
     __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                          :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
