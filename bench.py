@@ -566,9 +566,13 @@ def main():
 
     if args.which == "bwd":
         main_bwd(args, w)
+        if args.copy_probe:
+            copy_probe(args.copy_probe)
         return
     if args.which == "rotary":
         main_rotary(args, w)
+        if args.copy_probe:
+            copy_probe(args.copy_probe)
         return
     if args.which == "step":
         main_step(args, w)
