@@ -4,7 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace cattn {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device (the limit is a per-device property of the function; `done`
+// holds one bit per device id, and a repeated set is harmless).
+inline hipError_t set_dynamic_lds(const void *kern, int bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // OP_PCT is the sigmoid cell; the two siblings share its scaled cosine score
 // ("Complex-valued Phase-Coherent Transformers", Appendix D.2): the

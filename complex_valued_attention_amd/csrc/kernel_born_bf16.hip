@@ -326,13 +326,9 @@ template <int D, int NQT, int NW, int BN>
 hipError_t launch_cfg(const Problem &p) {
     using C = BornCfg<D, NQT, NW, BN>;
     auto kern = born_bf16_mfma_kernel<D, NQT, NW, BN>;
-    static bool attr_done = false;   // set once per process; idempotent
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
     const int nrb = (p.T + C::BM - 1) / C::BM;
     const int64_t blocks = (int64_t)p.BH * nrb;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -504,27 +504,18 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
         }
 }
 
-template <typename K>
-hipError_t set_lds(K kern, int bytes, bool &done) {
-    if (done) return hipSuccess;
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 template <int D, int OP>
 hipError_t launch_cfg(const BwdProblem &p) {
     using C = BCfg<D>;
-    static bool dq_done = false, kv_done = false;
+    static std::atomic<uint64_t> dq_set{0}, kv_set{0};
     const int nblk = (p.T + BM - 1) / BM;
     const int64_t blocks = (int64_t)p.BH * nblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     auto kkv = bwd_dkdv_f32_kernel<D, OP>;
     auto kdq = bwd_dq_f32_kernel<D, OP>;
-    hipError_t e = set_lds(kkv, C::LDS_BYTES_KV, kv_done);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), C::LDS_BYTES_KV, kv_set);
     if (e != hipSuccess) return e;
-    e = set_lds(kdq, C::LDS_BYTES, dq_done);
+    e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), C::LDS_BYTES, dq_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES_KV, p.stream, p, nblk);
     e = hipGetLastError();

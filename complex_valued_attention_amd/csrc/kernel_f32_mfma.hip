@@ -255,13 +255,9 @@ template <int D, int OP>
 hipError_t launch_cfg(const Problem &p) {
     using C = F32Cfg<D>;
     auto kern = attn_f32_mfma_kernel<D, OP>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
     const int nrb = (p.T + BM - 1) / BM;
     const int64_t blocks = (int64_t)p.BH * nrb;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
