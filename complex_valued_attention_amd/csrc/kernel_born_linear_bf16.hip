@@ -110,11 +110,13 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
         }
     }
 
-    // ---- state staging: feature row a of all 129 matrices, fp32 -> bf16
-    float4 sreg[SLOADS];
+    // ---- state staging: feature row a of all 129 matrices, fp32 -> bf16.  Rows
+    // are loaded two iterations ahead into alternating register sets (row r in
+    // set r % 2), so a row's load latency spans two feature rows of products.
+    float4 sreg0[SLOADS], sreg1[SLOADS];
     // 2064 float4 per row: four full passes of the workgroup and a 16-thread tail
     static_assert(NM * D / 4 == (SLOADS - 1) * MNT + 16, "state row split");
-    auto load_rows = [&](int a) {
+    auto load_rows = [&](int a, float4 (&sreg)[SLOADS]) {
 #pragma unroll
         for (int i = 0; i < SLOADS; ++i) {
             const int idx = tid + i * MNT;
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
                 sreg[i] = *reinterpret_cast<const float4 *>(S + ((int64_t)n * D + a) * D + 4 * q4);
         }
     };
-    auto store_rows = [&](int buf) {
+    auto store_rows = [&](int buf, const float4 (&sreg)[SLOADS]) {
 #pragma unroll
         for (int i = 0; i < SLOADS; ++i) {
             const int idx = tid + i * MNT;
@@ -135,8 +137,9 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
             if (i < SLOADS - 1 || tid < 16) *reinterpret_cast<uint2 *>(&Sb[buf][n][4 * q4]) = pk;
         }
     };
-    load_rows(0);
-    store_rows(0);
+    load_rows(0, sreg0);
+    store_rows(0, sreg0);
+    load_rows(1, sreg1);
     __syncthreads();
 
     // ---- this lane's token pairs for the channels b = 16 m + 8 h + e, doubled by
@@ -167,9 +170,11 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
             for (int r = 0; r < 16; ++r) acc[s][ti][r] = 0.f;
 
     const u32x4 zero4 = {0, 0, 0, 0};
-    for (int a = 0; a < D; ++a) {
+    // feature row a: products from Sb[a % 2]; rows a + 2 load into the set that held
+    // row a, rows a + 1 (loaded an iteration ago) go to the other buffer
+    auto feature_row = [&](int a, float4 (&ld)[SLOADS], const float4 (&sv)[SLOADS]) {
         const int buf = a & 1;
-        if (a + 1 < D) load_rows(a + 1);
+        if (a + 2 < D) load_rows(a + 2, ld);
         uint32_t qa[TPW], qr[TPW];
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
@@ -215,8 +220,12 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
                 for (int ti = 0; ti < NTILE; ++ti) acc[s][ti] = mfma(sa[ti], fq, acc[s][ti]);
             }
         }
-        if (a + 1 < D) store_rows(buf ^ 1);
+        if (a + 1 < D) store_rows(buf ^ 1, sv);
         __syncthreads();
+    };
+    for (int a = 0; a < D; a += 2) {
+        feature_row(a, sreg0, sreg1);
+        feature_row(a + 1, sreg1, sreg0);
     }
 
     // ---- epilogue: lane (token, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4
