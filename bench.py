@@ -56,7 +56,7 @@ MEASURED_TRAFFIC = {
     # chunked prefill, chunk 4096: the state build born_state_bf16_d64_kernel
     "linear:born_causal_bf16_b1h16t32768d64_rotary:4096": {
         "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
-        "sha256": "05a9bef9bc7a44946ab989f67027b8b00deccdcbae36c23bf6f21a6dd4570a1a",
+        "sha256": "271ea31f2ac5745f9f36fc050d6e22f98ca416bb5d0ed499f969d5fc3ad43ee1",
         "bytes": 96.6e6,    # read 62.8 MB + write 33.8 MB
     },
 }
