@@ -435,11 +435,13 @@ def main_linear(args, w):
     dom_ms = part[dom] / n_launch
     dom_flops = state_flops(C, d, heads)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    # bf16 planes at width 64 run the state kernels on the matrix cores; otherwise fp32 vector ALU
+    # bf16 planes at width 64 run the state kernels on the bf16 matrix cores, complex64 at widths
+    # 16/32/64 on the fp32 matrix cores; otherwise the fp32 vector ALU
     mfma = w.layout == "bf16" and d == 64
-    bound, peak = ("mfma", PEAK_TFLOPS["bf16"]) if mfma else ("alu", PEAK_TFLOPS["c64"])
-    kname = {"merge": "born_merge_bf16_d64_kernel" if mfma else "born_merge_kernel",
-             "state": "born_state_bf16_d64_kernel" if mfma else "born_state_kernel"}[dom]
+    mfma32 = w.layout == "c64" and d in (16, 32, 64)
+    bound, peak = ("mfma", PEAK_TFLOPS["bf16"]) if mfma else ("mfma" if mfma32 else "alu", PEAK_TFLOPS["c64"])
+    suffix = "_bf16_d64" if mfma else "_f32" if mfma32 else ""
+    kname = f"born_{dom}{suffix}_kernel"
     rec = {"metric": f"Born chunked carried-state prefill head-tokens/s ({w.name}, chunk {C})",
            "value": tok_s, "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

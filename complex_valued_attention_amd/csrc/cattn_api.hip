@@ -390,6 +390,7 @@ cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, co
     p.accumulate = accumulate != 0;
     p.stream = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = cattn::supports_born_linear_bf16_d64(p) ? cattn::launch_born_state_bf16_d64(p)
+                         : cattn::supports_born_linear_f32(p)     ? cattn::launch_born_state_f32(p)
                                                                   : cattn::launch_born_state(p);
     return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
@@ -409,6 +410,7 @@ cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, co
     p.row_den = row_den;
     p.stream = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = cattn::supports_born_linear_bf16_d64(p) ? cattn::launch_born_merge_bf16_d64(p)
+                         : cattn::supports_born_linear_f32(p)     ? cattn::launch_born_merge_f32(p)
                                                                   : cattn::launch_born_merge(p);
     return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }

@@ -132,5 +132,9 @@ hipError_t launch_born_step(const LinearProblem &p);
 bool supports_born_linear_bf16_d64(const LinearProblem &p);
 hipError_t launch_born_merge_bf16_d64(const LinearProblem &p);
 hipError_t launch_born_state_bf16_d64(const LinearProblem &p);
+// fp32 matrix-core versions for complex64 at head widths 16, 32, 64
+bool supports_born_linear_f32(const LinearProblem &p);
+hipError_t launch_born_state_f32(const LinearProblem &p);
+hipError_t launch_born_merge_f32(const LinearProblem &p);
 
 }  // namespace cattn

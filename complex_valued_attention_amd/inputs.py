@@ -58,7 +58,8 @@ class Workload:
 # (d_h = 16), Born causal with rotary unit-norm Q/K at T = 1024, PCT full
 # attention at the Needle length 2048, the bf16 Born workload at T = 4096
 # (B 8, H 16, d_h 64) and PCT causal at the Path-X length 16384; then 32768-
-# and 65536-token bf16 Born sequences for the carried-state (linear) form.
+# and 65536-token bf16 Born sequences for the carried-state (linear) form,
+# and a 32768-token complex64 one for its fp32 matrix-core kernels.
 WORKLOADS = {
     w.name: w for w in [
         Workload("born_causal_c64_b1h1t128d16", "born", True, 1, 1, 128, 16, "c64", seed=0),
@@ -73,6 +74,8 @@ WORKLOADS = {
                  seed=5, qk_unit=True, rotary=True),
         Workload("born_causal_bf16_b1h16t65536d64_rotary", "born", True, 1, 16, 65536, 64, "bf16",
                  seed=6, qk_unit=True, rotary=True),
+        Workload("born_causal_c64_b1h16t32768d64_rotary", "born", True, 1, 16, 32768, 64, "c64",
+                 seed=7, qk_unit=True, rotary=True),
     ]
 }
 BENCH_WORKLOAD = "born_causal_bf16_b8h16t4096d64_rotary"

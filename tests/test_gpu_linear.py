@@ -66,6 +66,10 @@ STATE_CASES = [
     ("bf16", 2, 3, 333, 64),
     ("bf16", 1, 1, 65, 64),
     ("bf16", 1, 2, 1, 64),
+    # complex64 at widths 16/32/64 runs on the fp32 matrix cores
+    ("c64", 2, 3, 333, 64),
+    ("c64", 1, 2, 100, 32),
+    ("c64", 3, 1, 45, 16),
 ]
 
 
@@ -107,6 +111,9 @@ CARRY_CASES = [
     # ragged tails; 24 workgroups (the XCD-grouped order) and 3 (plain order)
     ("bf16", 2, 3, 1100, 300, 64, 0.0),
     ("bf16", 1, 1, 700, 129, 64, 0.25),
+    ("c64", 2, 3, 700, 300, 64, 0.0),
+    ("c64", 1, 2, 333, 100, 32, 0.25),
+    ("c64", 2, 2, 150, 17, 16, 0.0),
 ]
 
 
@@ -229,3 +236,33 @@ def test_step_at_full_head_count_sampled():
         say(f"  head ({b},{h}): out {err:.3e} state {es:.3e}")
         assert err <= TOL["bf16"]
         assert es <= state_tol("bf16", d)
+
+
+@pytest.mark.parametrize("B,H,T,T1,d", [(2, 16, 2200, 152, 64), (4, 16, 1100, 76, 16), (2, 16, 2100, 50, 32)])
+def test_prefill_with_carried_state_wide_sampled(B, H, T, T1, d):
+    """A carried-state prefill with enough heads and chunk tokens that the
+    complex64 readout takes its 128-token workgroups (the short-chunk tests
+    take the 32-token ones): sampled rows of every head against the oracle's
+    causal Born over the whole sequence."""
+    import oracle
+    from complex_valued_attention_amd import cattn
+    w = gen.Workload("carrywide", "born", True, B, H, T, d, "c64", seed=74, qk_unit=True)
+    inp = gen.make_inputs(w)
+    q, k, v = to_device(inp)
+    say(f"carry wide c64 B{B} H{H} T{T} split {T1} d{d}")
+    S = cattn.born_state_buffer(B, H, d)
+    cattn.born_state(_slice(k, 0, T1), _slice(v, 0, T1), S)
+    q2, k2, v2 = (_slice(x, T1, T) for x in (q, k, v))
+    row_den = torch.empty(B * H * (T - T1), dtype=torch.float32, device="cuda")
+    o2 = cattn.born_fwd(q2, k2, v2, causal=True, row_den=row_den)
+    cattn.born_merge(q2, S, o2, row_den)
+    torch.cuda.synchronize()
+    got = from_device(o2)
+    rng = np.random.default_rng(7)
+    ts = np.concatenate([[0, 1, 127, 128, T - T1 - 1], rng.integers(0, T - T1, 11)])
+    rows = np.array([(b, h, t) for b in range(B) for h in range(H) for t in ts])
+    ref = oracle.born_attention_rows(inp.q64, inp.k64, inp.v64, rows + np.array([0, 0, T1]), causal=True)
+    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
+    err = rowwise_rel_err(sel, ref)
+    say(f"  {len(rows)} sampled rows: {err:.3e}")
+    assert err <= TOL["c64"]
