@@ -56,6 +56,35 @@ CASES = [
 ]
 
 
+def screen_row_condition(w, inp, r, t):
+    """Relative condition number of each output row of the screening gate
+    w = r^2 relu(s - t)^2 with respect to relative errors in its scores:
+
+        kappa_row = sum_j |dw_j/ds_j| |s_j| |v_j| / max_c |O_row|,
+        dw/ds = 2 r^2 max(s - t, 0).
+
+    A row whose output comes from one key just above the threshold has
+    kappa = 2 s / (s - t), without bound as s comes down to t: fp32 scores
+    (relative error of a few units of 2^-24) then cannot give a fixed relative
+    accuracy whatever the order of summation.  Rows that share their weight
+    among keys well clear of t have kappa of order 1 to 10.
+    """
+    import oracle
+    s = oracle.pct_scores(inp.q64, inp.k64)
+    x = np.maximum(s - t, 0.0)
+    sens = 2 * r * r * x * np.abs(s)
+    if w.causal:
+        sens = sens * np.tril(np.ones((w.T, w.T)))
+    vmax = np.abs(inp.v64).max(axis=-1)                      # [B, H, T] per key
+    ref = oracle.pct_screen_attention(inp.q64, inp.k64, inp.v64, causal=w.causal, r=r, t=t)
+    num = np.einsum("bhij,bhj->bhi", sens, vmax)
+    den = np.abs(ref).max(axis=-1)
+    return np.where(num > 0, num / np.maximum(den, 1e-300), 0.0)
+
+
+KAPPA0 = 10.0   # the condition number up to which a row is held to the plain bar
+
+
 @pytest.mark.parametrize("gate,layout,causal,B,H,T,d,a,b", CASES)
 def test_gate_parity(gate, layout, causal, B, H, T, d, a, b):
     w = gen.Workload("gate", "pct", causal, B, H, T, d, layout, seed=41)
@@ -65,7 +94,18 @@ def test_gate_parity(gate, layout, causal, B, H, T, d, a, b):
     ref = run_oracle(w, inp.q64, inp.k64, inp.v64, gate, a, b)
     err = rowwise_rel_err(got, ref)
     say(f"gate {gate} {layout} causal={causal} B{B} H{H} T{T} d{d}: {err:.3e} (tol {TOL[layout]})")
-    assert err <= TOL[layout]
+    if gate != "screen":
+        assert err <= TOL[layout]
+        return
+    # screening gate: the row bar, scaled up only for rows whose condition
+    # number exceeds KAPPA0 (an active key just above the threshold)
+    kappa = screen_row_condition(w, inp, a, b)
+    bar = TOL[layout] * np.maximum(1.0, kappa / KAPPA0)
+    rowerr = np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-300)
+    rowerr = np.where(np.abs(ref).max(axis=-1) > 0, rowerr, np.abs(got).max(axis=-1))
+    say(f"  screen: rows above kappa {KAPPA0:g}: {int((kappa > KAPPA0).sum())} of {kappa.size}; "
+        f"worst error / bar = {float((rowerr / bar).max()):.3f}")
+    assert np.all(rowerr <= bar)
 
 
 def test_screen_threshold_above_bound_gives_zero():
