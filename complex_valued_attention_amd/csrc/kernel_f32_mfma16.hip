@@ -1,0 +1,355 @@
+// Born and phase-coherent attention forward on interleaved complex64 with
+// gfx950 fp32 matrix cores in their 16 x 16 form (v_mfma_f32_16x16x4_f32),
+// for causal attention over few heads.
+//
+// Why a second complex64 kernel.  With 32-query tiles a causal problem of
+// B*H heads of T tokens has B*H*T/32 tiles, and the last tile of a head does
+// twice the average work.  When that tile count is about the SIMD count (four
+// heads of 1024 tokens times eight, for instance) the grid cannot be balanced:
+// pairing a long tile with a short one halves the number of waves.  With
+// 16-query tiles there are twice as many tiles, and a wave takes the mirrored
+// pair (t, n - 1 - t) of a head, so every wave carries the same work and the
+// waves still cover every SIMD.
+//
+// Operators as in the 32 x 32 kernel ("CNet ...", section 11.2, Figure 2, for
+// Born; "Complex-valued Phase-Coherent Transformers", section 1 and Appendix
+// D.2, for the PCT cells).
+//
+// Products.  A complex64 row x is the real row x' = (Re x0, Im x0, Re x1, ...)
+// of width 2d.  With q''' = (Im q0, -Re q0, Im q1, -Re q1, ...),
+//     Re <q, k> = sum_n k'[n] q'[n],   Im <q, k> = sum_n k'[n] q'''[n]
+// (<q, k> = sum_m q_m conj(k_m)), so one K' operand read from LDS feeds both
+// products and the two query operands q', q''' stay in registers.  Scores are
+// formed transposed, S^T = K' Q'^T: keys are MFMA rows, queries columns.  The
+// contraction index is visited in any order that the A and B operands share;
+// lane group g = lane / 16 takes the contiguous quarter [g d/2, (g+1) d/2) of
+// the row, so each lane reads its K' slice with wide LDS reads.
+//
+// Values.  O'^T += V'^T W^T over a 16-key block in 4 steps of 4 keys.  Lane
+// (g, query j) holds S^T rows (keys) 4 g + r, r = 0..3; step t uses key 4 g + t
+// from lane group g, which is its own register r = t, so the weights need no
+// shuffle.  Output channel tile c, row i stands for real channel (d/8) i + c, so
+// the V' slice a lane needs for one key is d/8 contiguous floats, and the output
+// rows a lane ends with are 4 (d/8) contiguous floats of its query.
+#include "cattn_internal.h"
+
+namespace cattn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NW = 4;          // waves per workgroup
+constexpr int NT = 64 * NW;    // threads
+constexpr int TQ = 16;         // queries per wave tile
+constexpr int BM = TQ * NW;    // queries per row block
+constexpr int BN = 32;         // keys per LDS stage (two 16-key blocks)
+
+template <int D>
+struct Cfg16 {
+    static constexpr int KD = 2 * D;        // real width of a row
+    static constexpr int KQ = KD / 4;       // contraction floats per lane group (= k-steps)
+    static constexpr int NC = KD / 16;      // 16-row channel tiles of O'^T
+    static constexpr int CPL = KD / 16;     // channels per lane per key in the value operand
+    static constexpr int ROW = KD + 4;      // padded LDS row (floats) of K' and V'
+    static constexpr int STAGE = 2 * BN * ROW + BN;   // K', V', per-key inverse norms
+    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    static constexpr int LPK = NT / BN;               // staging lanes per key (8)
+    static constexpr int CPT = (KD / 4) / LPK;        // float4 chunks per staging lane
+};
+
+// n floats from LDS into registers with the widest reads that fit
+template <int N>
+__device__ inline void lds_row(const float *p, float (&out)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(p + 4 * i);
+            out[4 * i] = x[0];
+            out[4 * i + 1] = x[1];
+            out[4 * i + 2] = x[2];
+            out[4 * i + 3] = x[3];
+        }
+    } else {
+        static_assert(N % 2 == 0, "even slices only");
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const f32x2 x = *reinterpret_cast<const f32x2 *>(p + 2 * i);
+            out[2 * i] = x[0];
+            out[2 * i + 1] = x[1];
+        }
+    }
+}
+
+__device__ inline f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, int OP>
+__global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb, int nwork) {
+    using C = Cfg16<D>;
+    static_assert(C::CPT >= 1, "head width too small for this staging split");
+    extern __shared__ __align__(16) float fsm[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j16 = lane & 15;   // query column (scores, values) / key row (K' operand)
+    const int g = lane >> 4;     // lane group
+    const int T = p.T;
+
+    // Workgroup -> (head, item); all items of a head on one XCD when BH % 8 == 0
+    const int L = blockIdx.x;
+    int bh, item;
+    if ((p.BH & 7) == 0) {
+        const int x = L & 7, jj = L >> 3;
+        bh = x + 8 * (jj / nwork);
+        item = jj % nwork;
+    } else {
+        bh = L / nwork;
+        item = L % nwork;
+    }
+    const int64_t head = (int64_t)bh * T * C::KD;   // in floats
+    const float *qg = reinterpret_cast<const float *>(p.q_re) + head;
+    const float *kg = reinterpret_cast<const float *>(p.k_re) + head;
+    const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
+    float *og = reinterpret_cast<float *>(p.o_re) + head;
+
+    // causal: the mirrored pair of row blocks (long one first); otherwise one
+    const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
+
+    // staging: lane t holds CPT consecutive float4 chunks of key t / LPK
+    const int skey = tid / C::LPK;
+    const int schunk = (tid % C::LPK) * C::CPT;
+    f32x4 kreg[C::CPT], vreg[C::CPT];
+    auto load_stage = [&](int k0) {
+        const int kr = k0 + skey;
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            if (kr < T) {
+                a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * (schunk + i));
+                b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * (schunk + i));
+            }
+            kreg[i] = a;
+            vreg[i] = b;
+        }
+    };
+    auto store_stage = [&](int buf) {
+        float *ks = fsm + buf * C::STAGE;
+        float *vs = ks + BN * C::ROW;
+        float *rk = vs + BN * C::ROW;
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+            *reinterpret_cast<f32x4 *>(ks + skey * C::ROW + 4 * (schunk + i)) = kreg[i];
+            *reinterpret_cast<f32x4 *>(vs + skey * C::ROW + 4 * (schunk + i)) = vreg[i];
+        }
+        if (OP != OP_BORN) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < C::CPT; ++i)
+                ss += kreg[i][0] * kreg[i][0] + kreg[i][1] * kreg[i][1] + kreg[i][2] * kreg[i][2] +
+                      kreg[i][3] * kreg[i][3];
+#pragma unroll
+            for (int o = 1; o < C::LPK; o <<= 1) ss += __shfl_xor(ss, o);
+            if (tid % C::LPK == 0) rk[skey] = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+        }
+    };
+
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const int rb = p.causal ? (blk == 0 ? nrb - 1 - item : item) : item;
+        const int m0 = rb * BM;
+        const int qt0 = m0 + TQ * wave;   // first query of this wave's tile
+        const int qrow = qt0 + j16;
+
+        // query operands: q' and q''' over this lane group's quarter of the row
+        float qre[C::KQ], qim[C::KQ];
+        {
+            f32x4 x[C::KQ / 4];
+#pragma unroll
+            for (int i = 0; i < C::KQ / 4; ++i) {
+                x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (qrow < T) x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qrow * C::KD + g * C::KQ + 4 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < C::KQ / 4; ++i) {
+                qre[4 * i] = x[i][0];
+                qre[4 * i + 1] = x[i][1];
+                qre[4 * i + 2] = x[i][2];
+                qre[4 * i + 3] = x[i][3];
+                // (Im, -Re) per complex element; a quarter starts on an element boundary
+                qim[4 * i] = x[i][1];
+                qim[4 * i + 1] = -x[i][0];
+                qim[4 * i + 2] = x[i][3];
+                qim[4 * i + 3] = -x[i][2];
+            }
+        }
+        float rq = 0.f;
+        if (OP != OP_BORN) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < C::KQ; ++i) ss += qre[i] * qre[i];
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            rq = ss > 0.f ? sqrtf((float)D) / sqrtf(ss) : 0.f;   // sqrt(d_h) / ||q||, 0 for a zero row
+        }
+
+        f32x4 oacc[C::NC];
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float rsum = 0.f;
+
+        const int kend = p.causal ? min(T, m0 + BM) : T;
+        const int nstages = (kend + BN - 1) / BN;
+
+        __syncthreads();   // the previous row block is done with both stage buffers
+        if (nstages > 0) {
+            load_stage(0);
+            store_stage(0);
+        }
+        __syncthreads();
+
+        for (int st = 0; st < nstages; ++st) {
+            const int k0 = st * BN;
+            const int buf = st & 1;
+            if (st + 1 < nstages) load_stage(k0 + BN);
+            const float *ks = fsm + buf * C::STAGE;
+            const float *vs = ks + BN * C::ROW;
+            const float *rk = vs + BN * C::ROW;
+
+#pragma unroll
+            for (int sb = 0; sb < BN / 16; ++sb) {
+                const int kb0 = k0 + 16 * sb;
+                if (kb0 >= T || (p.causal && kb0 > qt0) || qt0 >= T) continue;
+                const bool diag = p.causal && kb0 == qt0;
+
+                // S^T for 16 keys x 16 queries
+                float ka[C::KQ];
+                lds_row<C::KQ>(ks + (16 * sb + j16) * C::ROW + g * C::KQ, ka);
+                f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < C::KQ; ++s) {
+                    sr = mfma16(ka[s], qre[s], sr);
+                    if (OP == OP_BORN) si = mfma16(ka[s], qim[s], si);
+                }
+
+                // weights: register r is key 4 g + r of the block
+                float w[4];
+                if (OP == OP_BORN) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = sr[r] * sr[r] + si[r] * si[r];
+                } else {
+                    const f32x4 rkv = *reinterpret_cast<const f32x4 *>(rk + 16 * sb + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = sr[r] * rq * rkv[r];   // sqrt(d_h) Re<qh, kh>
+                        if (OP == OP_PCT) {
+                            w[r] = 1.f / (1.f + __expf(-(x + p.bias)));
+                        } else if (OP == OP_PCT_SOFTMAX) {
+                            w[r] = __expf(x);   // |x| <= sqrt(d_h): no shift needed
+                        } else {
+                            const float y = fmaxf(x - p.gate_t, 0.f);
+                            w[r] = p.gate_r * p.gate_r * y * y;
+                        }
+                    }
+                }
+                if (diag || kb0 + 16 > T) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = 4 * g + r;
+                        if ((diag && key > j16) || kb0 + key >= T) w[r] = 0.f;
+                    }
+                }
+                if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) rsum += (w[0] + w[1]) + (w[2] + w[3]);
+
+                // O'^T += V'^T W^T: step t takes key 4 g + t from lane group g
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    float va[C::CPL];
+                    lds_row<C::CPL>(vs + (16 * sb + 4 * g + t) * C::ROW + C::CPL * j16, va);
+#pragma unroll
+                    for (int c = 0; c < C::NC; ++c) oacc[c] = mfma16(va[c], w[t], oacc[c]);
+                }
+            }
+
+            if (st + 1 < nstages) store_stage(buf ^ 1);
+            __syncthreads();
+        }
+
+        // epilogue: lane (g, query j16) holds O'^T rows 4 g + r of tile c, i.e.
+        // real channel CPL (4 g + r) + c of its query: 4 CPL contiguous floats.
+        float scale = 1.f;
+        float den = 0.f;
+        if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) {
+            den = rsum + __shfl_xor(rsum, 16);
+            den += __shfl_xor(den, 32);
+            if (OP == OP_BORN) den += p.eps;
+            scale = den != 0.f ? 1.f / den : 0.f;
+        }
+        if (qrow < T) {
+            float *orow = og + (int64_t)qrow * C::KD + 4 * C::CPL * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (C::CPL % 4 == 0) {
+#pragma unroll
+                    for (int c = 0; c < C::NC; c += 4) {
+                        const f32x4 v = {oacc[c][r] * scale, oacc[c + 1][r] * scale, oacc[c + 2][r] * scale,
+                                         oacc[c + 3][r] * scale};
+                        *reinterpret_cast<f32x4 *>(orow + C::CPL * r + c) = v;
+                    }
+                } else {
+                    const f32x2 v = {oacc[0][r] * scale, oacc[1][r] * scale};
+                    *reinterpret_cast<f32x2 *>(orow + C::CPL * r) = v;
+                }
+            }
+            if (OP == OP_BORN && p.row_den && g == 0) p.row_den[(int64_t)bh * T + qrow] = den;
+        }
+    }
+}
+
+template <int D, int OP>
+hipError_t launch_cfg16(const Problem &p) {
+    using C = Cfg16<D>;
+    auto kern = attn_f32_mfma16_kernel<D, OP>;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
+    const int nrb = (p.T + BM - 1) / BM;
+    const int nwork = p.causal ? (nrb + 1) / 2 : nrb;
+    const int64_t blocks = (int64_t)p.BH * nwork;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nrb, nwork);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d16(const Problem &p) {
+    switch (p.op) {
+        case OP_BORN: return launch_cfg16<D, OP_BORN>(p);
+        case OP_PCT: return launch_cfg16<D, OP_PCT>(p);
+        case OP_PCT_SOFTMAX: return launch_cfg16<D, OP_PCT_SOFTMAX>(p);
+        default: return launch_cfg16<D, OP_PCT_SCREEN>(p);
+    }
+}
+
+}  // namespace
+
+bool supports_f32_mfma16(const Problem &p) {
+    return p.layout == LAYOUT_C64 && (p.d == 16 || p.d == 32 || p.d == 64);
+}
+
+// Causal attention: mirrored pairs of 16-query tiles balance the grid at any
+// head count.  Without a mask every tile carries the same work and the 32 x 32
+// kernel (half the LDS reads per flop) is as fast.
+bool prefer_f32_mfma16(const Problem &p) { return p.causal != 0; }
+
+hipError_t launch_f32_mfma16(const Problem &p) {
+    switch (p.d) {
+        case 16: return launch_d16<16>(p);
+        case 32: return launch_d16<32>(p);
+        case 64: return launch_d16<64>(p);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace cattn
