@@ -94,10 +94,8 @@ cattn_status run(const Problem &p) {
         e = cattn::launch_born_bf16_d64(p);
     else if (cattn::supports_born_bf16_mfma(p))
         e = cattn::launch_born_bf16_mfma(p);
-    else if (cattn::supports_f32_mfma16(p) && cattn::prefer_f32_mfma16(p))
+    else if (cattn::supports_f32_mfma16(p))
         e = cattn::launch_f32_mfma16(p);
-    else if (cattn::supports_f32_mfma(p))
-        e = cattn::launch_f32_mfma(p);
     else
         e = cattn::launch_generic(p);
     return e == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;

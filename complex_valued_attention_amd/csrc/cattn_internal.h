@@ -61,13 +61,8 @@ hipError_t launch_born_bf16_d64(const Problem &p);
 bool supports_born_bf16_mfma(const Problem &p);
 hipError_t launch_born_bf16_mfma(const Problem &p);
 
-bool supports_f32_mfma(const Problem &p);
-hipError_t launch_f32_mfma(const Problem &p);
-
-// complex64 on 16 x 16 fp32 matrix tiles with mirrored causal pairs of
-// 16-query tiles; preferred where 32-query tiles cannot balance the grid
+// complex64 on 16 x 16 fp32 matrix tiles, pairs of 64-query row blocks
 bool supports_f32_mfma16(const Problem &p);
-bool prefer_f32_mfma16(const Problem &p);
 hipError_t launch_f32_mfma16(const Problem &p);
 
 // One validated backward call (same [BH, T, d] layout).  G = dL/d(conj O);

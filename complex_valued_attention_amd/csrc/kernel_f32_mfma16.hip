@@ -1,19 +1,26 @@
 // Born and phase-coherent attention forward on interleaved complex64 with
 // gfx950 fp32 matrix cores in their 16 x 16 form (v_mfma_f32_16x16x4_f32),
-// for causal attention over few heads.
+// fp32 throughout.
 //
-// Why a second complex64 kernel.  With 32-query tiles a causal problem of
-// B*H heads of T tokens has B*H*T/32 tiles, and the last tile of a head does
-// twice the average work.  When that tile count is about the SIMD count (four
-// heads of 1024 tokens times eight, for instance) the grid cannot be balanced:
-// pairing a long tile with a short one halves the number of waves.  With
-// 16-query tiles there are twice as many tiles, and a wave takes the mirrored
-// pair (t, n - 1 - t) of a head, so every wave carries the same work and the
-// waves still cover every SIMD.
+// Operators.  Born ("CNet: A Complex-Valued Deep Learning Framework ...",
+// section 11.2, "Closing it: Born-rule attention", Figure 2): w = |<q, k>|^2
+// with a running row sum (no running maximum: w >= 0), O = acc / sum.  PCT
+// ("Complex-valued Phase-Coherent Transformers", section 1 and Appendix D.2):
+// w = sigmoid(sqrt(d_h) Re<q,k> / (|q| |k|) + b), O = acc, and the cells of the
+// same family on that score (L2-softmax, screening gate).  The query norms
+// come from the resident query operands, the key norms are reduced while a
+// key stage is staged into LDS.
 //
-// Operators as in the 32 x 32 kernel ("CNet ...", section 11.2, Figure 2, for
-// Born; "Complex-valued Phase-Coherent Transformers", section 1 and Appendix
-// D.2, for the PCT cells).
+// Why 16-query tiles.  With 32-query tiles a causal problem of B*H heads of T
+// tokens has B*H*T/32 tiles, and the last tile of a head does twice the
+// average work.  When that tile count is about the SIMD count (four heads of
+// 1024 tokens times eight, for instance) the grid cannot be balanced: pairing
+// a long tile with a short one halves the number of waves.  With 16-query
+// tiles there are twice as many tiles.  A workgroup of eight waves takes a
+// pair of 64-query row blocks of a head at once, one wave of each block per
+// SIMD: causal, the mirrored pair (nrb - 1 - i, i), so every SIMD carries the
+// same work; without a mask, two neighbouring blocks.  Two waves are resident
+// per SIMD to hide each other's latency.
 //
 // Products.  A complex64 row x is the real row x' = (Re x0, Im x0, Re x1, ...)
 // of width 2d.  With q''' = (Im q0, -Re q0, Im q1, -Re q1, ...),
@@ -39,10 +46,11 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;          // waves per workgroup
+constexpr int NW = 8;          // waves per workgroup: two row blocks of four tiles
 constexpr int NT = 64 * NW;    // threads
+constexpr int NST = 256;       // threads that stage K and V (the first four waves)
 constexpr int TQ = 16;         // queries per wave tile
-constexpr int BM = TQ * NW;    // queries per row block
+constexpr int BM = TQ * 4;     // queries per row block
 constexpr int BN = 32;         // keys per LDS stage (two 16-key blocks)
 
 template <int D>
@@ -54,7 +62,7 @@ struct Cfg16 {
     static constexpr int ROW = KD + 4;      // padded LDS row (floats) of K' and V'
     static constexpr int STAGE = 2 * BN * ROW + BN;   // K', V', per-key inverse norms
     static constexpr int LDS_BYTES = 2 * STAGE * 4;
-    static constexpr int LPK = NT / BN;               // staging lanes per key (8)
+    static constexpr int LPK = NST / BN;              // staging lanes per key (8)
     static constexpr int CPT = (KD / 4) / LPK;        // float4 chunks per staging lane
 };
 
@@ -115,8 +123,23 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
     float *og = reinterpret_cast<float *>(p.o_re) + head;
 
-    // causal: the mirrored pair of row blocks (long one first); otherwise one
-    const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
+    // Waves 0-3 take the four tiles of the first row block of the item, waves
+    // 4-7 those of the second, at the same time: a SIMD holds one wave of each.
+    // Causal: the mirrored pair nrb-1-item (long) and item (short), whose key
+    // range is a prefix of the long one's, so both read the same stages.  The
+    // middle block of an odd count has no partner.  Without a mask: the row
+    // blocks 2 item and 2 item + 1.
+    const int half = wave >> 2;
+    int rb;
+    if (p.causal)
+        rb = half == 0 ? nrb - 1 - item : (item != nrb - 1 - item ? item : -1);
+    else
+        rb = 2 * item + half < nrb ? 2 * item + half : -1;
+    const int m0 = rb * BM;
+    const int qt0 = m0 + TQ * (wave & 3);   // first query of this wave's tile
+    const int qrow = qt0 + j16;
+    const bool live = rb >= 0 && qt0 < T;
+    const bool stager = tid < NST;           // wave-uniform
 
     // staging: lane t holds CPT consecutive float4 chunks of key t / LPK
     const int skey = tid / C::LPK;
@@ -156,12 +179,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         }
     };
 
-    for (int blk = 0; blk < nblocks; ++blk) {
-        const int rb = p.causal ? (blk == 0 ? nrb - 1 - item : item) : item;
-        const int m0 = rb * BM;
-        const int qt0 = m0 + TQ * wave;   // first query of this wave's tile
-        const int qrow = qt0 + j16;
-
+    {
         // query operands: q' and q''' over this lane group's quarter of the row
         float qre[C::KQ], qim[C::KQ];
         {
@@ -169,7 +187,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
 #pragma unroll
             for (int i = 0; i < C::KQ / 4; ++i) {
                 x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (qrow < T) x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qrow * C::KD + g * C::KQ + 4 * i);
+                if (live && qrow < T)
+                    x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qrow * C::KD + g * C::KQ + 4 * i);
             }
 #pragma unroll
             for (int i = 0; i < C::KQ / 4; ++i) {
@@ -199,11 +218,11 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         for (int c = 0; c < C::NC; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         float rsum = 0.f;
 
-        const int kend = p.causal ? min(T, m0 + BM) : T;
+        // keys for both row blocks: the first (long) one's range
+        const int kend = p.causal ? min(T, (nrb - 1 - item) * BM + BM) : T;
         const int nstages = (kend + BN - 1) / BN;
 
-        __syncthreads();   // the previous row block is done with both stage buffers
-        if (nstages > 0) {
+        if (stager && nstages > 0) {
             load_stage(0);
             store_stage(0);
         }
@@ -212,7 +231,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         for (int st = 0; st < nstages; ++st) {
             const int k0 = st * BN;
             const int buf = st & 1;
-            if (st + 1 < nstages) load_stage(k0 + BN);
+            if (stager && st + 1 < nstages) load_stage(k0 + BN);
             const float *ks = fsm + buf * C::STAGE;
             const float *vs = ks + BN * C::ROW;
             const float *rk = vs + BN * C::ROW;
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
 #pragma unroll
             for (int sb = 0; sb < BN / 16; ++sb) {
                 const int kb0 = k0 + 16 * sb;
-                if (kb0 >= T || (p.causal && kb0 > qt0) || qt0 >= T) continue;
+                if (!live || kb0 >= T || (p.causal && kb0 > qt0)) continue;
                 const bool diag = p.causal && kb0 == qt0;
 
                 // S^T for 16 keys x 16 queries
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                 }
             }
 
-            if (st + 1 < nstages) store_stage(buf ^ 1);
+            if (stager && st + 1 < nstages) store_stage(buf ^ 1);
             __syncthreads();
         }
 
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             if (OP == OP_BORN) den += p.eps;
             scale = den != 0.f ? 1.f / den : 0.f;
         }
-        if (qrow < T) {
+        if (live && qrow < T) {
             float *orow = og + (int64_t)qrow * C::KD + 4 * C::CPL * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -315,7 +334,7 @@ hipError_t launch_cfg16(const Problem &p) {
     const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     const int nrb = (p.T + BM - 1) / BM;
-    const int nwork = p.causal ? (nrb + 1) / 2 : nrb;
+    const int nwork = (nrb + 1) / 2;   // row blocks in pairs, causal or not
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nrb, nwork);
@@ -341,8 +360,6 @@ bool supports_f32_mfma16(const Problem &p) {
 // Causal attention: mirrored pairs of 16-query tiles balance the grid at any
 // head count.  Without a mask every tile carries the same work and the 32 x 32
 // kernel (half the LDS reads per flop) is as fast.
-bool prefer_f32_mfma16(const Problem &p) { return p.causal != 0; }
-
 hipError_t launch_f32_mfma16(const Problem &p) {
     switch (p.d) {
         case 16: return launch_d16<16>(p);
