@@ -179,124 +179,52 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         }
     };
 
-    {
-        // query operands: q' and q''' over this lane group's quarter of the row
-        float qre[C::KQ], qim[C::KQ];
-        {
-            f32x4 x[C::KQ / 4];
+    // query operands q', q''' over this lane group's quarter of the row, and
+    // PCT's sqrt(d_h) / |q| (0 for a zero row)
+    float qre[C::KQ], qim[C::KQ];
+    float rq = 0.f;
+    auto load_q = [&](int qt, bool ok) {
+        const int qr = qt + j16;
+        f32x4 x[C::KQ / 4];
 #pragma unroll
-            for (int i = 0; i < C::KQ / 4; ++i) {
-                x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (live && qrow < T)
-                    x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qrow * C::KD + g * C::KQ + 4 * i);
-            }
-#pragma unroll
-            for (int i = 0; i < C::KQ / 4; ++i) {
-                qre[4 * i] = x[i][0];
-                qre[4 * i + 1] = x[i][1];
-                qre[4 * i + 2] = x[i][2];
-                qre[4 * i + 3] = x[i][3];
-                // (Im, -Re) per complex element; a quarter starts on an element boundary
-                qim[4 * i] = x[i][1];
-                qim[4 * i + 1] = -x[i][0];
-                qim[4 * i + 2] = x[i][3];
-                qim[4 * i + 3] = -x[i][2];
-            }
+        for (int i = 0; i < C::KQ / 4; ++i) {
+            x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ok && qr < T) x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qr * C::KD + g * C::KQ + 4 * i);
         }
-        float rq = 0.f;
+#pragma unroll
+        for (int i = 0; i < C::KQ / 4; ++i) {
+            qre[4 * i] = x[i][0];
+            qre[4 * i + 1] = x[i][1];
+            qre[4 * i + 2] = x[i][2];
+            qre[4 * i + 3] = x[i][3];
+            // (Im, -Re) per complex element; a quarter starts on an element boundary
+            qim[4 * i] = x[i][1];
+            qim[4 * i + 1] = -x[i][0];
+            qim[4 * i + 2] = x[i][3];
+            qim[4 * i + 3] = -x[i][2];
+        }
         if (OP != OP_BORN) {
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < C::KQ; ++i) ss += qre[i] * qre[i];
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
-            rq = ss > 0.f ? sqrtf((float)D) / sqrtf(ss) : 0.f;   // sqrt(d_h) / ||q||, 0 for a zero row
+            rq = ss > 0.f ? sqrtf((float)D) / sqrtf(ss) : 0.f;
         }
+    };
 
-        f32x4 oacc[C::NC];
+    f32x4 oacc[C::NC];
+    float rsum = 0.f;
+    auto reset = [&]() {
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float rsum = 0.f;
+        rsum = 0.f;
+    };
 
-        // keys for both row blocks: the first (long) one's range
-        const int kend = p.causal ? min(T, (nrb - 1 - item) * BM + BM) : T;
-        const int nstages = (kend + BN - 1) / BN;
-
-        if (stager && nstages > 0) {
-            load_stage(0);
-            store_stage(0);
-        }
-        __syncthreads();
-
-        for (int st = 0; st < nstages; ++st) {
-            const int k0 = st * BN;
-            const int buf = st & 1;
-            if (stager && st + 1 < nstages) load_stage(k0 + BN);
-            const float *ks = fsm + buf * C::STAGE;
-            const float *vs = ks + BN * C::ROW;
-            const float *rk = vs + BN * C::ROW;
-
-#pragma unroll
-            for (int sb = 0; sb < BN / 16; ++sb) {
-                const int kb0 = k0 + 16 * sb;
-                if (!live || kb0 >= T || (p.causal && kb0 > qt0)) continue;
-                const bool diag = p.causal && kb0 == qt0;
-
-                // S^T for 16 keys x 16 queries
-                float ka[C::KQ];
-                lds_row<C::KQ>(ks + (16 * sb + j16) * C::ROW + g * C::KQ, ka);
-                f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < C::KQ; ++s) {
-                    sr = mfma16(ka[s], qre[s], sr);
-                    if (OP == OP_BORN) si = mfma16(ka[s], qim[s], si);
-                }
-
-                // weights: register r is key 4 g + r of the block
-                float w[4];
-                if (OP == OP_BORN) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = sr[r] * sr[r] + si[r] * si[r];
-                } else {
-                    const f32x4 rkv = *reinterpret_cast<const f32x4 *>(rk + 16 * sb + 4 * g);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float x = sr[r] * rq * rkv[r];   // sqrt(d_h) Re<qh, kh>
-                        if (OP == OP_PCT) {
-                            w[r] = 1.f / (1.f + __expf(-(x + p.bias)));
-                        } else if (OP == OP_PCT_SOFTMAX) {
-                            w[r] = __expf(x);   // |x| <= sqrt(d_h): no shift needed
-                        } else {
-                            const float y = fmaxf(x - p.gate_t, 0.f);
-                            w[r] = p.gate_r * p.gate_r * y * y;
-                        }
-                    }
-                }
-                if (diag || kb0 + 16 > T) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = 4 * g + r;
-                        if ((diag && key > j16) || kb0 + key >= T) w[r] = 0.f;
-                    }
-                }
-                if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) rsum += (w[0] + w[1]) + (w[2] + w[3]);
-
-                // O'^T += V'^T W^T: step t takes key 4 g + t from lane group g
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    float va[C::CPL];
-                    lds_row<C::CPL>(vs + (16 * sb + 4 * g + t) * C::ROW + C::CPL * j16, va);
-#pragma unroll
-                    for (int c = 0; c < C::NC; ++c) oacc[c] = mfma16(va[c], w[t], oacc[c]);
-                }
-            }
-
-            if (stager && st + 1 < nstages) store_stage(buf ^ 1);
-            __syncthreads();
-        }
-
-        // epilogue: lane (g, query j16) holds O'^T rows 4 g + r of tile c, i.e.
-        // real channel CPL (4 g + r) + c of its query: 4 CPL contiguous floats.
+    // epilogue: lane (g, query j16) holds O'^T rows 4 g + r of tile c, i.e.
+    // real channel CPL (4 g + r) + c of its query: 4 CPL contiguous floats.
+    auto write_out = [&](int qt) {
+        const int qr = qt + j16;
         float scale = 1.f;
         float den = 0.f;
         if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) {
@@ -305,8 +233,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             if (OP == OP_BORN) den += p.eps;
             scale = den != 0.f ? 1.f / den : 0.f;
         }
-        if (live && qrow < T) {
-            float *orow = og + (int64_t)qrow * C::KD + 4 * C::CPL * g;
+        if (qr < T) {
+            float *orow = og + (int64_t)qr * C::KD + 4 * C::CPL * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (C::CPL % 4 == 0) {
@@ -321,9 +249,139 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                     *reinterpret_cast<f32x2 *>(orow + C::CPL * r) = v;
                 }
             }
-            if (OP == OP_BORN && p.row_den && g == 0) p.row_den[(int64_t)bh * T + qrow] = den;
+            if (OP == OP_BORN && p.row_den && g == 0) p.row_den[(int64_t)bh * T + qr] = den;
+        }
+    };
+
+    // Causal: a wave of the short block, once past its own diagonal, helps the
+    // long tile of its SIMD partner (wave - 4).  From stage st_switch on, the
+    // partner keeps the first 16-key block of each stage and the helper takes
+    // the second; at the end the helper's partial sums are added to the
+    // partner's through LDS, in a fixed order, so the result does not depend on
+    // timing.  Without a short block (the middle block of an odd count) the
+    // helpers start at once.  Without a mask nothing is shared.
+    const int tq = wave & 3;
+    const int rbL = nrb - 1 - item;
+    const int qtL = rbL * BM + TQ * tq;          // the long tile of this SIMD slot
+    const bool liveL = p.causal && qtL < T;
+    int st_switch = 0x7fffffff;
+    if (p.causal) st_switch = item != rbL ? (item * BM + TQ * tq) / BN + 1 : 0;
+
+    // keys for both row blocks: the first (long) one's range
+    const int kend = p.causal ? min(T, rbL * BM + BM) : T;
+    const int nstages = (kend + BN - 1) / BN;
+
+    int qt_cur = qt0;
+    bool live_cur = live;
+    bool helping = false;
+    load_q(qt0, live);
+    reset();
+
+    if (stager && nstages > 0) {
+        load_stage(0);
+        store_stage(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < nstages; ++st) {
+        const int k0 = st * BN;
+        const int buf = st & 1;
+        if (half == 1 && st == st_switch) {   // wave-uniform
+            if (live) write_out(qt0);
+            helping = true;
+            qt_cur = qtL;
+            live_cur = liveL;
+            load_q(qtL, liveL);
+            reset();
+        }
+        const bool split = st >= st_switch;
+        if (stager && st + 1 < nstages) load_stage(k0 + BN);
+        const float *ks = fsm + buf * C::STAGE;
+        const float *vs = ks + BN * C::ROW;
+        const float *rk = vs + BN * C::ROW;
+
+#pragma unroll
+        for (int sb = 0; sb < BN / 16; ++sb) {
+            if (split && sb != half) continue;   // long wave: block 0, helper: block 1
+            const int kb0 = k0 + 16 * sb;
+            if (!live_cur || kb0 >= T || (p.causal && kb0 > qt_cur)) continue;
+            const bool diag = p.causal && kb0 == qt_cur;
+
+            // S^T for 16 keys x 16 queries
+            float ka[C::KQ];
+            lds_row<C::KQ>(ks + (16 * sb + j16) * C::ROW + g * C::KQ, ka);
+            f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < C::KQ; ++s2) {
+                sr = mfma16(ka[s2], qre[s2], sr);
+                if (OP == OP_BORN) si = mfma16(ka[s2], qim[s2], si);
+            }
+
+            // weights: register r is key 4 g + r of the block
+            float w[4];
+            if (OP == OP_BORN) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = sr[r] * sr[r] + si[r] * si[r];
+            } else {
+                const f32x4 rkv = *reinterpret_cast<const f32x4 *>(rk + 16 * sb + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = sr[r] * rq * rkv[r];   // sqrt(d_h) Re<qh, kh>
+                    if (OP == OP_PCT) {
+                        w[r] = 1.f / (1.f + __expf(-(x + p.bias)));
+                    } else if (OP == OP_PCT_SOFTMAX) {
+                        w[r] = __expf(x);   // |x| <= sqrt(d_h): no shift needed
+                    } else {
+                        const float y = fmaxf(x - p.gate_t, 0.f);
+                        w[r] = p.gate_r * p.gate_r * y * y;
+                    }
+                }
+            }
+            if (diag || kb0 + 16 > T) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 4 * g + r;
+                    if ((diag && key > j16) || kb0 + key >= T) w[r] = 0.f;
+                }
+            }
+            if (OP == OP_BORN || OP == OP_PCT_SOFTMAX) rsum += (w[0] + w[1]) + (w[2] + w[3]);
+
+            // O'^T += V'^T W^T: step t takes key 4 g + t from lane group g
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float va[C::CPL];
+                lds_row<C::CPL>(vs + (16 * sb + 4 * g + t) * C::ROW + C::CPL * j16, va);
+#pragma unroll
+                for (int c = 0; c < C::NC; ++c) oacc[c] = mfma16(va[c], w[t], oacc[c]);
+            }
+        }
+
+        if (stager && st + 1 < nstages) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // merge the helpers' partial sums (the stage buffers are free now)
+    if (p.causal) {
+        constexpr int PW = 4 * C::NC + 1;   // floats per lane of one partial
+        static_assert(4 * PW * 64 <= 2 * C::STAGE, "partials fit in the stage buffers");
+        float *part = fsm + tq * PW * 64 + lane;
+        if (helping && liveL) {
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part[(4 * c + r) * 64] = oacc[c][r];
+            part[4 * C::NC * 64] = rsum;
+        }
+        __syncthreads();
+        if (half == 0 && st_switch < nstages && liveL) {
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[c][r] += part[(4 * c + r) * 64];
+            rsum += part[4 * C::NC * 64];
         }
     }
+    if (!helping && live_cur) write_out(qt_cur);
 }
 
 template <int D, int OP>
