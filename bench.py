@@ -47,6 +47,21 @@ MEASURED_TRAFFIC = {
         "sha256": "1ea06ab789c9db176c51489e8839f1ee6cad3e1863445d4fac4248dcb78e7f02",
         "bytes": 882.4e6,   # read 748.1 MB + write 134.2 MB
     },
+    "born_causal_c64_b4h8t1024d64_rotary": {
+        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
+        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
+        "bytes": 72.0e6,   # read 55.2 MB + write 16.8 MB
+    },
+    "pct_full_c64_b8h8t2048d64": {
+        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
+        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
+        "bytes": 268.7e6,   # read 201.5 MB + write 67.2 MB
+    },
+    "pct_causal_c64_b1h8t16384d64": {
+        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
+        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
+        "bytes": 599.7e6,   # read 532.6 MB + write 67.1 MB
+    },
     # one-token step with the carried state: born_step_kernel
     "step:born_causal_bf16_b8h16t4096d64_rotary": {
         "source": "complex_valued_attention_amd/csrc/kernel_born_linear.hip",
@@ -619,7 +634,8 @@ def main():
                    "d_h": w.d_h, "layout": w.layout, "seed": w.seed,
                    **({} if args.gate == "sigmoid" else {"gate": args.gate})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(name),
+                     "frac": achieved / peak,
+                     "traffic": measured_traffic(name) if args.gate == "sigmoid" else None,
                      "kernel": kernel_name(w),
                      "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per))},
     }
