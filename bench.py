@@ -49,18 +49,18 @@ MEASURED_TRAFFIC = {
     },
     "born_causal_c64_b4h8t1024d64_rotary": {
         "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
-        "bytes": 72.0e6,   # read 55.2 MB + write 16.8 MB
+        "sha256": "8a3c375922338d6d6f7e12fe277db989dd70a8818c555085867cd0ef8cdd7202",
+        "bytes": 71.4e6,   # read 54.7 MB + write 16.8 MB
     },
     "pct_full_c64_b8h8t2048d64": {
         "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
-        "bytes": 268.7e6,   # read 201.5 MB + write 67.2 MB
+        "sha256": "8a3c375922338d6d6f7e12fe277db989dd70a8818c555085867cd0ef8cdd7202",
+        "bytes": 268.6e6,   # read 201.5 MB + write 67.1 MB
     },
     "pct_causal_c64_b1h8t16384d64": {
         "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "39256ee66e389a9d0efe9787ec557260c627adce5c5e557954ace7b15dfc39fd",
-        "bytes": 599.7e6,   # read 532.6 MB + write 67.1 MB
+        "sha256": "8a3c375922338d6d6f7e12fe277db989dd70a8818c555085867cd0ef8cdd7202",
+        "bytes": 599.8e6,   # read 532.7 MB + write 67.1 MB
     },
     # one-token step with the carried state: born_step_kernel
     "step:born_causal_bf16_b8h16t4096d64_rotary": {

@@ -37,7 +37,16 @@
 // from lane group g, which is its own register r = t, so the weights need no
 // shuffle.  Output channel tile c, row i stands for real channel (d/8) i + c, so
 // the V' slice a lane needs for one key is d/8 contiguous floats, and the output
-// rows a lane ends with are 4 (d/8) contiguous floats of its query.
+// rows a lane ends with are 4 (d/8) contiguous floats of its query.  At d = 64
+// rows i with ((i >> 2) ^ (i >> 3)) odd take the two halves of their slice in
+// the other order (channel 8 i + (c ^ 4)): each 16-byte read of a slice then
+// touches every LDS bank once, whether the hardware serves it 16 lanes over 64
+// banks or 8 lanes over 32, instead of hitting half of them twice.
+//
+// LDS banks.  Rows are padded by 4 floats (K' reads conflict-free).  A staging
+// lane writes its key row's 16-byte chunks c + 8 i, rotated by 7 chunks on odd
+// key rows, so the 16 lanes of one write, two key rows, cover all 64 banks
+// (widths 32 and 64; at 16 the writes stay two-way).
 #include "cattn_internal.h"
 
 namespace cattn {
@@ -140,10 +149,17 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     const int qrow = qt0 + j16;
     const bool live = rb >= 0 && qt0 < T;
     const bool stager = tid < NST;           // wave-uniform
+    // d = 64: value rows i with ((i >> 2) ^ (i >> 3)) odd take their slice's
+    // halves swapped; as A operand row i = j16, as output row i = 4 g + r
+    const int vsw = C::CPL == 8 ? 4 * (((j16 >> 2) ^ (j16 >> 3)) & 1) : 0;
+    const int osw = C::CPL == 8 ? 4 * ((g ^ (g >> 1)) & 1) : 0;
 
     // staging: lane t holds CPT consecutive float4 chunks of key t / LPK
     const int skey = tid / C::LPK;
-    const int schunk = (tid % C::LPK) * C::CPT;
+    const int sc = tid % C::LPK;
+    constexpr int NCH = C::KD / 4;                 // 16-byte chunks per row
+    constexpr int ROT = D >= 32 ? 7 : 0;           // odd key rows: chunk rotation
+    auto chunk_of = [&](int i) { return (sc + C::LPK * i + ROT * (skey & 1)) % NCH; };
     f32x4 kreg[C::CPT], vreg[C::CPT];
     auto load_stage = [&](int k0) {
         const int kr = k0 + skey;
@@ -151,8 +167,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
             if (kr < T) {
-                a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * (schunk + i));
-                b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * (schunk + i));
+                a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * chunk_of(i));
+                b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * chunk_of(i));
             }
             kreg[i] = a;
             vreg[i] = b;
@@ -164,8 +180,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         float *rk = vs + BN * C::ROW;
 #pragma unroll
         for (int i = 0; i < C::CPT; ++i) {
-            *reinterpret_cast<f32x4 *>(ks + skey * C::ROW + 4 * (schunk + i)) = kreg[i];
-            *reinterpret_cast<f32x4 *>(vs + skey * C::ROW + 4 * (schunk + i)) = vreg[i];
+            *reinterpret_cast<f32x4 *>(ks + skey * C::ROW + 4 * chunk_of(i)) = kreg[i];
+            *reinterpret_cast<f32x4 *>(vs + skey * C::ROW + 4 * chunk_of(i)) = vreg[i];
         }
         if (OP != OP_BORN) {
             float ss = 0.f;
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                     for (int c = 0; c < C::NC; c += 4) {
                         const f32x4 v = {oacc[c][r] * scale, oacc[c + 1][r] * scale, oacc[c + 2][r] * scale,
                                          oacc[c + 3][r] * scale};
-                        *reinterpret_cast<f32x4 *>(orow + C::CPL * r + c) = v;
+                        *reinterpret_cast<f32x4 *>(orow + C::CPL * r + (c ^ osw)) = v;
                     }
                 } else {
                     const f32x2 v = {oacc[0][r] * scale, oacc[1][r] * scale};
@@ -350,7 +366,18 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 float va[C::CPL];
-                lds_row<C::CPL>(vs + (16 * sb + 4 * g + t) * C::ROW + C::CPL * j16, va);
+                const float *vrow = vs + (16 * sb + 4 * g + t) * C::ROW + C::CPL * j16;
+                if constexpr (C::CPL == 8) {   // halves in the order of this row's channels
+                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(vrow + vsw);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(vrow + (4 ^ vsw));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        va[e] = x0[e];
+                        va[4 + e] = x1[e];
+                    }
+                } else {
+                    lds_row<C::CPL>(vrow, va);
+                }
 #pragma unroll
                 for (int c = 0; c < C::NC; ++c) oacc[c] = mfma16(va[c], w[t], oacc[c]);
             }
