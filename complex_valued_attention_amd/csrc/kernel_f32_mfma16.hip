@@ -154,7 +154,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     const int vsw = C::CPL == 8 ? 4 * (((j16 >> 2) ^ (j16 >> 3)) & 1) : 0;
     const int osw = C::CPL == 8 ? 4 * ((g ^ (g >> 1)) & 1) : 0;
 
-    // staging: lane t holds CPT consecutive float4 chunks of key t / LPK
+    // staging: thread t holds CPT 16-byte chunks of key row t / LPK, chunk
+    // (t % LPK) + LPK i rotated by 7 on odd rows (see the LDS note above)
     const int skey = tid / C::LPK;
     const int sc = tid % C::LPK;
     constexpr int NCH = C::KD / 4;                 // 16-byte chunks per row
@@ -238,7 +239,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     };
 
     // epilogue: lane (g, query j16) holds O'^T rows 4 g + r of tile c, i.e.
-    // real channel CPL (4 g + r) + c of its query: 4 CPL contiguous floats.
+    // real channel CPL (4 g + r) + (c ^ osw) of its query: 4 CPL contiguous
+    // floats.
     auto write_out = [&](int qt) {
         const int qr = qt + j16;
         float scale = 1.f;
