@@ -305,7 +305,20 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, 
 
         loads_done_barrier();   // the previous row block is done with both buffers
         issue_stage(0);
-        for (int s = 0; s < nstages; ++s) {
+        // Stages whose key blocks are full for every wave (below the row
+        // block's diagonal region, inside T) run in a loop with no mask or
+        // skip branch, so the accumulators stay in place across it; a wave past
+        // T computes on zero operands there and stores nothing.
+        const int nfull = (p.causal ? min(m0, T) : T) / BS;
+        int s = 0;
+        for (; s < nfull; ++s) {
+            loads_done_barrier();
+            if (s + 1 < nstages) issue_stage(s + 1);
+            const char *st = lds + (s & 1) * QREG * REGION;
+#pragma unroll
+            for (int sb = 0; sb < BS / 32; ++sb) key_block(st, sb, false, 31);
+        }
+        for (; s < nstages; ++s) {
             loads_done_barrier();
             if (s + 1 < nstages) issue_stage(s + 1);
             if (!wave_live) continue;
