@@ -54,6 +54,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 8;          // waves per workgroup: two row blocks of four tiles
 constexpr int NT = 64 * NW;    // threads
@@ -102,7 +103,18 @@ __device__ inline f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, int OP>
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// LAY = LAYOUT_C64: interleaved complex64 in and out.  LAY = LAYOUT_BF16: two
+// bf16 planes per operand, widened to the same interleaved fp32 rows while K
+// and V are staged and Q is loaded, and rounded back to bf16 planes on store
+// (round to nearest even); all arithmetic stays fp32.
+template <int D, int OP, int LAY>
 __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb, int nwork) {
     using C = Cfg16<D>;
     static_assert(C::CPT >= 1, "head width too small for this staging split");
@@ -126,11 +138,23 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         bh = L / nwork;
         item = L % nwork;
     }
-    const int64_t head = (int64_t)bh * T * C::KD;   // in floats
+    const int64_t head = (int64_t)bh * T * C::KD;   // in floats (complex64)
     const float *qg = reinterpret_cast<const float *>(p.q_re) + head;
     const float *kg = reinterpret_cast<const float *>(p.k_re) + head;
     const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
     float *og = reinterpret_cast<float *>(p.o_re) + head;
+    const int64_t headb = (int64_t)bh * T * D;      // in bf16 elements (planes)
+    auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + headb; };
+    const uint16_t *bq_re = plane(p.q_re), *bq_im = plane(p.q_im), *bk_re = plane(p.k_re),
+                   *bk_im = plane(p.k_im), *bv_re = plane(p.v_re), *bv_im = plane(p.v_im);
+    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + headb;
+    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + headb;
+    // complex elements 2 e, 2 e + 1 of a row as the interleaved fp32 chunk
+    auto widen2 = [&](const uint16_t *re, const uint16_t *im, int64_t el) {
+        const uint32_t r2 = *reinterpret_cast<const uint32_t *>(re + el);
+        const uint32_t i2 = *reinterpret_cast<const uint32_t *>(im + el);
+        return f32x4{bf_lo(r2), bf_lo(i2), bf_hi(r2), bf_hi(i2)};
+    };
 
     // Waves 0-3 take the four tiles of the first row block of the item, waves
     // 4-7 those of the second, at the same time: a SIMD holds one wave of each.
@@ -168,8 +192,13 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
             if (kr < T) {
-                a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * chunk_of(i));
-                b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * chunk_of(i));
+                if constexpr (LAY == LAYOUT_C64) {
+                    a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * chunk_of(i));
+                    b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * chunk_of(i));
+                } else {
+                    a = widen2(bk_re, bk_im, (int64_t)kr * D + 2 * chunk_of(i));
+                    b = widen2(bv_re, bv_im, (int64_t)kr * D + 2 * chunk_of(i));
+                }
             }
             kreg[i] = a;
             vreg[i] = b;
@@ -206,7 +235,12 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
 #pragma unroll
         for (int i = 0; i < C::KQ / 4; ++i) {
             x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (ok && qr < T) x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qr * C::KD + g * C::KQ + 4 * i);
+            if (ok && qr < T) {
+                if constexpr (LAY == LAYOUT_C64)
+                    x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qr * C::KD + g * C::KQ + 4 * i);
+                else
+                    x[i] = widen2(bq_re, bq_im, (int64_t)qr * D + g * (C::KQ / 2) + 2 * i);
+            }
         }
 #pragma unroll
         for (int i = 0; i < C::KQ / 4; ++i) {
@@ -253,6 +287,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         }
         if (qr < T) {
             float *orow = og + (int64_t)qr * C::KD + 4 * C::CPL * g;
+            // bf16 planes: real channel n is element n / 2 of the Re (n even) or Im plane
+            const int64_t brow = (int64_t)qr * D + 2 * C::CPL * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (C::CPL % 4 == 0) {
@@ -260,11 +296,23 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                     for (int c = 0; c < C::NC; c += 4) {
                         const f32x4 v = {oacc[c][r] * scale, oacc[c + 1][r] * scale, oacc[c + 2][r] * scale,
                                          oacc[c + 3][r] * scale};
-                        *reinterpret_cast<f32x4 *>(orow + C::CPL * r + (c ^ osw)) = v;
+                        const int ch = C::CPL * r + (c ^ osw);   // first of 4 channels, relative to the lane's run
+                        if constexpr (LAY == LAYOUT_C64) {
+                            *reinterpret_cast<f32x4 *>(orow + ch) = v;
+                        } else {
+                            *reinterpret_cast<uint32_t *>(ore + brow + ch / 2) = pack_bf16x2(v[0], v[2]);
+                            *reinterpret_cast<uint32_t *>(oim + brow + ch / 2) = pack_bf16x2(v[1], v[3]);
+                        }
                     }
                 } else {
                     const f32x2 v = {oacc[0][r] * scale, oacc[1][r] * scale};
-                    *reinterpret_cast<f32x2 *>(orow + C::CPL * r) = v;
+                    if constexpr (LAY == LAYOUT_C64) {
+                        *reinterpret_cast<f32x2 *>(orow + C::CPL * r) = v;
+                    } else {
+                        const uint32_t pk = pack_bf16x2(v[0], v[1]);
+                        ore[brow + r] = (uint16_t)(pk & 0xffffu);
+                        oim[brow + r] = (uint16_t)(pk >> 16);
+                    }
                 }
             }
             if (OP == OP_BORN && p.row_den && g == 0) p.row_den[(int64_t)bh * T + qr] = den;
@@ -413,10 +461,10 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     if (!helping && live_cur) write_out(qt_cur);
 }
 
-template <int D, int OP>
+template <int D, int OP, int LAY>
 hipError_t launch_cfg16(const Problem &p) {
     using C = Cfg16<D>;
-    auto kern = attn_f32_mfma16_kernel<D, OP>;
+    auto kern = attn_f32_mfma16_kernel<D, OP, LAY>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -428,25 +476,29 @@ hipError_t launch_cfg16(const Problem &p) {
     return hipGetLastError();
 }
 
+template <int D, int LAY>
+hipError_t launch_op16(const Problem &p) {
+    switch (p.op) {
+        case OP_BORN: return launch_cfg16<D, OP_BORN, LAY>(p);
+        case OP_PCT: return launch_cfg16<D, OP_PCT, LAY>(p);
+        case OP_PCT_SOFTMAX: return launch_cfg16<D, OP_PCT_SOFTMAX, LAY>(p);
+        default: return launch_cfg16<D, OP_PCT_SCREEN, LAY>(p);
+    }
+}
+
 template <int D>
 hipError_t launch_d16(const Problem &p) {
-    switch (p.op) {
-        case OP_BORN: return launch_cfg16<D, OP_BORN>(p);
-        case OP_PCT: return launch_cfg16<D, OP_PCT>(p);
-        case OP_PCT_SOFTMAX: return launch_cfg16<D, OP_PCT_SOFTMAX>(p);
-        default: return launch_cfg16<D, OP_PCT_SCREEN>(p);
-    }
+    return p.layout == LAYOUT_C64 ? launch_op16<D, LAYOUT_C64>(p) : launch_op16<D, LAYOUT_BF16>(p);
 }
 
 }  // namespace
 
+// complex64 (every operator) and bf16 planes (the PCT cells: bf16 Born has
+// its own bf16 matrix-core kernels) at widths 16, 32, 64
 bool supports_f32_mfma16(const Problem &p) {
-    return p.layout == LAYOUT_C64 && (p.d == 16 || p.d == 32 || p.d == 64);
+    return (p.d == 16 || p.d == 32 || p.d == 64) && (p.layout == LAYOUT_C64 || p.op != OP_BORN);
 }
 
-// Causal attention: mirrored pairs of 16-query tiles balance the grid at any
-// head count.  Without a mask every tile carries the same work and the 32 x 32
-// kernel (half the LDS reads per flop) is as fast.
 hipError_t launch_f32_mfma16(const Problem &p) {
     switch (p.d) {
         case 16: return launch_d16<16>(p);

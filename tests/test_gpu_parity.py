@@ -118,23 +118,25 @@ def test_parity_edge_shapes(op, layout, causal, B, H, T, d):
 # causal helpers: one block (helpers from the start), an odd block count (a
 # middle block without a partner), even counts, ragged tails, every matrix
 # width
-PAIRS = [(op, causal, T, d) for op in ("born", "pct") for T in (64, 65, 191, 256, 449, 513)
+# bf16 planes take the same kernel for the PCT cells (widened to fp32 on load)
+PAIRS = [(op, causal, T, d, "c64") for op in ("born", "pct") for T in (64, 65, 191, 256, 449, 513)
          for d in (16, 32, 64) for causal in (True,)] + \
-        [(op, False, T, d) for op in ("born", "pct") for T in (65, 191, 513) for d in (16, 64)]
+        [(op, False, T, d, "c64") for op in ("born", "pct") for T in (65, 191, 513) for d in (16, 64)] + \
+        [("pct", causal, T, d, "bf16") for causal in (True, False) for T in (65, 191, 513) for d in (16, 32, 64)]
 
 
-@pytest.mark.parametrize("op,causal,T,d", PAIRS)
-def test_c64_row_block_pairs_and_helpers(op, causal, T, d):
+@pytest.mark.parametrize("op,causal,T,d,layout", PAIRS)
+def test_row_block_pairs_and_helpers(op, causal, T, d, layout):
     import oracle
-    w = gen.Workload("pairs", op, causal, 1, 2, T, d, "c64", seed=13)
+    w = gen.Workload("pairs", op, causal, 1, 2, T, d, layout, seed=13)
     say("case", w)
     inp = gen.make_inputs(w)
     den = torch.full((2 * T,), float("nan"), dtype=torch.float32, device="cuda") if op == "born" else None
     got = run_hip(w, inp, row_den=den)
     ref = run_oracle(w, inp)
     err = rowwise_rel_err(got, ref)
-    say(f"pairs {op} causal={causal} T={T} d={d}: rowwise rel err {err:.3e}")
-    assert err <= TOL["c64"]
+    say(f"pairs {op} {layout} causal={causal} T={T} d={d}: rowwise rel err {err:.3e}")
+    assert err <= TOL[layout]
     if op == "born":   # every row's denominator is written too
         _, ref_den = oracle.born_attention(inp.q64, inp.k64, inp.v64, causal=causal, return_den=True)
         np.testing.assert_allclose(den.cpu().numpy(), ref_den.reshape(-1), rtol=1e-4)
