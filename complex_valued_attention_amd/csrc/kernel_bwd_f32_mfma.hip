@@ -1,6 +1,7 @@
-// Backward of Born and phase-coherent attention on interleaved complex64 with
-// gfx950 fp32 matrix cores (v_mfma_f32_32x32x2_f32), fp32 throughout; head
-// widths 16, 32 and 64.
+// Backward of Born and phase-coherent attention on interleaved complex64 (or
+// bf16 planes, widened to the same fp32 rows on load and rounded back on
+// store) with gfx950 fp32 matrix cores (v_mfma_f32_32x32x2_f32), fp32
+// throughout; head widths 16, 32 and 64.
 //
 // Gradients are dL/d(conj z) for a real loss L given G = dL/d(conj O)
 // ("CNet ...", section 3, the Wirtinger accumulation rule (2)).  Born ("CNet
@@ -37,6 +38,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 4;          // waves per workgroup
 constexpr int NT = 64 * NW;
@@ -86,8 +88,41 @@ __device__ inline void map_block(int BH, int nblk, bool heavy_last, int &bh, int
     blk = heavy_last ? nblk - 1 - (j % nblk) : j % nblk;
 }
 
+
+// A 16-byte chunk (4 floats: complex elements f/2, f/2 + 1) of the interleaved
+// real row `row` (counted from the start of the tensor), at float offset f.
+// LAYOUT_BF16: the two elements are read from the bf16 planes and widened, or
+// rounded to bf16 (nearest even) and written to them.
+template <int LAY, int D>
+__device__ inline f32x4 load4(const void *re, const void *im, int64_t row, int f) {
+    if constexpr (LAY == LAYOUT_C64) {
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(re) + row * (2 * D) + f);
+    } else {
+        const int64_t el = row * D + f / 2;
+        const uint32_t r2 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(re) + el);
+        const uint32_t i2 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(im) + el);
+        return f32x4{__uint_as_float(r2 << 16), __uint_as_float(i2 << 16), __uint_as_float(r2 & 0xffff0000u),
+                     __uint_as_float(i2 & 0xffff0000u)};
+    }
+}
+
+template <int LAY, int D>
+__device__ inline void store4(void *re, void *im, int64_t row, int f, f32x4 v) {
+    if constexpr (LAY == LAYOUT_C64) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(re) + row * (2 * D) + f) = v;
+    } else {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const int64_t el = row * D + f / 2;
+        const f32x2 r = {v[0], v[2]}, i = {v[1], v[3]};
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(re) + el) =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(im) + el) =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(i, bf16x2_t));
+    }
+}
+
 // ------------------------------------------------------------------------------ dQ (and db)
-template <int D, int OP>
+template <int D, int OP, int LAY>
 __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
     using C = BCfg<D>;
     extern __shared__ __align__(16) float fsm[];
@@ -102,11 +137,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
     int bh, rb;
     map_block(p.BH, nrb, true, bh, rb);
     const int m0 = rb * BM;
-    const int64_t head = (int64_t)bh * T * C::KD;
-    const float *qg = reinterpret_cast<const float *>(p.q_re) + head;
-    const float *kg = reinterpret_cast<const float *>(p.k_re) + head;
-    const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
-    const float *gg = reinterpret_cast<const float *>(p.g_re) + head;
+    const int64_t hrow = (int64_t)bh * T;   // this head's first row
 
     // Q', G' operands: lane (query l32, half h) holds x'[8 j + 4 h .. +3]
     const int qt0 = m0 + 32 * wave;
@@ -117,10 +148,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
     for (int j = 0; j < C::KCH; ++j) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, g = x, o = x;
         if (qrow < T) {
-            x = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qrow * C::KD + 8 * j + 4 * h);
-            g = *reinterpret_cast<const f32x4 *>(gg + (int64_t)qrow * C::KD + 8 * j + 4 * h);
-            if (born) o = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.o_re) + head +
-                                                            (int64_t)qrow * C::KD + 8 * j + 4 * h);
+            x = load4<LAY, D>(p.q_re, p.q_im, hrow + qrow, 8 * j + 4 * h);
+            g = load4<LAY, D>(p.g_re, p.g_im, hrow + qrow, 8 * j + 4 * h);
+            if (born) o = load4<LAY, D>(p.o_re, p.o_im, hrow + qrow, 8 * j + 4 * h);
         }
         qb[j] = x;
         gb[j] = g;
@@ -156,8 +186,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
         for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
             if (kr < T) {
-                a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * (schunk + i));
-                b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * (schunk + i));
+                a = load4<LAY, D>(p.k_re, p.k_im, hrow + kr, 4 * (schunk + i));
+                b = load4<LAY, D>(p.v_re, p.v_im, hrow + kr, 4 * (schunk + i));
             }
             kreg[i] = a;
             vreg[i] = b;
@@ -276,17 +306,16 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
         if (p.db_rows && h == 0 && qrow < T) p.db_rows[(int64_t)bh * T + qrow] = db;
     }
     if (qrow >= T) return;
-    float *dqg = reinterpret_cast<float *>(p.dq_re) + head + (int64_t)qrow * C::KD;
 #pragma unroll
     for (int c = 0; c < C::CT; ++c)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<f32x4 *>(dqg + 32 * c + 8 * g + 4 * h) =
-                f32x4{dq[c][4 * g], dq[c][4 * g + 1], dq[c][4 * g + 2], dq[c][4 * g + 3]};
+            store4<LAY, D>(p.dq_re, p.dq_im, hrow + qrow, 32 * c + 8 * g + 4 * h,
+                           f32x4{dq[c][4 * g], dq[c][4 * g + 1], dq[c][4 * g + 2], dq[c][4 * g + 3]});
 }
 
 // ------------------------------------------------------------------------------ dK, dV
-template <int D, int OP>
+template <int D, int OP, int LAY>
 __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb) {
     using C = BCfg<D>;
     extern __shared__ __align__(16) float fsm[];
@@ -301,12 +330,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
     int bh, kblk;
     map_block(p.BH, nkb, false, bh, kblk);
     const int kb0 = kblk * BM;
-    const int64_t head = (int64_t)bh * T * C::KD;
-    const float *qg = reinterpret_cast<const float *>(p.q_re) + head;
-    const float *kg = reinterpret_cast<const float *>(p.k_re) + head;
-    const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
-    const float *gg = reinterpret_cast<const float *>(p.g_re) + head;
-    const float *og = reinterpret_cast<const float *>(p.o_re) + head;
+    const int64_t hrow = (int64_t)bh * T;   // this head's first row
 
     // K' operand of this wave's 32 keys in registers (K'' for Im S is formed from it); the
     // V' operand is parked in this wave's LDS rows, each lane reading back what it wrote
@@ -319,8 +343,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
     for (int j = 0; j < C::KCH; ++j) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, v = x;
         if (krow < T) {
-            x = *reinterpret_cast<const f32x4 *>(kg + (int64_t)krow * C::KD + 8 * j + 4 * h);
-            v = *reinterpret_cast<const f32x4 *>(vg + (int64_t)krow * C::KD + 8 * j + 4 * h);
+            x = load4<LAY, D>(p.k_re, p.k_im, hrow + krow, 8 * j + 4 * h);
+            v = load4<LAY, D>(p.v_re, p.v_im, hrow + krow, 8 * j + 4 * h);
         }
         kb[j] = x;
         *reinterpret_cast<f32x4 *>(vw + 8 * j + 4 * h) = v;
@@ -347,9 +371,9 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
         for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, g = a, o = a;
             if (qr < T) {
-                a = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qr * C::KD + 4 * (schunk + i));
-                g = *reinterpret_cast<const f32x4 *>(gg + (int64_t)qr * C::KD + 4 * (schunk + i));
-                if (born) o = *reinterpret_cast<const f32x4 *>(og + (int64_t)qr * C::KD + 4 * (schunk + i));
+                a = load4<LAY, D>(p.q_re, p.q_im, hrow + qr, 4 * (schunk + i));
+                g = load4<LAY, D>(p.g_re, p.g_im, hrow + qr, 4 * (schunk + i));
+                if (born) o = load4<LAY, D>(p.o_re, p.o_im, hrow + qr, 4 * (schunk + i));
             }
             qreg[i] = a;
             greg[i] = g;
@@ -491,28 +515,26 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
             for (int r = 0; r < 16; ++r) dk[c][r] = (dk[c][r] - dot * kb[4 * c + (r >> 2)][r & 3]) * rk;
     }
     if (krow >= T) return;
-    float *dkg = reinterpret_cast<float *>(p.dk_re) + head + (int64_t)krow * C::KD;
-    float *dvg = reinterpret_cast<float *>(p.dv_re) + head + (int64_t)krow * C::KD;
 #pragma unroll
     for (int c = 0; c < C::CT; ++c)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            *reinterpret_cast<f32x4 *>(dkg + 32 * c + 8 * g + 4 * h) =
-                f32x4{dk[c][4 * g], dk[c][4 * g + 1], dk[c][4 * g + 2], dk[c][4 * g + 3]};
-            *reinterpret_cast<f32x4 *>(dvg + 32 * c + 8 * g + 4 * h) =
-                f32x4{dv[c][4 * g], dv[c][4 * g + 1], dv[c][4 * g + 2], dv[c][4 * g + 3]};
+            store4<LAY, D>(p.dk_re, p.dk_im, hrow + krow, 32 * c + 8 * g + 4 * h,
+                           f32x4{dk[c][4 * g], dk[c][4 * g + 1], dk[c][4 * g + 2], dk[c][4 * g + 3]});
+            store4<LAY, D>(p.dv_re, p.dv_im, hrow + krow, 32 * c + 8 * g + 4 * h,
+                           f32x4{dv[c][4 * g], dv[c][4 * g + 1], dv[c][4 * g + 2], dv[c][4 * g + 3]});
         }
 }
 
-template <int D, int OP>
+template <int D, int OP, int LAY>
 hipError_t launch_cfg(const BwdProblem &p) {
     using C = BCfg<D>;
     static std::atomic<uint64_t> dq_set{0}, kv_set{0};
     const int nblk = (p.T + BM - 1) / BM;
     const int64_t blocks = (int64_t)p.BH * nblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    auto kkv = bwd_dkdv_f32_kernel<D, OP>;
-    auto kdq = bwd_dq_f32_kernel<D, OP>;
+    auto kkv = bwd_dkdv_f32_kernel<D, OP, LAY>;
+    auto kdq = bwd_dq_f32_kernel<D, OP, LAY>;
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), C::LDS_BYTES_KV, kv_set);
     if (e != hipSuccess) return e;
     e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), C::LDS_BYTES, dq_set);
@@ -524,15 +546,22 @@ hipError_t launch_cfg(const BwdProblem &p) {
     return hipGetLastError();
 }
 
+template <int D, int LAY>
+hipError_t launch_op(const BwdProblem &p) {
+    return p.op == OP_BORN ? launch_cfg<D, OP_BORN, LAY>(p) : launch_cfg<D, OP_PCT, LAY>(p);
+}
+
 template <int D>
 hipError_t launch_d(const BwdProblem &p) {
-    return p.op == OP_BORN ? launch_cfg<D, OP_BORN>(p) : launch_cfg<D, OP_PCT>(p);
+    return p.layout == LAYOUT_C64 ? launch_op<D, LAYOUT_C64>(p) : launch_op<D, LAYOUT_BF16>(p);
 }
 
 }  // namespace
 
 bool supports_bwd_f32_mfma(const BwdProblem &p) {
-    return p.layout == LAYOUT_C64 && (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64);
+    // complex64, or bf16 planes widened to fp32 on load (bf16 Born at width 64
+    // has its own bf16 matrix-core pair, tried first)
+    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64);
 }
 
 hipError_t launch_bwd_f32_mfma(const BwdProblem &p) {

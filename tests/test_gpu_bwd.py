@@ -171,6 +171,13 @@ CASES = [
     ("pct", "c64", True, 2, 1, 520, 32, False),
     ("pct", "c64", False, 1, 8, 190, 64, False),
     ("pct", "c64", True, 1, 8, 300, 16, False),
+    # bf16 planes on the fp32 matrix-core pair (widened on load): PCT at widths
+    # 16/32/64 and Born at 16/32, causal and not, ragged tails, 8 heads
+    ("pct", "bf16", False, 1, 2, 300, 64, False),
+    ("pct", "bf16", True, 1, 8, 260, 32, False),
+    ("pct", "bf16", True, 2, 1, 130, 16, False),
+    ("born", "bf16", True, 1, 8, 200, 32, True),
+    ("born", "bf16", False, 1, 3, 150, 32, False),
 ]
 
 
