@@ -1,5 +1,6 @@
 // Carried-state Born attention on gfx950 fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32), interleaved complex64, head widths 16, 32, 64
+// (v_mfma_f32_32x32x2_f32), interleaved complex64 or bf16 planes (widened to
+// fp32 on load, rounded back on store), head widths 16, 32, 64
 // ("Show HN: CNET", BornAttention's linear mode: the key lifted to its outer
 // product, a running state; "The Quantum Shortcut", section 2: the Born rule
 // q^H rho q as a linear functional of rho = k k^H).
@@ -53,7 +54,31 @@ struct StateSmem {
     float W[STS][2 * D];        // Re V channels, then Im V channels
 };
 
-template <int D>
+
+// One complex element i (counted from the start of the tensor): interleaved
+// complex64, or two bf16 planes widened on load and rounded (nearest even) on
+// store; the arithmetic is fp32 either way.
+template <int LAY>
+__device__ inline float2 ld2(const void *re, const void *im, int64_t i) {
+    if constexpr (LAY == LAYOUT_C64) {
+        return reinterpret_cast<const float2 *>(re)[i];
+    } else {
+        return make_float2(__uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(re)[i] << 16),
+                           __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(im)[i] << 16));
+    }
+}
+
+template <int LAY>
+__device__ inline void st2(void *re, void *im, int64_t i, float2 v) {
+    if constexpr (LAY == LAYOUT_C64) {
+        reinterpret_cast<float2 *>(re)[i] = v;
+    } else {
+        reinterpret_cast<uint16_t *>(re)[i] = __builtin_bit_cast(uint16_t, (__bf16)v.x);
+        reinterpret_cast<uint16_t *>(im)[i] = __builtin_bit_cast(uint16_t, (__bf16)v.y);
+    }
+}
+
+template <int D, int LAY>
 __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int groups) {
     using C = LCfg<D>;
     __shared__ __align__(16) StateSmem<D> sm;
@@ -64,8 +89,6 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
     const int64_t bh = lin / groups;
     const int f0 = (lin % groups) * (32 * NW * SFT) + wave * 32 * SFT;   // this wave's first feature
     const int64_t base = bh * (int64_t)T * D;
-    const float2 *kg = reinterpret_cast<const float2 *>(p.k_re) + base;
-    const float2 *vg = reinterpret_cast<const float2 *>(p.v_re) + base;
 
     // this lane's features (a, b) and which pair table its first operand reads
     int fa[SFT], fb[SFT];
@@ -96,8 +119,8 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
             const int r = i / D, m = i % D;
             pk[j] = pv[j] = make_float2(0.f, 0.f);
             if (t0 + r < T) {
-                pk[j] = kg[(int64_t)(t0 + r) * D + m];
-                pv[j] = vg[(int64_t)(t0 + r) * D + m];
+                pk[j] = ld2<LAY>(p.k_re, p.k_im, base + (int64_t)(t0 + r) * D + m);
+                pv[j] = ld2<LAY>(p.v_re, p.v_im, base + (int64_t)(t0 + r) * D + m);
             }
         }
     };
@@ -171,7 +194,7 @@ struct MergeSmem {
     float2 Qs[32 * TG][D + 1];
 };
 
-template <int D, int TG>
+template <int D, int TG, int LAY>
 __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int ntile_t) {
     using C = LCfg<D>;
     using M = MergeSmem<D, TG>;
@@ -190,12 +213,11 @@ __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int
     const int t0 = (lin % ntile_t) * 32 * TG;
     const int64_t base = bh * (int64_t)T * D;
     const float *S = p.S + bh * (int64_t)NM * C::F;
-    const float2 *qg = reinterpret_cast<const float2 *>(p.q_re) + base;
     auto Sb = [&](int b, int n, int c) -> float & { return sm.buf[(b * NM + n) * LD + c]; };
 
     for (int i = tid; i < 32 * TG * D; i += NT) {
         const int r = i / D, m = i % D;
-        sm.Qs[r][m] = t0 + r < T ? qg[(int64_t)(t0 + r) * D + m] : make_float2(0.f, 0.f);
+        sm.Qs[r][m] = t0 + r < T ? ld2<LAY>(p.q_re, p.q_im, base + (int64_t)(t0 + r) * D + m) : make_float2(0.f, 0.f);
     }
 
     // block k: features k MBC .. k MBC + 31 of every matrix, one float4 per
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int
     const float l = p.row_den[rowi];
     const float Dn = l + den;
     const float inv = Dn != 0.f ? 1.f / Dn : 0.f;
-    float2 *og = reinterpret_cast<float2 *>(p.o_re) + base + (int64_t)tq * D;
+    const int64_t orow = base + (int64_t)tq * D;
 #pragma unroll
     for (int ti = 0; ti < C::NTI - 1; ++ti)
 #pragma unroll
@@ -305,52 +327,64 @@ __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int
             if (c >= D) continue;
             // the imaginary row d + c sits D / 32 tiles (D >= 32) or 16 rows (D = 16) further on
             const float im = D >= 32 ? acc[ti + D / 32][r] : acc[ti][r + 8];
-            const float2 o = og[c];
-            og[c] = make_float2((o.x * l + acc[ti][r]) * inv, (o.y * l + im) * inv);
+            const float2 o = ld2<LAY>(p.o_re, p.o_im, orow + c);
+            st2<LAY>(p.o_re, p.o_im, orow + c, make_float2((o.x * l + acc[ti][r]) * inv, (o.y * l + im) * inv));
         }
     if (h == 0) p.row_den[rowi] = Dn;
 }
 
-template <int D>
+template <int D, int LAY>
 hipError_t launch_state_d(const LinearProblem &p) {
     const int groups = LCfg<D>::F / (32 * NW * SFT);
     const int64_t blocks = (int64_t)p.BH * groups;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_state_f32_kernel<D>, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, groups);
+    hipLaunchKernelGGL((born_state_f32_kernel<D, LAY>), dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, groups);
     return hipGetLastError();
 }
 
-template <int D, int TG>
+template <int D, int TG, int LAY>
 hipError_t launch_merge_tg(const LinearProblem &p) {
     static std::atomic<uint64_t> lds_set{0};
     const int bytes = (int)sizeof(MergeSmem<D, TG>);
-    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(born_merge_f32_kernel<D, TG>), bytes, lds_set);
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(born_merge_f32_kernel<D, TG, LAY>), bytes, lds_set);
     if (e != hipSuccess) return e;
     const int ntile_t = (p.T + 32 * TG - 1) / (32 * TG);
     const int64_t blocks = (int64_t)p.BH * ntile_t;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((born_merge_f32_kernel<D, TG>), dim3((unsigned)blocks), dim3(NT), bytes, p.stream, p, ntile_t);
+    hipLaunchKernelGGL((born_merge_f32_kernel<D, TG, LAY>), dim3((unsigned)blocks), dim3(NT), bytes, p.stream, p, ntile_t);
     return hipGetLastError();
 }
 
 // 128-token workgroups once they alone give two per compute unit, else 32
+template <int D, int LAY>
+hipError_t launch_merge_l(const LinearProblem &p) {
+    const int64_t wide = (int64_t)p.BH * ((p.T + 127) / 128);
+    return wide >= 512 ? launch_merge_tg<D, 4, LAY>(p) : launch_merge_tg<D, 1, LAY>(p);
+}
+
 template <int D>
 hipError_t launch_merge_d(const LinearProblem &p) {
-    const int64_t wide = (int64_t)p.BH * ((p.T + 127) / 128);
-    return wide >= 512 ? launch_merge_tg<D, 4>(p) : launch_merge_tg<D, 1>(p);
+    return p.layout == LAYOUT_C64 ? launch_merge_l<D, LAYOUT_C64>(p) : launch_merge_l<D, LAYOUT_BF16>(p);
+}
+
+template <int D>
+hipError_t launch_state_l(const LinearProblem &p) {
+    return p.layout == LAYOUT_C64 ? launch_state_d<D, LAYOUT_C64>(p) : launch_state_d<D, LAYOUT_BF16>(p);
 }
 
 }  // namespace
 
+// complex64 at widths 16/32/64, and bf16 planes at 16/32 (bf16 at 64 has its
+// own bf16 matrix-core kernels, tried first)
 bool supports_born_linear_f32(const LinearProblem &p) {
-    return p.layout == LAYOUT_C64 && (p.d == 16 || p.d == 32 || p.d == 64);
+    return p.d == 16 || p.d == 32 || p.d == 64;
 }
 
 hipError_t launch_born_state_f32(const LinearProblem &p) {
     switch (p.d) {
-        case 16: return launch_state_d<16>(p);
-        case 32: return launch_state_d<32>(p);
-        default: return launch_state_d<64>(p);
+        case 16: return launch_state_l<16>(p);
+        case 32: return launch_state_l<32>(p);
+        default: return launch_state_l<64>(p);
     }
 }
 

@@ -70,6 +70,9 @@ STATE_CASES = [
     ("c64", 2, 3, 333, 64),
     ("c64", 1, 2, 100, 32),
     ("c64", 3, 1, 45, 16),
+    # bf16 planes at widths 16/32 take the fp32 matrix-core kernels (widened on load)
+    ("bf16", 2, 3, 333, 32),
+    ("bf16", 1, 2, 100, 16),
 ]
 
 
@@ -114,6 +117,8 @@ CARRY_CASES = [
     ("c64", 2, 3, 700, 300, 64, 0.0),
     ("c64", 1, 2, 333, 100, 32, 0.25),
     ("c64", 2, 2, 150, 17, 16, 0.0),
+    ("bf16", 1, 2, 333, 100, 32, 0.25),
+    ("bf16", 2, 2, 150, 17, 16, 0.0),
 ]
 
 
