@@ -479,7 +479,9 @@ hipError_t launch_cfg16(const Problem &p) {
 template <int D, int LAY>
 hipError_t launch_op16(const Problem &p) {
     switch (p.op) {
-        case OP_BORN: return launch_cfg16<D, OP_BORN, LAY>(p);
+        case OP_BORN:   // bf16 Born runs on the bf16 matrix-core kernels
+            if constexpr (LAY == LAYOUT_C64) return launch_cfg16<D, OP_BORN, LAY>(p);
+            return hipErrorNotSupported;
         case OP_PCT: return launch_cfg16<D, OP_PCT, LAY>(p);
         case OP_PCT_SOFTMAX: return launch_cfg16<D, OP_PCT_SOFTMAX, LAY>(p);
         default: return launch_cfg16<D, OP_PCT_SCREEN, LAY>(p);

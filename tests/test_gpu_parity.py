@@ -81,6 +81,22 @@ def test_parity_full_size_sampled(name):
     assert err <= TOL[w.layout]
 
 
+@pytest.mark.parametrize("name", ["pct_full_c64_b8h8t2048d64", "pct_causal_c64_b1h8t16384d64"])
+def test_pct_bf16_planes_full_size_sampled(name):
+    # the PCT workloads' shapes on bf16 planes (the fp32 matrix-core kernel, widened on load)
+    import oracle
+    w = dataclasses.replace(gen.WORKLOADS[name], layout="bf16")
+    say("case full bf16", w)
+    inp = gen.make_inputs(w)
+    got = run_hip(w, inp)
+    assert np.isfinite(got).all()
+    rows = sample_rows(w.B, w.H, w.T, 96, seed=w.seed)
+    ref = oracle.pct_attention_rows(inp.q64, inp.k64, inp.v64, rows, causal=w.causal)
+    err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
+    say(f"{name} on bf16 planes, {len(rows)} sampled rows: rowwise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 EDGE = [
     # (op, layout, causal, B, H, T, d)
     ("born", "c64", True, 1, 1, 1, 64),
