@@ -31,3 +31,13 @@ def test_state_buffer_shape():
     from complex_valued_attention_amd import cattn
     S = cattn.born_state_buffer(2, 3, 5, device="cpu")
     assert S.dtype == torch.float32 and tuple(S.shape) == (2, 3, 11, 5, 5) and not S.any()
+
+
+def test_measured_traffic_entries_match_their_sources():
+    # a measured-traffic entry is reported only while its kernel source is the
+    # one the counters were taken on; every entry in the table must be current
+    import hashlib
+    import bench
+    for name, m in bench.MEASURED_TRAFFIC.items():
+        with open(os.path.join(bench.ROOT, m["source"]), "rb") as f:
+            assert hashlib.sha256(f.read()).hexdigest() == m["sha256"], name
