@@ -67,7 +67,8 @@ __device__ inline float swap_adj(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
 }
 
-__device__ inline float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+// hardware reciprocal (1 ulp), not the IEEE division sequence
+__device__ inline float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // Workgroup -> (head, owned block).  The blocks of a head go to one XCD when
 // BH % 8 == 0 (workgroups are dealt to the 8 XCDs in turn).  `heavy_last`

@@ -394,7 +394,8 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                 for (int r = 0; r < 4; ++r) {
                     const float x = sr[r] * rq * rkv[r];   // sqrt(d_h) Re<qh, kh>
                     if (OP == OP_PCT) {
-                        w[r] = 1.f / (1.f + __expf(-(x + p.bias)));
+                        // hardware reciprocal (1 ulp), not the IEEE division sequence
+                        w[r] = __builtin_amdgcn_rcpf(1.f + __expf(-(x + p.bias)));
                     } else if (OP == OP_PCT_SOFTMAX) {
                         w[r] = __expf(x);   // |x| <= sqrt(d_h): no shift needed
                     } else {
