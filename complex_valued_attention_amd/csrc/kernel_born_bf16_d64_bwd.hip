@@ -422,74 +422,141 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 #pragma unroll
         for (int c = 0; c < 4; ++c) dk[c] = dv[c] = f32x16{};
 
-        auto query_block = [&](const char *st, const float *sc_inv2, const float *sc_dinv2, int sb, bool masked,
-                               int lo, int hi) {
-            f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
+        // The work of one 32-query block sb, in steps that a full stage
+        // interleaves across its two blocks.
+        // S^T and E = Re(G V^H)^T, contraction step kk (three products)
+        auto score_step = [&](const char *st, int sb, int kk, f32x16 &sr, f32x16 &si, f32x16 &e) {
+            const int o = (kk >> 2) * REGION + sb * 32 * ROWB + off.koff[kk & 3];
+            const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(st + o);
+            sr = mfma(aq, kb[kk], sr);
+            si = mfma(aq, kk < 4 ? kni[kk] : kb[kk - 4], si);
+            const bf16x8 ag = *reinterpret_cast<const bf16x8 *>(st + 2 * REGION + o);
+            e = mfma(ag, vb[kk], e);
+        };
+        // weights of register group g: register r of lane half h is query
+        // 8 (r/4) + 4 h + r % 4 of the block
+        auto weight_group = [&](const float *sc_inv2, const float *sc_dinv2, int sb, int g, bool masked, int lo,
+                                int hi, const f32x16 &sr, const f32x16 &si, const f32x16 &e, uint32_t (&aw)[8],
+                                uint32_t (&pr)[8], uint32_t (&pi)[8]) {
+            const f32x4 i2 = *reinterpret_cast<const f32x4 *>(sc_inv2 + 32 * sb + 8 * g + 4 * h);
+            const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv2 + 32 * sb + 8 * g + 4 * h);
+            float a[4], d2[4];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int o = (kk >> 2) * REGION + sb * 32 * ROWB + off.koff[kk & 3];
-                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(st + o);
-                sr = mfma(aq, kb[kk], sr);
-                si = mfma(aq, kk < 4 ? kni[kk] : kb[kk - 4], si);
-                const bf16x8 ag = *reinterpret_cast<const bf16x8 *>(st + 2 * REGION + o);
-                e = mfma(ag, vb[kk], e);
-            }
-            // register r of lane half h is query 8 (r/4) + 4 h + r % 4 of the block
-            uint32_t aw[8], pr[8], pi[8];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 i2 = *reinterpret_cast<const f32x4 *>(sc_inv2 + 32 * sb + 8 * g + 4 * h);
-                const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv2 + 32 * sb + 8 * g + 4 * h);
-                float a[4], d2[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int r = 4 * g + c;
-                    a[c] = 0.5f * i2[c] * (sr[r] * sr[r] + si[r] * si[r]);
-                    d2[c] = e[r] * i2[c] - di[c];
-                    if (masked) {
-                        const int qi = 8 * g + 4 * h + c;
-                        const bool ok = qi >= lo && qi <= hi;
-                        a[c] = ok ? a[c] : 0.f;
-                        d2[c] = ok ? d2[c] : 0.f;
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < 4; c += 2) {
-                    const int r = 4 * g + c;
-                    aw[r >> 1] = pack_bf16x2(a[c], a[c + 1]);
-                    pr[r >> 1] = pack_bf16x2(d2[c] * sr[r], d2[c + 1] * sr[r + 1]);
-                    pi[r >> 1] = pack_bf16x2(d2[c] * si[r], d2[c + 1] * si[r + 1]);
+            for (int c = 0; c < 4; ++c) {
+                const int r = 4 * g + c;
+                a[c] = 0.5f * i2[c] * (sr[r] * sr[r] + si[r] * si[r]);
+                d2[c] = e[r] * i2[c] - di[c];
+                if (masked) {
+                    const int qi = 8 * g + 4 * h + c;
+                    const bool ok = qi >= lo && qi <= hi;
+                    a[c] = ok ? a[c] : 0.f;
+                    d2[c] = ok ? d2[c] : 0.f;
                 }
             }
+#pragma unroll
+            for (int c = 0; c < 4; c += 2) {
+                const int r = 4 * g + c;
+                aw[r >> 1] = pack_bf16x2(a[c], a[c + 1]);
+                pr[r >> 1] = pack_bf16x2(d2[c] * sr[r], d2[c + 1] * sr[r + 1]);
+                pi[r >> 1] = pack_bf16x2(d2[c] * si[r], d2[c + 1] * si[r + 1]);
+            }
+        };
+        // the packed weights as B operands: w/l, Re P, Im P, -Im P
+        struct GradOps {
             bf16x8 ab[2], prb[2], pib[2], pnb[2];
+        };
+        auto grad_ops = [&](const uint32_t (&aw)[8], const uint32_t (&pr)[8], const uint32_t (&pi)[8]) {
+            GradOps o;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const u32x4 w4 = {aw[4 * m], aw[4 * m + 1], aw[4 * m + 2], aw[4 * m + 3]};
                 const u32x4 a4 = {pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3]};
                 const u32x4 b4 = {pi[4 * m], pi[4 * m + 1], pi[4 * m + 2], pi[4 * m + 3]};
-                ab[m] = as_bf16x8(w4);
-                prb[m] = as_bf16x8(a4);
-                pib[m] = as_bf16x8(b4);
-                pnb[m] = as_bf16x8(b4 ^ 0x80008000u);
+                o.ab[m] = as_bf16x8(w4);
+                o.prb[m] = as_bf16x8(a4);
+                o.pib[m] = as_bf16x8(b4);
+                o.pnb[m] = as_bf16x8(b4 ^ 0x80008000u);
             }
-            // dV^T += G'^T (w/l);  dK^T: Re += Q_r P_r + Q_i P_i,  Im += Q_i P_r - Q_r P_i
+            return o;
+        };
+        // gradient products of step j (query half m = j / 2, channel tile ct = j % 2):
+        // dV^T += G'^T (w/l);  dK^T: Re += Q_r P_r + Q_i P_i,  Im += Q_i P_r - Q_r P_i
+        auto grad_step = [&](const char *st, int sb, int j, const GradOps &w) {
+            const int m = j >> 1, ct = j & 1;
+            const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
+            const bf16x8 grt = tr_operand(st + 6 * REGION + o);
+            const bf16x8 git = tr_operand(st + 7 * REGION + o);
+            dv[ct] = mfma(grt, w.ab[m], dv[ct]);
+            dv[2 + ct] = mfma(git, w.ab[m], dv[2 + ct]);
+            const bf16x8 qrt = tr_operand(st + 4 * REGION + o);
+            const bf16x8 qit = tr_operand(st + 5 * REGION + o);
+            dk[ct] = mfma(qrt, w.prb[m], dk[ct]);
+            dk[ct] = mfma(qit, w.pib[m], dk[ct]);
+            dk[2 + ct] = mfma(qit, w.prb[m], dk[2 + ct]);
+            dk[2 + ct] = mfma(qrt, w.pnb[m], dk[2 + ct]);
+        };
+        auto query_block = [&](const char *st, const float *sc_inv2, const float *sc_dinv2, int sb, bool masked,
+                               int lo, int hi) {
+            f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int kk = 0; kk < 8; ++kk) score_step(st, sb, kk, sr, si, e);
+            uint32_t aw[8], pr[8], pi[8];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
-                    const bf16x8 grt = tr_operand(st + 6 * REGION + o);
-                    const bf16x8 git = tr_operand(st + 7 * REGION + o);
-                    dv[ct] = mfma(grt, ab[m], dv[ct]);
-                    dv[2 + ct] = mfma(git, ab[m], dv[2 + ct]);
-                    const bf16x8 qrt = tr_operand(st + 4 * REGION + o);
-                    const bf16x8 qit = tr_operand(st + 5 * REGION + o);
-                    dk[ct] = mfma(qrt, prb[m], dk[ct]);
-                    dk[ct] = mfma(qit, pib[m], dk[ct]);
-                    dk[2 + ct] = mfma(qit, prb[m], dk[2 + ct]);
-                    dk[2 + ct] = mfma(qrt, pnb[m], dk[2 + ct]);
+            for (int g = 0; g < 4; ++g) weight_group(sc_inv2, sc_dinv2, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi);
+            const GradOps w = grad_ops(aw, pr, pi);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) grad_step(st, sb, j, w);
+        };
+        // both blocks of a stage with no mask: block 1's score products run
+        // beside block 0's weight arithmetic, and block 0's gradient products
+        // beside block 1's weight arithmetic
+        auto full_stage = [&](const char *st, const float *sc_inv2, const float *sc_dinv2) {
+            f32x16 sr0 = f32x16{}, si0 = f32x16{}, e0 = f32x16{};
+            f32x16 sr1 = f32x16{}, si1 = f32x16{}, e1 = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) score_step(st, 0, kk, sr0, si0, e0);
+            uint32_t aw0[8], pr0[8], pi0[8], aw1[8], pr1[8], pi1[8];
+            // Issue is in order: a run of products holds the vector
+            // instructions behind it. The scheduling groups below ask for the
+            // two streams to alternate, one product then four vector
+            // instructions, with each step's LDS reads ahead of its products
+            // (the scheduler follows the pattern only in part).
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                score_step(st, 1, 2 * g, sr1, si1, e1);
+                score_step(st, 1, 2 * g + 1, sr1, si1, e1);
+                weight_group(sc_inv2, sc_dinv2, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0);
+            }
+            const GradOps w0 = grad_ops(aw0, pr0, pi0);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // product
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // vector ALU
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                grad_step(st, 0, j, w0);
+                weight_group(sc_inv2, sc_dinv2, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1);
+            }
+            const GradOps w1 = grad_ops(aw1, pr1, pi1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) grad_step(st, 1, j, w1);
         };
 
         const int qs = p.causal ? k0 : 0;   // earlier queries see none of these keys
@@ -507,7 +574,9 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             scal_load(qs);
             scal_store(qs, 0);
         }
-        for (int s = 0; s < nstages; ++s) {
+        // One stage: wait for it, issue the next one, run its two query blocks.
+        // ALL_FULL drops the mask and skip branches (see below).
+        auto stage = [&](int s, bool all_full) {
             loads_done_barrier();   // stage s and its scalars are visible
             const bool next = s + 1 < nstages;
             if (next) {
@@ -516,8 +585,10 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             }
             const char *st = lds + (s & 1) * KREG * REGION;
             const float *si2 = scal[s & 1][0], *sdi = scal[s & 1][1];
+            if (all_full) full_stage(st, si2, sdi);
 #pragma unroll
             for (int sb = 0; sb < BS / 32; ++sb) {
+                if (all_full) continue;
                 const int qb0 = qs + s * BS + 32 * sb;
                 const bool skip = qb0 >= T || kw0 >= T || (p.causal && qb0 + 31 < kw0);
                 const bool full = (!p.causal || qb0 >= kw0 + 31) && qb0 + 32 <= T && kw0 + 32 <= T;
@@ -530,7 +601,18 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
                 }
             }
             if (next) scal_store(qs + (s + 1) * BS, (s + 1) & 1);
-        }
+        };
+        // Stages [s_lo, s_hi) hold only queries inside T that see every key of
+        // the tile (causal: at least BT - 1 past its first key), so they run in
+        // a loop with no mask or skip branch and the accumulators stay in
+        // place. A lane whose key is past T has zero K' and V' there, so its
+        // sums stay zero, and it stores nothing.
+        const int s_lo = min(p.causal ? (BT - 1 + BS - 1) / BS : 0, nstages);
+        const int s_hi = max(s_lo, nstages > 0 ? (T - qs) / BS : 0);
+        int s = 0;
+        for (; s < s_lo; ++s) stage(s, false);
+        for (; s < s_hi; ++s) stage(s, true);
+        for (; s < nstages; ++s) stage(s, false);
         if (key < T) {
             store_rows(reinterpret_cast<uint16_t *>(p.dk_re) + head, reinterpret_cast<uint16_t *>(p.dk_im) + head,
                        key, h, dk);
