@@ -26,7 +26,7 @@
 //    wave's Q' and G' in registers) and streams K and V.  Per 32-key block:
 //    S^T and E^T (keys x queries), P^T, then dQ^T += K^T P^T.
 //  * dK/dV kernel: a workgroup owns 128 keys (K' and V' in registers) and
-//    streams Q and G with the per-query 2/l and 2 delta/l.  Per 32-query
+//    streams Q and G with the per-query 1/l and delta/l.  Per 32-query
 //    block: S and E (queries x keys), w/l and P, then dV^T += G^T (w/l) and
 //    dK^T += Q^T P.
 // Causal work is balanced by mirrored pairs of tiles, as in the forward.
@@ -344,7 +344,7 @@ constexpr int KREG = 8;   // Q re, Q im, G re, G im (row-major), the same four (
 
 __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p, int nkt, int nwork) {
     __shared__ __align__(16) char lds[2 * KREG * REGION];
-    __shared__ __align__(16) float scal[2][2][BS];   // [buffer][2/l, 2 delta/l][query of the stage]
+    __shared__ __align__(16) float scal[2][2][BS];   // [buffer][1/l, delta/l][query of the stage]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -388,13 +388,13 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         dl += __shfl_xor(dl, 2);
         if (sp == 0) {
             const int q = q0 + sq;
-            float inv2 = 0.f;
+            float inv = 0.f;
             if (q < T) {
                 const float l = p.row_den[(int64_t)bh * T + q];
-                inv2 = l != 0.f ? 2.f / l : 0.f;
+                inv = l != 0.f ? 1.f / l : 0.f;
             }
-            scal[buf][0][sq] = inv2;
-            scal[buf][1][sq] = dl * inv2;
+            scal[buf][0][sq] = inv;
+            scal[buf][1][sq] = dl * inv;
         }
     };
 
@@ -435,17 +435,18 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         };
         // weights of register group g: register r of lane half h is query
         // 8 (r/4) + 4 h + r % 4 of the block
-        auto weight_group = [&](const float *sc_inv2, const float *sc_dinv2, int sb, int g, bool masked, int lo,
+        auto weight_group = [&](const float *sc_inv, const float *sc_dinv, int sb, int g, bool masked, int lo,
                                 int hi, const f32x16 &sr, const f32x16 &si, const f32x16 &e, uint32_t (&aw)[8],
                                 uint32_t (&pr)[8], uint32_t (&pi)[8]) {
-            const f32x4 i2 = *reinterpret_cast<const f32x4 *>(sc_inv2 + 32 * sb + 8 * g + 4 * h);
-            const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv2 + 32 * sb + 8 * g + 4 * h);
+            const f32x4 iv = *reinterpret_cast<const f32x4 *>(sc_inv + 32 * sb + 8 * g + 4 * h);
+            const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv + 32 * sb + 8 * g + 4 * h);
             float a[4], d2[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int r = 4 * g + c;
-                a[c] = 0.5f * i2[c] * (sr[r] * sr[r] + si[r] * si[r]);
-                d2[c] = e[r] * i2[c] - di[c];
+                // w/l, and half of dL/ds (2 (e - delta)/l); dK is doubled on store
+                a[c] = iv[c] * (sr[r] * sr[r] + si[r] * si[r]);
+                d2[c] = e[r] * iv[c] - di[c];
                 if (masked) {
                     const int qi = 8 * g + 4 * h + c;
                     const bool ok = qi >= lo && qi <= hi;
@@ -495,14 +496,14 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             dk[2 + ct] = mfma(qit, w.prb[m], dk[2 + ct]);
             dk[2 + ct] = mfma(qrt, w.pnb[m], dk[2 + ct]);
         };
-        auto query_block = [&](const char *st, const float *sc_inv2, const float *sc_dinv2, int sb, bool masked,
+        auto query_block = [&](const char *st, const float *sc_inv, const float *sc_dinv, int sb, bool masked,
                                int lo, int hi) {
             f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) score_step(st, sb, kk, sr, si, e);
             uint32_t aw[8], pr[8], pi[8];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) weight_group(sc_inv2, sc_dinv2, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi);
+            for (int g = 0; g < 4; ++g) weight_group(sc_inv, sc_dinv, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi);
             const GradOps w = grad_ops(aw, pr, pi);
 #pragma unroll
             for (int j = 0; j < 4; ++j) grad_step(st, sb, j, w);
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         // both blocks of a stage with no mask: block 1's score products run
         // beside block 0's weight arithmetic, and block 0's gradient products
         // beside block 1's weight arithmetic
-        auto full_stage = [&](const char *st, const float *sc_inv2, const float *sc_dinv2) {
+        auto full_stage = [&](const char *st, const float *sc_inv, const float *sc_dinv) {
             f32x16 sr0 = f32x16{}, si0 = f32x16{}, e0 = f32x16{};
             f32x16 sr1 = f32x16{}, si1 = f32x16{}, e1 = f32x16{};
 #pragma unroll
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             for (int g = 0; g < 4; ++g) {
                 score_step(st, 1, 2 * g, sr1, si1, e1);
                 score_step(st, 1, 2 * g + 1, sr1, si1, e1);
-                weight_group(sc_inv2, sc_dinv2, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0);
+                weight_group(sc_inv, sc_dinv, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0);
             }
             const GradOps w0 = grad_ops(aw0, pr0, pi0);
 #pragma unroll
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 grad_step(st, 0, j, w0);
-                weight_group(sc_inv2, sc_dinv2, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1);
+                weight_group(sc_inv, sc_dinv, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1);
             }
             const GradOps w1 = grad_ops(aw1, pr1, pi1);
 #pragma unroll
@@ -614,6 +615,8 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         for (; s < s_hi; ++s) stage(s, true);
         for (; s < nstages; ++s) stage(s, false);
         if (key < T) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dk[c] *= 2.f;   // the weights carried half of dL/ds
             store_rows(reinterpret_cast<uint16_t *>(p.dk_re) + head, reinterpret_cast<uint16_t *>(p.dk_im) + head,
                        key, h, dk);
             store_rows(reinterpret_cast<uint16_t *>(p.dv_re) + head, reinterpret_cast<uint16_t *>(p.dv_im) + head,
