@@ -157,6 +157,10 @@ CASES = [
     ("born", "bf16", True, 2, 4, 129, 64, True),
     ("born", "bf16", True, 1, 8, 520, 64, False),
     ("born", "bf16", False, 1, 1, 127, 64, False),
+    # tile multiples: the key-side kernel runs every stage (non-causal) or every
+    # stage past the diagonal (causal) in its branch-free loop
+    ("born", "bf16", False, 1, 2, 256, 64, True),
+    ("born", "bf16", True, 1, 2, 384, 64, True),
     ("pct", "c64", True, 1, 2, 300, 64, False),
     ("pct", "c64", False, 1, 2, 65, 16, False),
     ("pct", "c64", True, 1, 1, 100, 17, False),
