@@ -25,7 +25,7 @@ def rowwise_rel_err(got: np.ndarray, ref: np.ndarray, floor: float = 0.0) -> flo
     ``floor`` > 0 raises each row's scale to at least ``floor`` times the
     largest row scale of the tensor.  Gradients use it: some of their rows are
     exactly zero in exact arithmetic (Born's first causal row of dQ), and those
-    are judged on their absolute error at the tensor's scale.
+    are measured by their absolute error at the tensor's scale.
     """
     got = np.asarray(got, dtype=np.complex128).reshape(-1, ref.shape[-1])
     ref = np.asarray(ref, dtype=np.complex128).reshape(-1, ref.shape[-1])

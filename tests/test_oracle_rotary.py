@@ -3,7 +3,8 @@ position 0, step-mode consistency (a token rotated alone at its absolute
 position), additive composition for one token, channel 0 turns by exactly one
 radian per position, a hand-worked value, and the property that makes it a
 relative position code for Born attention -- shifting every position by the
-same amount leaves |<R q_t, R k_j>|^2 unchanged."""
+same amount leaves |<R q_t, R k_j>|^2 unchanged (*Show HN: CNET*, the
+RotaryEmbed layer: position enters as a phase rotation)."""
 import math
 
 import numpy as np
