@@ -69,3 +69,36 @@ def test_every_pair_once_every_tile_written_once(causal):
                 need = kb <= qt if causal else True
                 assert done[(qt, kb)] == int(need), (T, qt, kb, done[(qt, kb)])
         assert all(q < T and k < T for q, k in done), T
+
+
+# ---------------------------------------------------------------------------
+# The bf16 width-64 backward's key-side kernel: a workgroup owns 128 keys (32
+# per wave) and streams 64-query stages.  Stages [s_lo, s_hi) run with no mask
+# or skip branch; the replay checks that every such stage holds only queries
+# inside T that every key of the tile may see, and that the general stages
+# before and after it cover the rest of the stream.
+BT_KEYS, BS_QUERIES = 128, 64
+
+
+def key_tile_stages(T: int, causal: bool, kt: int):
+    k0 = kt * BT_KEYS
+    qs = k0 if causal else 0
+    nstages = (T - qs + BS_QUERIES - 1) // BS_QUERIES if qs < T else 0
+    s_lo = min((BT_KEYS - 1 + BS_QUERIES - 1) // BS_QUERIES if causal else 0, nstages)
+    s_hi = max(s_lo, (T - qs) // BS_QUERIES if nstages > 0 else 0)
+    return k0, qs, nstages, s_lo, s_hi
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_key_tile_branch_free_stages(causal):
+    for T in list(range(1, 700)) + [4095, 4096, 4097, 16384]:
+        for kt in range((T + BT_KEYS - 1) // BT_KEYS):
+            k0, qs, nstages, s_lo, s_hi = key_tile_stages(T, causal, kt)
+            assert 0 <= s_lo <= s_hi <= nstages, (T, kt)
+            # every query the stream must visit: causal, those at or after the tile's first key
+            assert qs + nstages * BS_QUERIES >= T and (nstages == 0 or qs + (nstages - 1) * BS_QUERIES < T)
+            for s in range(s_lo, s_hi):
+                q_first, q_last = qs + s * BS_QUERIES, qs + s * BS_QUERIES + BS_QUERIES - 1
+                assert q_last < T, (T, kt, s)   # staged rows are real queries, not clamped copies
+                if causal:
+                    assert q_first >= k0 + BT_KEYS - 1, (T, kt, s)   # past every key of the tile
