@@ -22,7 +22,7 @@
 // each lane's 16 accumulator values are directly the bf16 B operand of the
 // next product (no shuffles).
 //
-//  * dQ kernel: a workgroup of 4 waves owns 128 queries (32 per wave, the
+//  * dQ kernel: a workgroup of 8 waves owns 256 queries (32 per wave, the
 //    wave's Q' and G' in registers) and streams K and V.  Per 32-key block:
 //    S^T and E^T (keys x queries), P^T, then dQ^T += K^T P^T.
 //  * dK/dV kernel: a workgroup owns 128 keys (K' and V' in registers) and
@@ -53,8 +53,6 @@ constexpr int BT = 32 * NW;             // rows owned by a workgroup (queries or
 constexpr int BS = 64;                  // streamed rows per LDS stage
 constexpr int ROWB = 2 * D;             // bytes per row of one plane
 constexpr int REGION = BS * ROWB;       // 8 KiB
-constexpr int CPT = REGION / 16 / NT;   // 16-byte chunks per thread per region
-static_assert(CPT * 16 * NT == REGION, "staging split");
 
 __device__ inline int swz_k(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
@@ -102,15 +100,19 @@ __device__ inline void loads_done_barrier() {
 
 // Rows r0 .. r0 + 63 of one plane into one LDS region, chunk c of row r at
 // slot c ^ swz(r).  Rows past T repeat row T - 1 (they are masked later).
+// NTH threads of the workgroup share the copy.
+template <int NTH>
 __device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, bool vswz, int tid,
                                     int wave) {
+    constexpr int C = REGION / 16 / NTH;   // 16-byte chunks per thread
+    static_assert(C * 16 * NTH == REGION, "staging split");
     const int slot = tid & 7;
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-        const int row = (tid >> 3) + (NT / 8) * e;
+    for (int e = 0; e < C; ++e) {
+        const int row = (tid >> 3) + (NTH / 8) * e;
         const int lc = slot ^ (vswz ? swz_v(row) : swz_k(row));
         const int g = min(r0 + row, T - 1);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NT * 16 + wave * 1024));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NTH * 16 + wave * 1024));
         dma16(dst, plane, (uint32_t)(g * ROWB + 16 * lc));
     }
 }
@@ -184,8 +186,13 @@ __device__ inline void work_item(const BwdProblem &p, int nwork, int &bh, int &i
 
 // ---------------------------------------------------------------------------- dQ
 constexpr int QREG = 6;   // K re, K im, V re, V im (row-major swizzle), K re, K im (transposing swizzle)
+// The dQ kernel runs 8 waves (two per SIMD) over 256 queries: every staged
+// K/V stage feeds twice the queries, and one wave's waits are filled by the other.
+constexpr int QNW = 8;
+constexpr int QNT = 64 * QNW;
+constexpr int QBT = 32 * QNW;
 
-__global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
+__global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
     __shared__ __align__(16) char lds[2 * QREG * REGION];
 
     const int tid = threadIdx.x;
@@ -208,13 +215,13 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, 
         const uint32_t base = lds0 + (uint32_t)((s & 1) * QREG * REGION);
 #pragma unroll
         for (int r = 0; r < QREG; ++r)
-            stage_region(base + r * REGION, stage_planes[r], s * BS, T, r >= 4, tid, wave);
+            stage_region<QNT>(base + r * REGION, stage_planes[r], s * BS, T, r >= 4, tid, wave);
     };
 
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
     for (int blk = 0; blk < nblocks; ++blk) {
         const int rb = p.causal ? (blk == 0 ? nrb - 1 - item : item) : item;
-        const int m0 = rb * BT;
+        const int m0 = rb * QBT;
         const int qt0 = m0 + 32 * wave;
         const int q = qt0 + l32;
 
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, 
             }
         };
 
-        const int kend = p.causal ? min(T, m0 + BT) : T;
+        const int kend = p.causal ? min(T, m0 + QBT) : T;
         const int nstages = (kend + BS - 1) / BS;
         const bool wave_live = qt0 < T;
 
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             const uint32_t base = lds0 + (uint32_t)((s & 1) * KREG * REGION);
 #pragma unroll
             for (int r = 0; r < KREG; ++r)
-                stage_region(base + r * REGION, stage_planes[r], qs + s * BS, T, r >= 4, tid, wave);
+                stage_region<NT>(base + r * REGION, stage_planes[r], qs + s * BS, T, r >= 4, tid, wave);
         };
 
         loads_done_barrier();   // the previous key tile is done with both buffers
@@ -632,11 +639,11 @@ bool supports_born_bf16_d64_bwd(const BwdProblem &p) {
 }
 
 hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {
-    const int nrb = (p.T + BT - 1) / BT;
+    const int nrb = (p.T + QBT - 1) / QBT;
     const int nwork = p.causal ? (nrb + 1) / 2 : nrb;
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_bf16_d64_bwd_dq_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nrb, nwork);
+    hipLaunchKernelGGL(born_bf16_d64_bwd_dq_kernel, dim3((unsigned)blocks), dim3(QNT), 0, p.stream, p, nrb, nwork);
     return hipGetLastError();
 }
 
