@@ -42,26 +42,6 @@ PEAK_HBM_GBS = 8000.0
 # --copy-probe kernel.  Valid only for the kernel source it was measured on:
 # any other source gives traffic = null.
 MEASURED_TRAFFIC = {
-    "born_causal_bf16_b8h16t4096d64_rotary": {
-        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_d64.hip",
-        "sha256": "1ea06ab789c9db176c51489e8839f1ee6cad3e1863445d4fac4248dcb78e7f02",
-        "bytes": 882.4e6,   # read 748.1 MB + write 134.2 MB
-    },
-    "born_causal_c64_b4h8t1024d64_rotary": {
-        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "2d491cd756c15574d9ece914f4819974a32d198f67c4f6c25c61917c7bdaad03",
-        "bytes": 71.4e6,   # read 54.7 MB + write 16.8 MB
-    },
-    "pct_full_c64_b8h8t2048d64": {
-        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "2d491cd756c15574d9ece914f4819974a32d198f67c4f6c25c61917c7bdaad03",
-        "bytes": 268.6e6,   # read 201.5 MB + write 67.1 MB
-    },
-    "pct_causal_c64_b1h8t16384d64": {
-        "source": "complex_valued_attention_amd/csrc/kernel_f32_mfma16.hip",
-        "sha256": "2d491cd756c15574d9ece914f4819974a32d198f67c4f6c25c61917c7bdaad03",
-        "bytes": 599.5e6,   # read 532.4 MB + write 67.1 MB
-    },
     # one-token step with the carried state: born_step_kernel
     "step:born_causal_bf16_b8h16t4096d64_rotary": {
         "source": "complex_valued_attention_amd/csrc/kernel_born_linear.hip",

@@ -17,21 +17,64 @@ struct Span {
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+// Resolves one operand's strides (0 -> dense) and its extent in elements
+// (largest element offset + 1).  False if a stride is negative or the extent
+// overflows.
+bool resolve_strides(const cattn_stride *in, int64_t B, int64_t H, int64_t T, int64_t d, cattn::Str3 *out,
+                     int64_t *extent) {
+    cattn::Str3 s{in ? in->b : 0, in ? in->h : 0, in ? in->t : 0};
+    if (s.b < 0 || s.h < 0 || s.t < 0) return false;
+    if (s.t == 0) s.t = d;
+    if (s.h == 0) s.h = T * d;          // T * d and H * T * d are bounded by the caller's size check
+    if (s.b == 0) s.b = H * T * d;
+    const int64_t n[3] = {B, H, T}, st[3] = {s.b, s.h, s.t};
+    int64_t e = d;
+    for (int i = 0; i < 3; ++i) {
+        int64_t m;
+        if (__builtin_mul_overflow(n[i] - 1, st[i], &m) || __builtin_add_overflow(e, m, &e)) return false;
+    }
+    if (e > INT64_MAX / 16) return false;   // byte extents stay far from overflow
+    *out = s;
+    *extent = e;
+    return true;
+}
+
+// True when no two (b, h, t) rows of an operand share an element: with the
+// dimensions of size > 1 sorted by stride, each stride reaches past the span
+// of the dimensions inside it.
+bool rows_disjoint(const cattn::Str3 &s, int64_t B, int64_t H, int64_t T, int64_t d) {
+    int64_t n[3] = {B, H, T}, st[3] = {s.b, s.h, s.t};
+    for (int i = 0; i < 3; ++i)        // sort by stride, ascending
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                int64_t a = st[i]; st[i] = st[j]; st[j] = a;
+                a = n[i]; n[i] = n[j]; n[j] = a;
+            }
+    int64_t ext = d;
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] <= 1) continue;
+        if (st[i] < ext) return false;
+        ext += st[i] * (n[i] - 1);     // bounded by the operand's extent
+    }
+    return true;
+}
 
 // Validates a call and fills `p`.  Returns CATTN_OK, or the first error found.
 // `empty` is set when B*H*T == 0 (valid, nothing to do).
 cattn_status validate(int op, int layout, const void *q_re, const void *q_im, const void *k_re,
                       const void *k_im, const void *v_re, const void *v_im, void *o_re, void *o_im,
-                      int64_t B, int64_t H, int64_t T, int64_t d_h, int causal, float eps, float bias,
-                      float *row_den, void *stream, Problem *p, bool *empty, float gate_r = 0.f,
-                      float gate_t = 0.f) {
+                      int64_t B, int64_t H, int64_t T, int64_t d_h, const cattn_strides *strides, int causal,
+                      float eps, float bias, float *row_den, void *stream, Problem *p, bool *empty,
+                      float gate_r = 0.f, float gate_t = 0.f) {
     if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
     if (op == cattn::OP_BORN && (!isfinite(eps) || eps < 0.f)) return CATTN_E_ARG;
     if (op == cattn::OP_PCT && !isfinite(bias)) return CATTN_E_ARG;
     if (op == cattn::OP_PCT_SCREEN && (!isfinite(gate_r) || !isfinite(gate_t))) return CATTN_E_ARG;
     if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
     if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
-    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    if (T > CATTN_MAX_T || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t BH = B * H;  // both <= 2^31, no overflow
     if (BH > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;  // bytes per element per pointer
@@ -40,6 +83,13 @@ cattn_status validate(int op, int layout, const void *q_re, const void *q_im, co
     *empty = BH == 0 || T == 0;
     if (*empty) return CATTN_OK;
 
+    cattn::Str3 st[4];
+    int64_t ext[4];
+    const cattn_stride *given[4] = {strides ? &strides->q : nullptr, strides ? &strides->k : nullptr,
+                                    strides ? &strides->v : nullptr, strides ? &strides->o : nullptr};
+    for (int i = 0; i < 4; ++i)
+        if (!resolve_strides(given[i], B, H, T, d_h, &st[i], &ext[i])) return CATTN_E_SHAPE;
+
     const void *ins[6] = {q_re, q_im, k_re, k_im, v_re, v_im};
     if (!q_re || !k_re || !v_re || !o_re) return CATTN_E_NULL;
     if (layout == CATTN_LAYOUT_C64) {
@@ -47,26 +97,30 @@ cattn_status validate(int op, int layout, const void *q_re, const void *q_im, co
     } else {
         if (!q_im || !k_im || !v_im || !o_im) return CATTN_E_NULL;
     }
+    // element alignment is required; the matrix-core kernels also want 16 bytes (below)
     for (const void *x : ins)
-        if (x && !aligned16(x)) return CATTN_E_ALIGN;
-    if (!aligned16(o_re) || (o_im && !aligned16(o_im))) return CATTN_E_ALIGN;
-    if (row_den && !aligned16(row_den)) return CATTN_E_ALIGN;
+        if (x && !aligned_to(x, elem)) return CATTN_E_ALIGN;
+    if (!aligned_to(o_re, elem) || (o_im && !aligned_to(o_im, elem))) return CATTN_E_ALIGN;
+    if (row_den && !aligned_to(row_den, 4)) return CATTN_E_ALIGN;
+    if (!rows_disjoint(st[3], B, H, T, d_h)) return CATTN_E_ALIAS;
 
-    const uintptr_t bytes = (uintptr_t)(BH * T * d_h * elem);
-    auto span = [bytes](const void *x) { return Span{(uintptr_t)x, (uintptr_t)x + bytes}; };
+    // input i (pointer slot) belongs to operand i / 2
+    auto span = [&](const void *x, int operand) {
+        return Span{(uintptr_t)x, (uintptr_t)x + (uintptr_t)(ext[operand] * elem)};
+    };
     const void *outs[2] = {o_re, o_im};
     for (const void *o : outs) {
         if (!o) continue;
-        for (const void *x : ins)
-            if (x && overlaps(span(o), span(x))) return CATTN_E_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (ins[i] && overlaps(span(o, 3), span(ins[i], i / 2))) return CATTN_E_ALIAS;
     }
-    if (o_im && overlaps(span(o_re), span(o_im))) return CATTN_E_ALIAS;
+    if (o_im && overlaps(span(o_re, 3), span(o_im, 3))) return CATTN_E_ALIAS;
     if (row_den) {
         const Span rd{(uintptr_t)row_den, (uintptr_t)row_den + (uintptr_t)(BH * T * 4)};
-        for (const void *x : ins)
-            if (x && overlaps(rd, span(x))) return CATTN_E_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (ins[i] && overlaps(rd, span(ins[i], i / 2))) return CATTN_E_ALIAS;
         for (const void *o : outs)
-            if (o && overlaps(rd, span(o))) return CATTN_E_ALIAS;
+            if (o && overlaps(rd, span(o, 3))) return CATTN_E_ALIAS;
     }
 
     p->op = op;
@@ -76,7 +130,20 @@ cattn_status validate(int op, int layout, const void *q_re, const void *q_im, co
     p->v_re = v_re; p->v_im = v_im;
     p->o_re = o_re; p->o_im = o_im;
     p->row_den = row_den;
+    p->sq = st[0]; p->sk = st[1]; p->sv = st[2]; p->so = st[3];
+    p->aligned16 = true;
+    for (const void *x : ins)
+        if (x && !aligned16(x)) p->aligned16 = false;
+    if (!aligned16(o_re) || (o_im && !aligned16(o_im))) p->aligned16 = false;
+    for (int i = 0; i < 4; ++i) {
+        const int64_t n[3] = {B, H, T}, v[3] = {st[i].b, st[i].h, st[i].t};
+        for (int j = 0; j < 3; ++j) {
+            if (n[j] <= 1) continue;   // the stride of a dimension of size 1 is never used
+            if ((v[j] * elem) % 16 != 0) p->aligned16 = false;
+        }
+    }
     p->BH = (int)BH;
+    p->H = (int)H;
     p->T = (int)T;
     p->d = (int)d_h;
     p->causal = causal != 0;
@@ -113,7 +180,7 @@ cattn_status validate_bwd(int op, int layout, const void *const in_re[5], const 
     if (op == cattn::OP_PCT && !isfinite(bias)) return CATTN_E_ARG;
     if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
     if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
-    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    if (T > CATTN_MAX_T || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t BH = B * H;
     if (BH > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
@@ -200,30 +267,32 @@ extern "C" {
 
 cattn_status cattn_born_fwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
                             const void *v_re, const void *v_im, void *o_re, void *o_im, int64_t B, int64_t H,
-                            int64_t T, int64_t d_h, int causal, float eps, float *row_den, void *stream) {
+                            int64_t T, int64_t d_h, const cattn_strides *strides, int causal, float eps,
+                            float *row_den, void *stream) {
     Problem p{};
     bool empty = false;
     const cattn_status s = validate(cattn::OP_BORN, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H,
-                                    T, d_h, causal, eps, 0.f, row_den, stream, &p, &empty);
+                                    T, d_h, strides, causal, eps, 0.f, row_den, stream, &p, &empty);
     if (s != CATTN_OK || empty) return s;
     return run(p);
 }
 
 cattn_status cattn_pct_fwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
                            const void *v_re, const void *v_im, void *o_re, void *o_im, int64_t B, int64_t H,
-                           int64_t T, int64_t d_h, int causal, float bias, void *stream) {
+                           int64_t T, int64_t d_h, const cattn_strides *strides, int causal, float bias,
+                           void *stream) {
     Problem p{};
     bool empty = false;
     const cattn_status s = validate(cattn::OP_PCT, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H,
-                                    T, d_h, causal, 0.f, bias, nullptr, stream, &p, &empty);
+                                    T, d_h, strides, causal, 0.f, bias, nullptr, stream, &p, &empty);
     if (s != CATTN_OK || empty) return s;
     return run(p);
 }
 
 cattn_status cattn_pct_gate_fwd(int layout, const void *q_re, const void *q_im, const void *k_re,
                                 const void *k_im, const void *v_re, const void *v_im, void *o_re, void *o_im,
-                                int64_t B, int64_t H, int64_t T, int64_t d_h, int causal, int gate, float a,
-                                float b, void *stream) {
+                                int64_t B, int64_t H, int64_t T, int64_t d_h, const cattn_strides *strides,
+                                int causal, int gate, float a, float b, void *stream) {
     int op;
     switch (gate) {
         case CATTN_GATE_SIGMOID: op = cattn::OP_PCT; break;
@@ -233,8 +302,8 @@ cattn_status cattn_pct_gate_fwd(int layout, const void *q_re, const void *q_im, 
     }
     Problem p{};
     bool empty = false;
-    const cattn_status s = validate(op, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H, T, d_h, causal,
-                                    0.f, gate == CATTN_GATE_SIGMOID ? a : 0.f, nullptr, stream, &p, &empty,
+    const cattn_status s = validate(op, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H, T, d_h, strides,
+                                    causal, 0.f, gate == CATTN_GATE_SIGMOID ? a : 0.f, nullptr, stream, &p, &empty,
                                     gate == CATTN_GATE_SCREEN ? a : 0.f, gate == CATTN_GATE_SCREEN ? b : 0.f);
     if (s != CATTN_OK || empty) return s;
     return run(p);
@@ -280,7 +349,7 @@ cattn_status cattn_rotary(int layout, const void *x_re, const void *x_im, void *
     if (pos0 < 0 || pos0 > ((int64_t)1 << 40)) return CATTN_E_ARG;
     if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
     if (d_h < 1 || d_h > CATTN_MAX_DH) return CATTN_E_UNSUPPORTED;
-    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    if (T > CATTN_MAX_T || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t BH = B * H;
     const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
     if (BH != 0 && T > (int64_t)(INT64_MAX / 16) / BH / d_h / elem) return CATTN_E_SHAPE;
@@ -330,7 +399,7 @@ cattn_status check_linear(int layout, int64_t B, int64_t H, int64_t T, int64_t d
     if (layout != CATTN_LAYOUT_C64 && layout != CATTN_LAYOUT_BF16_PLANES) return CATTN_E_LAYOUT;
     if (B < 0 || H < 0 || T < 0 || d_h < 0) return CATTN_E_SHAPE;
     if (d_h < 1 || d_h > CATTN_LIN_MAXD) return CATTN_E_UNSUPPORTED;
-    if (T > INT32_MAX || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
+    if (T > CATTN_MAX_T || H > INT32_MAX || B > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t BH = B * H;
     if (BH > INT32_MAX) return CATTN_E_SHAPE;
     const int64_t elem = layout == CATTN_LAYOUT_C64 ? 8 : 2;
@@ -434,7 +503,7 @@ cattn_status cattn_born_step(int layout, const void *q_re, const void *q_im, con
     return cattn::launch_born_step(p) == hipSuccess ? CATTN_OK : CATTN_E_LAUNCH;
 }
 
-const char *cattn_status_str(int status) {
+const char *cattn_status_str(cattn_status status) {
     switch (status) {
         case CATTN_OK: return "ok";
         case CATTN_E_NULL: return "required pointer is NULL (or an imaginary-plane pointer was given for complex64)";
@@ -449,6 +518,6 @@ const char *cattn_status_str(int status) {
     }
 }
 
-int cattn_abi_version(void) { return 6; }
+int cattn_abi_version(void) { return 7; }
 
 }  // extern "C"

@@ -32,17 +32,32 @@ __host__ __device__ inline bool op_pct_score(int op) { return op != OP_BORN; }
 __host__ __device__ inline bool op_row_norm(int op) { return op == OP_BORN || op == OP_PCT_SOFTMAX; }
 enum Layout : int { LAYOUT_C64 = 0, LAYOUT_BF16 = 1 };
 
-// One validated forward call.  Pointers are device pointers; tensors are
-// [BH, T, d] row-major (B and H folded, they never interact).
+// Element strides of one [B, H, T, d] operand (batch, head, token), resolved
+// (never 0 for a dimension of size > 1); d is contiguous.
+struct Str3 {
+    int64_t b, h, t;
+};
+
+// Element offset of head bh = b * H + h.
+__host__ __device__ inline int64_t head_offset(const Str3 &s, int bh, int H) {
+    return (int64_t)(bh / H) * s.b + (int64_t)(bh % H) * s.h;
+}
+
+// One validated forward call.  Pointers are device pointers; operand x of
+// head bh, token t starts at x + head_offset(sx, bh, H) + t * sx.t (in
+// elements of the layout).  B and H are folded into BH; heads never interact.
 struct Problem {
     int op;
     int layout;
     const void *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
     void *o_re, *o_im;
-    float *row_den;     // Born only, may be null
+    float *row_den;     // Born only, may be null; dense [BH, T]
+    Str3 sq, sk, sv, so;
     int BH;
+    int H;
     int T;
     int d;
+    bool aligned16;     // every base pointer and every stride is a multiple of 16 bytes
     int causal;
     float eps;          // Born
     float bias;         // PCT sigmoid cell

@@ -100,14 +100,17 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
         rb = nrb - 1 - (L % nrb);
     }
     const int m0 = rb * C::BM;
-    const int64_t head = (int64_t)bh * T * D;
+    // head bases and token strides (elements) of each operand
+    const int64_t hq = head_offset(p.sq, bh, p.H), hk = head_offset(p.sk, bh, p.H);
+    const int64_t hv = head_offset(p.sv, bh, p.H);
+    const int64_t tq = p.sq.t, tk = p.sk.t, tv = p.sv.t;
 
-    const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re) + head;
-    const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im) + head;
-    const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re) + head;
-    const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im) + head;
-    const uint16_t *vre = reinterpret_cast<const uint16_t *>(p.v_re) + head;
-    const uint16_t *vim = reinterpret_cast<const uint16_t *>(p.v_im) + head;
+    const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re) + hq;
+    const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im) + hq;
+    const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re) + hk;
+    const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im) + hk;
+    const uint16_t *vre = reinterpret_cast<const uint16_t *>(p.v_re) + hv;
+    const uint16_t *vim = reinterpret_cast<const uint16_t *>(p.v_im) + hv;
 
     // ---- Q' operands, resident for the whole kernel ------------------------
     // B operand of k-step ks, lane (q = l32, h): Q'[q][16 ks + 8 h .. +8].
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
             const int col = 16 * ks + 8 * h;
             u32x4 x = {0u, 0u, 0u, 0u};
             if (q < T) {
-                const uint16_t *src = col < D ? qre + (int64_t)q * D + col : qim + (int64_t)q * D + (col - D);
+                const uint16_t *src = col < D ? qre + (int64_t)q * tq + col : qim + (int64_t)q * tq + (col - D);
                 x = *reinterpret_cast<const u32x4 *>(src);
             }
             qb[t][ks] = as_bf16x8(x);
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
                 const int col = part * 8;
                 const int kg = k0 + key;
                 if (kg < T) {
-                    const uint16_t *src = col < D ? kre + (int64_t)kg * D + col : kim + (int64_t)kg * D + (col - D);
+                    const uint16_t *src = col < D ? kre + (int64_t)kg * tk + col : kim + (int64_t)kg * tk + (col - D);
                     x = *reinterpret_cast<const u32x4 *>(src);
                 }
             }
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
                 const int key = 32 * (pos >> 5) + vt_key_of_pos(pos & 31);
                 const int kg = k0 + key;
                 uint32_t x = 0u;
-                if (u < C::VUNITS && kg < T) x = *reinterpret_cast<const uint32_t *>(src + (int64_t)kg * D + cc);
+                if (u < C::VUNITS && kg < T) x = *reinterpret_cast<const uint32_t *>(src + (int64_t)kg * tv + cc);
                 vreg[i][s] = x;
             }
         }
@@ -299,8 +302,9 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
     }
 
     // ---- epilogue: O = acc / (sum w + eps), stored as bf16 planes ------------
-    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + head;
-    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + head;
+    const int64_t ho = head_offset(p.so, bh, p.H), to = p.so.t;
+    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + ho;
+    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + ho;
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
         const float den = rsum[t] + __shfl_xor(rsum[t], 32) + p.eps;   // both lane halves hold this query
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
                 const int col = 32 * c + 8 * g + 4 * h;     // rows col..col+3 of O^T
                 const u32x2 v = {pack_bf16x2(oacc[t][c][4 * g] * inv, oacc[t][c][4 * g + 1] * inv),
                                  pack_bf16x2(oacc[t][c][4 * g + 2] * inv, oacc[t][c][4 * g + 3] * inv)};
-                uint16_t *dst = col < D ? ore + (int64_t)q * D + col : oim + (int64_t)q * D + (col - D);
+                uint16_t *dst = col < D ? ore + (int64_t)q * to + col : oim + (int64_t)q * to + (col - D);
                 *reinterpret_cast<u32x2 *>(dst) = v;
             }
         }
@@ -339,7 +343,7 @@ hipError_t launch_cfg(const Problem &p) {
 }  // namespace
 
 bool supports_born_bf16_mfma(const Problem &p) {
-    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && (p.d == 16 || p.d == 32 || p.d == 128);
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && (p.d == 16 || p.d == 32 || p.d == 128) && p.aligned16;
 }
 
 hipError_t launch_born_bf16_mfma(const Problem &p) {

@@ -121,15 +121,19 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         bh = L / nwork;
         item = L % nwork;
     }
-    const int64_t head = (int64_t)bh * T * D;
-    const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re) + head;
-    const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im) + head;
-    const uint16_t *planes[4] = {reinterpret_cast<const uint16_t *>(p.k_re) + head,
-                                 reinterpret_cast<const uint16_t *>(p.k_im) + head,
-                                 reinterpret_cast<const uint16_t *>(p.v_re) + head,
-                                 reinterpret_cast<const uint16_t *>(p.v_im) + head};
-    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + head;
-    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + head;
+    // head bases and token strides (elements) of each operand
+    const int64_t hq = head_offset(p.sq, bh, p.H), hk = head_offset(p.sk, bh, p.H);
+    const int64_t hv = head_offset(p.sv, bh, p.H), ho = head_offset(p.so, bh, p.H);
+    const int64_t tq = p.sq.t, to = p.so.t;
+    const int64_t tkv[2] = {p.sk.t, p.sv.t};
+    const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re) + hq;
+    const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im) + hq;
+    const uint16_t *planes[4] = {reinterpret_cast<const uint16_t *>(p.k_re) + hk,
+                                 reinterpret_cast<const uint16_t *>(p.k_im) + hk,
+                                 reinterpret_cast<const uint16_t *>(p.v_re) + hv,
+                                 reinterpret_cast<const uint16_t *>(p.v_im) + hv};
+    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + ho;
+    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + ho;
 
     // ---- staging: global -> LDS, no registers ------------------------------
     // Within a region, chunk id = NT e + t (e < RPT) covers row id / 8 and
@@ -149,7 +153,7 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
             int row = k0 + srow + (NT / 8) * e;
             if (tail) row = min(row, T - 1);   // rows past T are masked out of the weights
             const int lc = g < 2 ? lck : lcv;
-            __builtin_amdgcn_global_load_lds((GLB_AS void *)(planes[g] + (int64_t)row * D + 8 * lc),
+            __builtin_amdgcn_global_load_lds((GLB_AS void *)(planes[g] + (int64_t)row * tkv[g >> 1] + 8 * lc),
                                              (LDS_AS void *)(dst + g * REGION + e * (NT * 16)), 16, 0, 0);
         }
     };
@@ -187,7 +191,7 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         for (int kk = 0; kk < 8; ++kk) {
             u32x4 x = {0u, 0u, 0u, 0u};
             if (q < T) {
-                const uint16_t *src = (kk < 4 ? qre : qim) + (int64_t)q * D + 16 * (kk & 3) + 8 * h;
+                const uint16_t *src = (kk < 4 ? qre : qim) + (int64_t)q * tq + 16 * (kk & 3) + 8 * h;
                 x = *reinterpret_cast<const u32x4 *>(src);
             }
             qb[kk] = as_bf16x8(x);
@@ -315,7 +319,7 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
                     const int col = 32 * (c & 1) + 8 * g + 4 * h;   // channel of register 4 g in its plane
                     const u32x2 v = {pack_bf16x2(oacc[c][4 * g] * inv, oacc[c][4 * g + 1] * inv),
                                      pack_bf16x2(oacc[c][4 * g + 2] * inv, oacc[c][4 * g + 3] * inv)};
-                    *reinterpret_cast<u32x2 *>((c < 2 ? ore : oim) + (int64_t)q * D + col) = v;
+                    *reinterpret_cast<u32x2 *>((c < 2 ? ore : oim) + (int64_t)q * to + col) = v;
                 }
             }
             if (p.row_den && h == 0) p.row_den[(int64_t)bh * T + q] = den;
@@ -326,7 +330,7 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
 }  // namespace
 
 bool supports_born_bf16_d64(const Problem &p) {
-    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D;
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D && p.aligned16;
 }
 
 hipError_t launch_born_bf16_d64(const Problem &p) {

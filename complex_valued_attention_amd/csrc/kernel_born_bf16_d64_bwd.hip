@@ -45,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
 
 constexpr int D = 64;
 constexpr int NW = 4;                   // waves per workgroup, one per SIMD
@@ -76,18 +77,14 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16 bytes per lane from global memory (SGPR base + per-lane byte offset)
-// straight into LDS at lds + 16 * lane.  Completion is tracked by hand
-// (vmcnt(0) before the barrier that publishes a stage).  M0 is a reserved
-// register: the compiler does not honour it as a clobber, so this form is
-// sound only while the compiler itself keeps no value in M0 across these
-// statements.  In these two kernels it emits no M0 use at all (checked in
-// their assembly: the only writes to M0 are the ones below); the SGPR-base
-// form saves the 64-bit per-lane addresses of the builtin's form, which
-// these kernels, at 512 registers, do not have room for.
-__device__ inline void dma16(uint32_t lds, const void *base, uint32_t voff) {
-    __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                         :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane,
+// as a buffer load: the resource (SGPRs) holds the stage's first row as its
+// base and the 8 KiB a stage spans as its extent, and each lane supplies a
+// 32-bit byte offset (one VGPR, where a plain global address takes two).  The
+// compiler sets M0 from the LDS pointer itself.  Completion is tracked by
+// hand (vmcnt(0) before the barrier that publishes a stage).
+__device__ inline void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(uintptr_t)lds, 16, voff, 0, 0, 0);
 }
 
 // All of this wave's loads have landed; then workgroup barrier.
@@ -106,14 +103,18 @@ __device__ inline void stage_region(uint32_t region, const uint16_t *plane, int 
                                     int wave) {
     constexpr int C = REGION / 16 / NTH;   // 16-byte chunks per thread
     static_assert(C * 16 * NTH == REGION, "staging split");
+    // the stage's first row as the uniform base (64-bit arithmetic, any T);
+    // dword 3 is the gfx9 raw-buffer format word
+    const char *sbase = reinterpret_cast<const char *>(plane) + (int64_t)r0 * ROWB;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)sbase, 0, REGION, 0x00020000);
     const int slot = tid & 7;
 #pragma unroll
     for (int e = 0; e < C; ++e) {
         const int row = (tid >> 3) + (NTH / 8) * e;
         const int lc = slot ^ (vswz ? swz_v(row) : swz_k(row));
-        const int g = min(r0 + row, T - 1);
+        const int g = min(row, T - 1 - r0);   // row within the stage; < 64, so the offset is < 8 KiB
         const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NTH * 16 + wave * 1024));
-        dma16(dst, plane, (uint32_t)(g * ROWB + 16 * lc));
+        dma16(dst, rsrc, (uint32_t)(g * ROWB + 16 * lc));
     }
 }
 

@@ -138,17 +138,20 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
         bh = L / nwork;
         item = L % nwork;
     }
-    const int64_t head = (int64_t)bh * T * C::KD;   // in floats (complex64)
-    const float *qg = reinterpret_cast<const float *>(p.q_re) + head;
-    const float *kg = reinterpret_cast<const float *>(p.k_re) + head;
-    const float *vg = reinterpret_cast<const float *>(p.v_re) + head;
-    float *og = reinterpret_cast<float *>(p.o_re) + head;
-    const int64_t headb = (int64_t)bh * T * D;      // in bf16 elements (planes)
-    auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + headb; };
-    const uint16_t *bq_re = plane(p.q_re), *bq_im = plane(p.q_im), *bk_re = plane(p.k_re),
-                   *bk_im = plane(p.k_im), *bv_re = plane(p.v_re), *bv_im = plane(p.v_im);
-    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + headb;
-    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + headb;
+    // head bases (elements: complex64 values, or bf16 values of a plane) and
+    // token strides of each operand; a complex64 element is two floats
+    const int64_t hq = head_offset(p.sq, bh, p.H), hk = head_offset(p.sk, bh, p.H);
+    const int64_t hv = head_offset(p.sv, bh, p.H), ho = head_offset(p.so, bh, p.H);
+    const int64_t rsq = p.sq.t, rsk = p.sk.t, rsv = p.sv.t, rso = p.so.t;
+    const float *qg = reinterpret_cast<const float *>(p.q_re) + 2 * hq;
+    const float *kg = reinterpret_cast<const float *>(p.k_re) + 2 * hk;
+    const float *vg = reinterpret_cast<const float *>(p.v_re) + 2 * hv;
+    float *og = reinterpret_cast<float *>(p.o_re) + 2 * ho;
+    auto plane = [&](const void *x, int64_t off) { return reinterpret_cast<const uint16_t *>(x) + off; };
+    const uint16_t *bq_re = plane(p.q_re, hq), *bq_im = plane(p.q_im, hq), *bk_re = plane(p.k_re, hk),
+                   *bk_im = plane(p.k_im, hk), *bv_re = plane(p.v_re, hv), *bv_im = plane(p.v_im, hv);
+    uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + ho;
+    uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + ho;
     // complex elements 2 e, 2 e + 1 of a row as the interleaved fp32 chunk
     auto widen2 = [&](const uint16_t *re, const uint16_t *im, int64_t el) {
         const uint32_t r2 = *reinterpret_cast<const uint32_t *>(re + el);
@@ -193,11 +196,11 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
             if (kr < T) {
                 if constexpr (LAY == LAYOUT_C64) {
-                    a = *reinterpret_cast<const f32x4 *>(kg + (int64_t)kr * C::KD + 4 * chunk_of(i));
-                    b = *reinterpret_cast<const f32x4 *>(vg + (int64_t)kr * C::KD + 4 * chunk_of(i));
+                    a = *reinterpret_cast<const f32x4 *>(kg + 2 * (int64_t)kr * rsk + 4 * chunk_of(i));
+                    b = *reinterpret_cast<const f32x4 *>(vg + 2 * (int64_t)kr * rsv + 4 * chunk_of(i));
                 } else {
-                    a = widen2(bk_re, bk_im, (int64_t)kr * D + 2 * chunk_of(i));
-                    b = widen2(bv_re, bv_im, (int64_t)kr * D + 2 * chunk_of(i));
+                    a = widen2(bk_re, bk_im, (int64_t)kr * rsk + 2 * chunk_of(i));
+                    b = widen2(bv_re, bv_im, (int64_t)kr * rsv + 2 * chunk_of(i));
                 }
             }
             kreg[i] = a;
@@ -237,9 +240,9 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (ok && qr < T) {
                 if constexpr (LAY == LAYOUT_C64)
-                    x[i] = *reinterpret_cast<const f32x4 *>(qg + (int64_t)qr * C::KD + g * C::KQ + 4 * i);
+                    x[i] = *reinterpret_cast<const f32x4 *>(qg + 2 * (int64_t)qr * rsq + g * C::KQ + 4 * i);
                 else
-                    x[i] = widen2(bq_re, bq_im, (int64_t)qr * D + g * (C::KQ / 2) + 2 * i);
+                    x[i] = widen2(bq_re, bq_im, (int64_t)qr * rsq + g * (C::KQ / 2) + 2 * i);
             }
         }
 #pragma unroll
@@ -286,9 +289,9 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             scale = den != 0.f ? 1.f / den : 0.f;
         }
         if (qr < T) {
-            float *orow = og + (int64_t)qr * C::KD + 4 * C::CPL * g;
+            float *orow = og + 2 * (int64_t)qr * rso + 4 * C::CPL * g;
             // bf16 planes: real channel n is element n / 2 of the Re (n even) or Im plane
-            const int64_t brow = (int64_t)qr * D + 2 * C::CPL * g;
+            const int64_t brow = (int64_t)qr * rso + 2 * C::CPL * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (C::CPL % 4 == 0) {
@@ -499,7 +502,7 @@ hipError_t launch_d16(const Problem &p) {
 // complex64 (every operator) and bf16 planes (the PCT cells: bf16 Born has
 // its own bf16 matrix-core kernels) at widths 16, 32, 64
 bool supports_f32_mfma16(const Problem &p) {
-    return (p.d == 16 || p.d == 32 || p.d == 64) && (p.layout == LAYOUT_C64 || p.op != OP_BORN);
+    return (p.d == 16 || p.d == 32 || p.d == 64) && (p.layout == LAYOUT_C64 || p.op != OP_BORN) && p.aligned16;
 }
 
 hipError_t launch_f32_mfma16(const Problem &p) {

@@ -62,14 +62,16 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
     const int nqb = (p.T + BQ - 1) / BQ;
     const int bh = blockIdx.x / nqb;
     const int q0 = (blockIdx.x % nqb) * BQ;
-    const int64_t base = (int64_t)bh * p.T * d;
+    // head bases and token strides (elements) of each operand
+    const int64_t bq = head_offset(p.sq, bh, p.H), bk = head_offset(p.sk, bh, p.H);
+    const int64_t bv = head_offset(p.sv, bh, p.H), bo = head_offset(p.so, bh, p.H);
     const bool pct = op_pct_score(p.op);
     const bool norm = op_row_norm(p.op);
 
     for (int i = tid; i < BQ * DP; i += NT) {
         const int r = i / DP, m = i % DP;
         float2 x = make_float2(0.f, 0.f);
-        if (m < d && q0 + r < p.T) x = load_c(p.layout, p.q_re, p.q_im, base + (int64_t)(q0 + r) * d + m);
+        if (m < d && q0 + r < p.T) x = load_c(p.layout, p.q_re, p.q_im, bq + (int64_t)(q0 + r) * p.sq.t + m);
         Qs[r][m] = x;
     }
     __syncthreads();
@@ -94,9 +96,8 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
             const int r = i / DP, m = i % DP;
             float2 kx = make_float2(0.f, 0.f), vx = make_float2(0.f, 0.f);
             if (m < d && k0 + r < p.T) {
-                const int64_t idx = base + (int64_t)(k0 + r) * d + m;
-                kx = load_c(p.layout, p.k_re, p.k_im, idx);
-                vx = load_c(p.layout, p.v_re, p.v_im, idx);
+                kx = load_c(p.layout, p.k_re, p.k_im, bk + (int64_t)(k0 + r) * p.sk.t + m);
+                vx = load_c(p.layout, p.v_re, p.v_im, bv + (int64_t)(k0 + r) * p.sv.t + m);
             }
             Ks[r][m] = kx;
             Vs[r][m] = vx;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
         if (c < d) {
             float2 o = acc[ci];
             if (norm) o = make_float2(o.x * inv, o.y * inv);
-            store_c(p.layout, p.o_re, p.o_im, base + (int64_t)qi * d + c, o);
+            store_c(p.layout, p.o_re, p.o_im, bo + (int64_t)qi * p.so.t + c, o);
         }
     }
     if (!pct && og == 0 && p.row_den) p.row_den[(int64_t)bh * p.T + qi] = D;

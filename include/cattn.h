@@ -22,9 +22,13 @@
  *
  * J(k) = {0..k} if causal != 0, else {0..T-1}.
  *
- * Tensors.  Q, K, V and O are [B, H, T, d_h], dense and row-major (d_h
- * fastest), in DEVICE memory owned by the caller; the library allocates
- * nothing and keeps no state.  Two layouts:
+ * Tensors.  Q, K, V and O are [B, H, T, d_h] in DEVICE memory owned by the
+ * caller; the library allocates nothing and keeps no state.  The d_h
+ * components of a row are contiguous.  The forward calls take element
+ * strides for the batch, head and token dimensions of each operand
+ * (cattn_strides below), so Q, K and V may be views into one fused
+ * projection output; every other call takes dense row-major tensors.  Two
+ * layouts:
  *   CATTN_LAYOUT_C64        interleaved complex64 (float re, float im); pass
  *                           the tensor in the *_re argument, *_im must be NULL.
  *   CATTN_LAYOUT_BF16_PLANES two bf16 tensors per operand, real plane in *_re
@@ -56,7 +60,7 @@ typedef enum {
     CATTN_E_NULL = 1,        /* a required pointer is NULL, or *_im is non-NULL for C64 */
     CATTN_E_SHAPE = 2,       /* a size is negative, or the byte size overflows int64 */
     CATTN_E_LAYOUT = 3,      /* unknown layout value */
-    CATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    CATTN_E_ALIGN = 4,       /* a pointer is misaligned: forward calls need element alignment, other calls 16 bytes */
     CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
     CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 (1..64 for the carried-state calls) */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
@@ -79,12 +83,53 @@ typedef enum {
 /* Largest head width accepted. */
 #define CATTN_MAX_DH 128
 
+/* Largest sequence length accepted (2^30), so that token indices plus a tile
+ * never overflow 32-bit arithmetic inside the kernels. */
+#define CATTN_MAX_T (1 << 30)
+
+/*
+ * Element strides of one [B, H, T, d_h] operand: how far apart, in elements
+ * of the layout, consecutive batches (b), heads (h) and tokens (t) sit.  An
+ * element is one complex64 value for CATTN_LAYOUT_C64 and one bf16 value of
+ * a plane for CATTN_LAYOUT_BF16_PLANES (both planes of an operand share the
+ * strides).  The d_h components of a row are always contiguous.  A stride of
+ * 0 stands for the dense value (b: H*T*d_h, h: T*d_h, t: d_h); a negative
+ * stride is CATTN_E_SHAPE.
+ *
+ * Example: the pages' BornAttention layer ("Show HN: CNET", BornAttention)
+ * takes Q, K and V as one concatenated input.  From a complex64 projection
+ * output P laid out [B, T, 3, H, d_h], the views are q = P + 0*H*d_h,
+ * k = P + 1*H*d_h, v = P + 2*H*d_h, each with strides
+ * {b = 3*T*H*d_h, h = d_h, t = 3*H*d_h}, and no copy is needed.
+ */
+typedef struct {
+    int64_t b, h, t;
+} cattn_stride;
+
+/* Strides of the four operands of a forward call (12 consecutive int64). */
+typedef struct {
+    cattn_stride q, k, v, o;
+} cattn_strides;
+
 /*
  * Born-rule attention forward (definition above).
  *   layout        CATTN_LAYOUT_C64 or CATTN_LAYOUT_BF16_PLANES.
  *   q_*, k_*, v_* inputs, o_* output (device pointers, see "Tensors").
  *   B, H, T, d_h  batch, heads, sequence length, head width (complex
- *                 components per token); 1 <= d_h <= CATTN_MAX_DH.
+ *                 components per token); 1 <= d_h <= CATTN_MAX_DH,
+ *                 T <= CATTN_MAX_T.
+ *   strides       NULL (every operand dense) or the element strides of
+ *                 Q, K, V and O (see cattn_strides).  Rows of O must not
+ *                 share memory (CATTN_E_ALIAS).  Each operand spans the bytes
+ *                 from its base to the end of its last row; O's span must
+ *                 not overlap an input's or row_den's, while the inputs'
+ *                 spans may overlap each other (views of one buffer).
+ *                 Pointers must be aligned to their element (8 bytes for
+ *                 complex64, 2 for bf16, 4 for row_den); strides need no
+ *                 alignment.  The matrix-core kernels run when every base
+ *                 pointer and every stride is a multiple of 16 bytes (always
+ *                 so for dense tensors from a 16-byte aligned allocation),
+ *                 an element-wise kernel otherwise.
  *   causal        non-zero: query k sees keys 0..k; zero: all keys.
  *   eps           added to each row denominator; >= 0 and finite.
  *   row_den       optional (NULL allowed) device float[B*H*T]: receives each
@@ -97,6 +142,7 @@ cattn_status cattn_born_fwd(int layout,
                             const void *v_re, const void *v_im,
                             void *o_re, void *o_im,
                             int64_t B, int64_t H, int64_t T, int64_t d_h,
+                            const cattn_strides *strides,
                             int causal, float eps, float *row_den, void *stream);
 
 /*
@@ -110,6 +156,7 @@ cattn_status cattn_pct_fwd(int layout,
                            const void *v_re, const void *v_im,
                            void *o_re, void *o_im,
                            int64_t B, int64_t H, int64_t T, int64_t d_h,
+                           const cattn_strides *strides,
                            int causal, float bias, void *stream);
 
 /*
@@ -130,6 +177,7 @@ cattn_status cattn_pct_gate_fwd(int layout,
                                 const void *v_re, const void *v_im,
                                 void *o_re, void *o_im,
                                 int64_t B, int64_t H, int64_t T, int64_t d_h,
+                                const cattn_strides *strides,
                                 int causal, int gate, float a, float b, void *stream);
 
 /*
@@ -265,11 +313,12 @@ cattn_status cattn_born_step(int layout,
                              float *S, float *row_den,
                              int64_t B, int64_t H, int64_t d_h, float eps, void *stream);
 
-/* Static, NUL-terminated description of a status value (never NULL). */
-const char *cattn_status_str(int status);
+/* Static, NUL-terminated description of a status value (never NULL; an
+ * unknown value gives "unknown status"). */
+const char *cattn_status_str(cattn_status status);
 
-/* ABI version of this header: 6 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state,
-   6 its packed real layout). */
+/* ABI version of this header: 7 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state,
+   6 its packed real layout, 7 strided operands in the forward calls). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,12 +1,13 @@
 """Born attention with a carried density state: state build, prefill with an
 incoming state, and the one-token step (test infrastructure only).
 
-"Show HN: CNET", BornAttention: the linear mode lifts each key to its outer
-product and carries a running state, giving O(N) memory, an exact result (the
-feature map is finite) and constant-memory autoregressive decoding in step
-mode ("one token in, one token out, the state updated in place");
-"The Quantum Shortcut", section 2: the Born rule as the linear functional
-q^H rho q of the density matrix rho = k k^H.  Per head:
+"Show HN: CNET", BornAttention (linear and step modes): each key is lifted
+to its outer product and a running state is carried along the sequence, so
+memory grows linearly, the result is exact (the feature map is finite), and
+decoding processes a single token per call while updating that state in
+place, at constant memory.  "The Quantum Shortcut", section 2: the Born rule
+as the linear functional q^H rho q of the density matrix rho = k k^H.  Per
+head:
 
     Z      = sum_j k_j k_j^H                   (d x d, the normaliser state)
     M[c]   = sum_j V[j, c] k_j k_j^H            (d x d for each value channel c)

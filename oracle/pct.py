@@ -71,10 +71,11 @@ def pct_attention_rows(q, k, v, rows, causal: bool = False, bias: float = 0.0):
 
 
 # ---------------------------------------------------------------------------- siblings
-# "Complex-valued Phase-Coherent Transformers", Appendix D.2 lists the family's
-# other members on the same scaled cosine score: the L2-softmax cell (the PCT
-# cell with the sigmoid replaced by a row softmax over j) and the complex
-# screening cell (gate r^2 relu(s - t)^2).  Only the weight map differs.  The
+# "Complex-valued Phase-Coherent Transformers", Appendix D.2: two further
+# members of the family use the same scaled cosine score.  The L2-softmax cell
+# normalises exp(s) over the keys of a row where the PCT cell applies an
+# independent sigmoid per key; the complex screening cell gates each score by
+# r^2 relu(s - t)^2.  Only the weight map differs.  The
 # screening cell's TanhNorm of the aggregate and its modReLU Hadamard gate act
 # after the attention sum and are not part of it.
 

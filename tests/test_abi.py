@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 6
+    assert L.cattn_abi_version() == 7
 
 
 def test_status_strings():
@@ -43,14 +43,18 @@ def test_status_strings():
 P = [0x100000 * (i + 1) for i in range(8)]
 
 
-def born(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=1, eps=0.0, row_den=None):
-    q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
-    return cattn.lib().cattn_born_fwd(layout, *q, B, H, T, d, causal, eps, row_den, None)
+def strides(q=(0, 0, 0), k=(0, 0, 0), v=(0, 0, 0), o=(0, 0, 0)):
+    return ctypes.byref(cattn.Strides(cattn.Stride(*q), cattn.Stride(*k), cattn.Stride(*v), cattn.Stride(*o)))
 
 
-def pct(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0):
+def born(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=1, eps=0.0, row_den=None, st=None):
     q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
-    return cattn.lib().cattn_pct_fwd(layout, *q, B, H, T, d, causal, bias, None)
+    return cattn.lib().cattn_born_fwd(layout, *q, B, H, T, d, st, causal, eps, row_den, None)
+
+
+def pct(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0, st=None):
+    q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
+    return cattn.lib().cattn_pct_fwd(layout, *q, B, H, T, d, st, causal, bias, None)
 
 
 def test_bad_layout():
@@ -65,6 +69,7 @@ def test_bad_sizes():
     assert born(d=129) == 6
     assert pct(d=1000) == 6
     assert born(T=2 ** 40) == 2
+    assert born(T=2 ** 30 + 1) == 2      # past CATTN_MAX_T
     assert born(B=2 ** 20, H=2 ** 20, T=2 ** 20) == 2
 
 
@@ -85,9 +90,10 @@ def test_null_pointers():
 
 
 def test_alignment():
-    assert born(ptrs=[P[0] + 8, None, P[1], None, P[2], None, P[3], None]) == 4
-    assert pct(layout=1, ptrs=[P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7] + 2]) == 4
-    assert born(row_den=P[7] + 4) == 4
+    # the forward calls need element alignment: 8 bytes (complex64), 2 (bf16), 4 (row_den)
+    assert born(ptrs=[P[0] + 4, None, P[1], None, P[2], None, P[3], None]) == 4
+    assert pct(layout=1, ptrs=[P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7] + 1]) == 4
+    assert born(row_den=P[7] + 2) == 4
 
 
 def test_aliasing():
@@ -107,6 +113,26 @@ def test_bad_scalars():
     assert pct(bias=float("-inf")) == 8
 
 
+def test_strides_validation():
+    # negative strides
+    assert born(st=strides(q=(0, 0, -4))) == 2
+    assert pct(st=strides(o=(-1, 0, 0)), B=2) == 2
+    # an extent past int64
+    assert born(st=strides(k=(0, 0, 2 ** 62)), T=8) == 2
+    # rows of O sharing memory: token stride below the row width, or heads on top of each other
+    assert born(st=strides(o=(0, 0, 2)), d=4) == 5
+    assert born(st=strides(o=(0, 8, 4)), H=2, T=4, d=4) == 5
+    # O's span reaching into an input: Q dense at P0 (8 rows of 4 = 256 B), O from P0 + 256 - 16
+    assert born(ptrs=[P[0], None, P[1], None, P[2], None, P[0] + 240, None]) == 5
+    # strides stretch spans: K at P1 with token stride 2^20 elements reaches far past O at P3
+    assert born(st=strides(k=(0, 0, 2 ** 20))) == 5
+    # row_den inside a strided input's span
+    assert born(st=strides(v=(0, 0, 2 ** 20)), row_den=P[5]) == 5
+    # with a stride, the other checks still come first: NULL, alignment
+    assert born(st=strides(q=(0, 0, 8)), ptrs=[None, None, P[1], None, P[2], None, P[3], None]) == 1
+    assert born(st=strides(q=(0, 0, 8)), ptrs=[P[0] + 4, None, P[1], None, P[2], None, P[3], None]) == 4
+
+
 def test_python_binding_rejects_bad_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 4, 4, dtype=torch.complex64)
@@ -114,6 +140,31 @@ def test_python_binding_rejects_bad_tensors():
         cattn.born_fwd(x, x, x)            # host tensors are refused before any call
     with pytest.raises(TypeError):
         cattn.born_fwd(x.real, x.real, x.real)
+    # per-row float32 buffers (row_den, db_rows): dtype, device, size and layout are checked
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="must be on"):
+        cattn._rows_f32(torch.zeros(8), 8, dev, "row_den")                     # a host tensor
+    with pytest.raises(TypeError, match="float32"):
+        cattn._rows_f32(torch.zeros(8, dtype=torch.bfloat16), 8, dev, "row_den")
+    with pytest.raises(TypeError, match="float32"):
+        cattn._rows_f32(torch.zeros(8, dtype=torch.float64), 8, dev, "row_den")
+    with pytest.raises(ValueError, match="8 elements"):
+        cattn._rows_f32(torch.zeros(7), 8, torch.device("cpu"), "row_den")
+    with pytest.raises(ValueError, match="8 elements"):
+        cattn._rows_f32(torch.zeros(16)[::2], 8, torch.device("cpu"), "row_den")
+    assert cattn._rows_f32(torch.zeros(8), 8, torch.device("cpu"), "row_den") is not None
+    # the carried state: dtype and device
+    with pytest.raises(ValueError, match="must be on"):
+        cattn._state_ptr(torch.zeros(1, 1, 3, 1, 1), 1, 1, 1, dev)
+    with pytest.raises(TypeError):
+        cattn._state_ptr(torch.zeros(1, 1, 3, 1, 1, dtype=torch.float64), 1, 1, 1, torch.device("cpu"))
+    # strides: a broadcast view is refused, a slice of a fused buffer passes through as it is
+    with pytest.raises(ValueError, match="broadcast"):
+        cattn._stride3(torch.zeros(1, 1, 4, 4).expand(2, 1, 4, 4), "k")
+    fused = torch.zeros(2, 5, 3, 4, 8)           # [B, T, 3, H, d]
+    qv = fused[:, :, 0].permute(0, 2, 1, 3)      # [B, H, T, d] view
+    st = cattn._stride3(qv, "q")
+    assert (st.b, st.h, st.t) == (5 * 3 * 4 * 8, 8, 3 * 4 * 8)
 
 
 # ---- backward entry points -------------------------------------------------
@@ -185,7 +236,7 @@ def test_bwd_empty_problem_is_ok():
 def gate_fwd(gate, a=0.0, b=0.0, layout=0, T=8, misalign=0):
     # every call must fail validation: a misaligned O stops the ones whose gate arguments pass
     q = [P[0], None, P[1], None, P[2], None, P[3] + misalign, None] if layout == 0 else P
-    return cattn.lib().cattn_pct_gate_fwd(layout, *q, 1, 1, T, 4, 1, gate, a, b, None)
+    return cattn.lib().cattn_pct_gate_fwd(layout, *q, 1, 1, T, 4, None, 1, gate, a, b, None)
 
 
 def test_gate_arguments():
@@ -194,7 +245,7 @@ def test_gate_arguments():
     assert gate_fwd(0, a=float("nan")) == 8    # sigmoid bias
     assert gate_fwd(2, a=float("inf")) == 8    # screening r
     assert gate_fwd(2, b=float("nan")) == 8    # screening t
-    assert gate_fwd(1, a=float("nan"), misalign=8) == 4   # the softmax gate ignores a and b
+    assert gate_fwd(1, a=float("nan"), misalign=4) == 4   # the softmax gate ignores a and b
     assert gate_fwd(1, T=0) == 0
 
 
