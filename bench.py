@@ -170,7 +170,7 @@ def main_bwd(args, w):
         t = time.perf_counter() - t0
         one = dataclasses.replace(w, B=1, H=1)
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        rec["cpu_baseline"] = {"value": bwd_flops(one) / t / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        rec["cpu_baseline"] = {"value": bwd_flops(one) / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), **host_info(),
                                "kind": "oracle", "sample": f"1 of {w.B * w.H} heads (full T={w.T}), fp64 numpy, "
                                                            f"{t:.1f} s",
                                "gpu_rowwise_rel_err_dv": rowwise_rel_err(got[2][b, h], ref[2])}
@@ -221,7 +221,7 @@ def main_rotary(args, w):
                 break
         per_head = 2 * w.T * w.d_h * (8 if w.layout == "c64" else 4)
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        cpu = {"value": done * per_head / t_used / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        cpu = {"value": done * per_head / t_used / 1e9, "unit": "GB/s", "cores": int(threads), **host_info(), "kind": "oracle",
                "sample": f"{done} of {w.B * w.H} heads of Q (full T={w.T}), fp64 numpy, {t_used:.1f} s",
                "gpu_rowwise_rel_err": err, "gpu_parity_pass": bool(err <= TOL[w.layout])}
     rec = {"metric": f"rotary GB/s ({w.name})", "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -325,7 +325,7 @@ def main_step(args, w):
                         "kernel": "born_step_kernel",
                         "bytes_per_step": nbytes, "kernel_ms_mean": float(np.mean(per)),
                         "kernel_ms_median": float(np.median(per))},
-           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads), **host_info(), "kind": "oracle",
                             "sample": f"head (0,0), {n_cpu} steps after the {T}-token prefix, fp64 numpy, "
                                       f"{t_used:.1f} s", "gpu_rowwise_rel_err": err,
                             "gpu_parity_pass": bool(err <= TOL[w.layout])}}
@@ -452,7 +452,7 @@ def main_linear(args, w):
                         "kernel": kname, "kernel_ms_mean": dom_ms,
                         "flops_per_launch": dom_flops},
            "gpu_vs_quadratic_rowwise_rel_err": err_quad,
-           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads),
+           "cpu_baseline": {"value": n_cpu / t_used, "unit": "head-tokens/s", "cores": int(threads), **host_info(),
                             "kind": "oracle",
                             "sample": f"head (0,0), first {n_cpu} tokens by the oracle's step recursion, "
                                       f"fp64 numpy, {t_used:.1f} s; {len(rows)} sampled rows by the quadratic "
@@ -533,7 +533,61 @@ def cpu_baseline(w, inp, got, budget_s: float = 12.0, gate: str = "sigmoid"):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads (full T={w.T} each), fp64 numpy, {t_used:.1f} s",
+            **host_info(),
             "gpu_rowwise_rel_err": err, "gpu_parity_pass": bool(err <= TOL[w.layout])}
+
+
+def host_info() -> dict:
+    """nproc, the CPUs this process may run on, and the CPU model of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+# The five workloads of the metric's config list, in its order: the headline is
+# the fourth; the others are timed in the same run and reported beside it.
+CONFIG_WORKLOADS = ["born_causal_c64_b1h1t128d16", "born_causal_c64_b4h8t1024d64_rotary",
+                    "pct_full_c64_b8h8t2048d64", "born_causal_bf16_b8h16t4096d64_rotary",
+                    "pct_causal_c64_b1h8t16384d64"]
+
+
+def config_record(w, got, inp, ms, per, n_rows: int = 48) -> dict:
+    """Timing, roofline fraction and sampled-row oracle parity of one workload."""
+    import oracle
+    from complex_valued_attention_amd import inputs as gen
+    from complex_valued_attention_amd.check import TOL, rowwise_rel_err, sample_rows
+    kernel_ms = float(np.mean(per))
+    flops = gen.attention_flops(w.T, w.d_h, w.causal, w.B * w.H)
+    alg = algorithmic_flops(w)
+    peak = PEAK_TFLOPS[w.layout]
+    rows = sample_rows(w.B, w.H, w.T, n_rows, seed=w.seed)
+    fn = oracle.born_attention_rows if w.op == "born" else oracle.pct_attention_rows
+    ref = fn(inp.q64, inp.k64, inp.v64, rows, causal=w.causal)
+    err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
+    achieved = alg / (kernel_ms * 1e-3) / 1e12
+    # a single workgroup's worth of work cannot fill the chip: bound by launch latency
+    latency = w.B * w.H * w.T <= 4096
+    return {"op": w.op, "causal": w.causal, "B": w.B, "H": w.H, "T": w.T, "d_h": w.d_h, "layout": w.layout,
+            "kernel": kernel_name(w), "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per)),
+            "ms_per_step": ms,
+            "flops_formula": flops, "flops_algorithmic": alg,
+            "tflops_formula": flops / (kernel_ms * 1e-3) / 1e12, "tflops_algorithmic": achieved,
+            "bound": "latency" if latency else "mfma", "peak_tflops": peak,
+            "precision": "bf16 products, fp32 accumulation" if w.layout == "bf16" else "fp32",
+            "frac": achieved / peak, "frac_of_bf16_peak": achieved / PEAK_TFLOPS["bf16"],
+            "rows_checked": int(len(rows)), "rowwise_rel_err": err, "tol": TOL[w.layout],
+            "parity_pass": bool(err <= TOL[w.layout])}
 
 
 def main():
@@ -543,6 +597,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default run: skip timing the other four workloads beside the headline")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "rotary", "step", "linear"], default="fwd")
     ap.add_argument("--chunk", type=int, default=4096, help="--pass linear: tokens per chunk")
     ap.add_argument("--gate", choices=["sigmoid", "softmax", "screen"], default="sigmoid",
@@ -622,6 +678,22 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, got, gate=args.gate)
         log(f"[bench] cpu baseline {rec['cpu_baseline']}")
+    if args.workload is None and not args.no_configs:
+        # every workload of the metric's config list, timed in this run (the
+        # headline's own entry repeats the numbers above)
+        configs = {}
+        for cname in CONFIG_WORKLOADS:
+            if cname == name:
+                configs[cname] = config_record(w, got, inp, ms, per)
+                continue
+            cw = gen.WORKLOADS[cname]
+            cinp, cgot, cms, cper, _ = run_gpu(cw, args.steps, args.warmup)
+            configs[cname] = config_record(cw, cgot, cinp, cms, cper)
+            c = configs[cname]
+            log(f"[bench] {cname}: {c['kernel_ms_mean']:.4f} ms, {c['tflops_algorithmic']:.1f} TFLOP/s "
+                f"algorithmic, frac {c['frac']:.3f}, parity {c['rowwise_rel_err']:.2e}")
+            del cinp, cgot
+        rec["configs"] = configs
     print(json.dumps(rec), flush=True)
     if args.copy_probe:
         copy_probe(args.copy_probe)

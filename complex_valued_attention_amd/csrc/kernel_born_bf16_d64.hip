@@ -96,10 +96,20 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// gfx9 raw-buffer descriptor format word (dword 3)
+constexpr int RSRC_WORD3 = 0x00020000;
+
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
-    __shared__ __align__(16) char stage_a[STAGE];   // even stages
-    __shared__ __align__(16) char stage_b[STAGE];   // odd stages
+    // Four stage buffers, each its own LDS variable: every access names its
+    // buffer at compile time, so the compiler can tell the transposing and
+    // operand reads of one buffer from the LDS-direct loads into another and
+    // waits only for the loads a read depends on.
+    __shared__ __align__(16) char buf0[STAGE];
+    __shared__ __align__(16) char buf1[STAGE];
+    __shared__ __align__(16) char buf2[STAGE];
+    __shared__ __align__(16) char buf3[STAGE];
+    char *const bufs[4] = {buf0, buf1, buf2, buf3};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,36 +135,42 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     const int64_t hq = head_offset(p.sq, bh, p.H), hk = head_offset(p.sk, bh, p.H);
     const int64_t hv = head_offset(p.sv, bh, p.H), ho = head_offset(p.so, bh, p.H);
     const int64_t tq = p.sq.t, to = p.so.t;
-    const int64_t tkv[2] = {p.sk.t, p.sv.t};
     const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re) + hq;
     const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im) + hq;
-    const uint16_t *planes[4] = {reinterpret_cast<const uint16_t *>(p.k_re) + hk,
-                                 reinterpret_cast<const uint16_t *>(p.k_im) + hk,
-                                 reinterpret_cast<const uint16_t *>(p.v_re) + hv,
-                                 reinterpret_cast<const uint16_t *>(p.v_im) + hv};
+    const char *planes[4] = {reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.k_re) + hk),
+                             reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.k_im) + hk),
+                             reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.v_re) + hv),
+                             reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.v_im) + hv)};
     uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re) + ho;
     uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + ho;
 
     // ---- staging: global -> LDS, no registers ------------------------------
-    // Within a region, chunk id = NT e + t (e < RPT) covers row id / 8 and
-    // physical slot t % 8, and receives logical chunk slot ^ swz(row) of that
-    // key row.  A wave's 64 chunks of one (region, e) are 1 KiB of LDS.
+    // Thread t covers key row t / 8 of the stage and physical chunk slot t % 8
+    // of each region, and fetches logical chunk slot ^ swz(row) of that row.
+    // A wave's 64 chunks of one region are 1 KiB of LDS.  Each plane's load is
+    // a buffer load: the descriptor's base is the stage's first key row and
+    // its extent ends at row T, so rows past T read as zero (zero keys carry
+    // zero weight, zero values add nothing); each lane adds a 32-bit offset.
     const int srow = tid >> 3;
     const int sslot = tid & 7;
-    const int lck = sslot ^ swz_k(srow);   // swizzles depend on row % 16 only
-    const int lcv = sslot ^ swz_v(srow);
+    const int64_t rbk = 2 * p.sk.t, rbv = 2 * p.sv.t;   // bytes from one key row to the next (K, V planes)
+    const uint32_t offk = (uint32_t)(srow * rbk) + 16u * (uint32_t)(sslot ^ swz_k(srow));
+    const uint32_t offv = (uint32_t)(srow * rbv) + 16u * (uint32_t)(sslot ^ swz_v(srow));
 
-    auto issue_stage = [&](int k0, char *buf) {
-        const bool tail = k0 + BN > T;
+    // live = false: an extent of 0, so the loads touch no memory (they fill
+    // the buffer with zeros); it keeps the caller free of branches.
+    auto dma_stage = [&](int k0, char *buf, bool live) {
         char *dst = buf + wave * 1024;
+        const int64_t left = live ? T - k0 : 0;
 #pragma unroll
-        for (int i = 0; i < LOADS_PER_T; ++i) {
-            const int g = i / RPT, e = i % RPT;
-            int row = k0 + srow + (NT / 8) * e;
-            if (tail) row = min(row, T - 1);   // rows past T are masked out of the weights
-            const int lc = g < 2 ? lck : lcv;
-            __builtin_amdgcn_global_load_lds((GLB_AS void *)(planes[g] + (int64_t)row * tkv[g >> 1] + 8 * lc),
-                                             (LDS_AS void *)(dst + g * REGION + e * (NT * 16)), 16, 0, 0);
+        for (int g = 0; g < 4; ++g) {
+            const int64_t rb = g < 2 ? rbk : rbv;
+            const int64_t ext = left * rb;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(planes[g] + (int64_t)k0 * rb), 0, (int)(uint32_t)(ext < 0xffffffffll ? ext : 0xffffffffll),
+                RSRC_WORD3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(dst + g * REGION), 16,
+                                                     g < 2 ? offk : offv, 0, 0, 0);
         }
     };
 
@@ -177,14 +193,39 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
 
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+    // ---- the workgroup's row blocks and their key stages --------------------
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
     auto row_block = [&](int blk) { return p.causal ? (blk == 0 ? nrb - 1 - item : item) : item; };
-    auto tile_of = [&](int blk) { return row_block(blk) * BM + 32 * wave; };   // this wave's first query
+    auto stages_of = [&](int blk) {
+        const int kend = p.causal ? min(T, row_block(blk) * BM + BM) : T;
+        return (kend + BN - 1) / BN;
+    };
+    const int nst0 = stages_of(0);
+    const int nst1 = nblocks > 1 ? stages_of(1) : 0;
+    // Stage s of a row block lives in buffer s % 4.  When the first row block
+    // has a multiple of 4 stages the stream runs on into the second with no
+    // break; otherwise (a ragged last row block) the second restarts it.
+    const bool seamless = (nst0 & 3) == 0;
+    // Loads of the workgroup's stage gs (row blocks in order) into buffer buf;
+    // past the stream's end they load nothing.  A restarted stream loads the
+    // second row block's first two stages itself, at the restart.
+    auto dma_global = [&](int gs, char *buf) {
+        const bool first = gs < nst0;
+        const int s = first ? gs : gs - nst0;
+        // no short-circuit evaluation: no branch inside the pipeline
+        dma_stage(s * BN, buf, first | ((s < nst1) & (seamless | (s >= 2))));
+    };
+    // This wave's stage loads have landed, and every wave is past the barrier.
+    auto stage_barrier = [&]() {
+        __asm__ __volatile__("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __asm__ __volatile__("" ::: "memory");
+    };
 
     // Q operands (B operand of the score products): k-step kk, lane
     // (query l32, half h) holds Q'[q][16 kk + 8 h .. + 8].
     bf16x8 qb[8];
-    bf16x8 qneg[4];   // -Re Q chunks: second half of [Im Q | -Re Q]
     auto load_q = [&](int qt0) {
         const int q = qt0 + l32;
 #pragma unroll
@@ -195,120 +236,236 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
                 x = *reinterpret_cast<const u32x4 *>(src);
             }
             qb[kk] = as_bf16x8(x);
-            if (kk < 4) qneg[kk] = as_bf16x8(x ^ 0x80008000u);
         }
     };
-    load_q(tile_of(0));
-    bool stage0_issued = false;   // the next row block's first stage is already in flight
 
-    for (int blk = 0; blk < nblocks; ++blk) {
-        const int rb = row_block(blk);
-        const int m0 = rb * BM;
-        const int qt0 = tile_of(blk);   // first query of this wave's tile
+    f32x16 oacc[4];
+    // The row sum of the weights in four independent partial sums: one
+    // accumulator would chain every pair's dot2 on the previous one, and at
+    // that instruction's latency the chain stalls the wave (products included).
+    float rsum[4];
 
-        f32x16 oacc[4];
+    // -Re Q chunk kk: the second half of [Im Q | -Re Q], formed as it is
+    // needed (one exclusive-or per register, in the issue slots between
+    // products) rather than held in 16 more registers.
+    auto neg_req = [&](int kk) { return as_bf16x8(__builtin_bit_cast(u32x4, qb[kk]) ^ 0x80008000u); };
+    // Scores S^T of a block from K' operands held in registers.
+    auto scores_reg = [&](const bf16x8 (&ka)[8], f32x16 &sr, f32x16 &si) {
+        sr = f32x16{};
+        si = f32x16{};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) oacc[c] = f32x16{};
-        float rsum = 0.f;
-
-        // Scores S^T of 32-key block sb of LDS stage st
-        auto scores = [&](const char *st, int sb, f32x16 &sr, f32x16 &si) {
-            sr = f32x16{};
-            si = f32x16{};
+        for (int kk = 0; kk < 8; ++kk) {
+            sr = mfma(ka[kk], qb[kk], sr);
+            si = mfma(ka[kk], kk < 4 ? qb[kk + 4] : neg_req(kk - 4), si);
+        }
+    };
+    auto read_k = [&](const char *st, int sb, bf16x8 (&ka)[8]) {
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + (kk >> 2) * REGION + sb * 32 * ROWB + koff[kk & 3]);
-                sr = mfma(a, qb[kk], sr);
-                si = mfma(a, kk < 4 ? qb[kk + 4] : qneg[kk - 4], si);
+        for (int kk = 0; kk < 8; ++kk)
+            ka[kk] = *reinterpret_cast<const bf16x8 *>(st + (kk >> 2) * REGION + sb * 32 * ROWB + koff[kk & 3]);
+    };
+    // The same products for the pipeline, with fewer live registers: the Re K
+    // half of K' (k-steps 0-3) arrives prefetched; the Im K half is read here
+    // and lands while the first eight products run.
+    auto read_k_re = [&](const char *st, int sb, bf16x8 (&kre)[4]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kre[kk] = *reinterpret_cast<const bf16x8 *>(st + sb * 32 * ROWB + koff[kk]);
+    };
+    auto scores_pipe = [&](const char *st, int sb, const bf16x8 (&kre)[4], f32x16 &sr, f32x16 &si) {
+        bf16x8 kim[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kim[kk] = *reinterpret_cast<const bf16x8 *>(st + REGION + sb * 32 * ROWB + koff[kk]);
+        sr = f32x16{};
+        si = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            sr = mfma(kre[kk], qb[kk], sr);
+            si = mfma(kre[kk], qb[kk + 4], si);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            sr = mfma(kim[kk], qb[kk + 4], sr);
+            si = mfma(kim[kk], neg_req(kk), si);
+        }
+    };
+    // V^T operand halves of a block: vt[2 c + m] = (lo, hi) of output tile c, keys 16 m .. 16 m + 15
+    auto read_v = [&](const char *st, int sb, u32x4 (&vt)[8]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const char *vb = st + (2 + (c >> 1)) * REGION + (32 * sb + 16 * m) * ROWB + voff[c & 1];
+                const u32x2 lo = ds_read_tr(vb);
+                const u32x2 hi = ds_read_tr(vb + 8 * ROWB);
+                vt[2 * c + m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
-        };
-        // w = |S|^2 packed to bf16; register r of lane half h is key 8 (r/4) + 4 h + r % 4.
-        // MASKED zeroes keys past `lim` (per lane): the causal diagonal, a ragged tail.
-        auto weights = [&](const f32x16 &sr, const f32x16 &si, bf16x8 (&wop)[2], bool masked, int lim) {
-            uint32_t pk[8];
+        }
+    };
+    // w = |S|^2 of one pair of keys packed to bf16, added to the row sum;
+    // register r of lane half h is key 8 (r/4) + 4 h + r % 4.
+    auto weight_pair = [&](const f32x16 &sr, const f32x16 &si, int r, bool masked, int lim) {
+        float w0 = sr[r] * sr[r] + si[r] * si[r];
+        float w1 = sr[r + 1] * sr[r + 1] + si[r + 1] * si[r + 1];
+        if (masked) {
+            const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);
+            w0 = key0 > lim ? 0.f : w0;
+            w1 = key0 + 1 > lim ? 0.f : w1;
+        }
+        const uint32_t pk = pack_bf16x2(w0, w1);
+        rsum[(r >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rsum[(r >> 1) & 3], false);
+        return pk;
+    };
+    // The value product of the previous block (operands vt, wprev) interleaved
+    // with the weights of this block (scores sr, si -> wop): one product, then
+    // the vector work of one pair of keys.
+    auto values_and_weights = [&](const u32x4 (&vt)[8], const bf16x8 (&wprev)[2], const f32x16 &sr,
+                                  const f32x16 &si, bf16x8 (&wop)[2]) {
+        uint32_t pk[8];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float w0 = sr[r] * sr[r] + si[r] * si[r];
-                float w1 = sr[r + 1] * sr[r + 1] + si[r + 1] * si[r + 1];
-                if (masked) {
-                    const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);
-                    w0 = key0 > lim ? 0.f : w0;
-                    w1 = key0 + 1 > lim ? 0.f : w1;
-                }
-                pk[r >> 1] = pack_bf16x2(w0, w1);
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]), ones, rsum, false);
-            }
-            wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-            wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
-        };
-        // O^T += V'^T W^T for block sb
-        auto values = [&](const char *st, int sb, const bf16x8 (&wop)[2]) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const char *vb = st + (2 + (c >> 1)) * REGION + (32 * sb + 16 * m) * ROWB + voff[c & 1];
-                    const u32x2 lo = ds_read_tr(vb);
-                    const u32x2 hi = ds_read_tr(vb + 8 * ROWB);
-                    oacc[c] = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), wop[m], oacc[c]);
-                }
-            }
-        };
-        auto key_block = [&](const char *st, int sb, bool masked, int lim) {
-            f32x16 sr, si;
-            bf16x8 wop[2];
-            scores(st, sb, sr, si);
-            weights(sr, si, wop, masked, lim);
-            values(st, sb, wop);
-        };
+        for (int i = 0; i < 8; ++i) {
+            oacc[i >> 1] = mfma(as_bf16x8(vt[i]), wprev[i & 1], oacc[i >> 1]);
+            pk[i] = weight_pair(sr, si, 2 * i, false, 31);
+        }
+        wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+        wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+    };
 
-        const int kend = p.causal ? min(T, m0 + BM) : T;
-        const int nstages = (kend + BN - 1) / BN;
+    // Software pipeline over the key blocks of full stages (no mask: every
+    // key of the stage is visible to every query of the row block).  Per block
+    // b: the scores of b, the Re K reads of b + 1, the value product of b - 1
+    // beside the weights of b, the V^T reads of b.  The stage's barrier sits
+    // after the scores of its second block: past it the next stage is
+    // readable, and the stage two ahead is loaded into the buffer that was
+    // read two stages back.  Entry: ka holds K' of the stage's first block,
+    // vt and wprev the previous block's value operands.
+    bf16x8 ka[4];
+    u32x4 vt[8];
+    bf16x8 wprev[2];
+    auto main_stage = [&](auto J, int gs) {
+        constexpr int j = decltype(J)::value;
+        const char *st = bufs[j];
+        f32x16 sr, si;
+        bf16x8 wop[2];
+        // block 0
+        scores_pipe(st, 0, ka, sr, si);
+        read_k_re(st, 1, ka);
+        values_and_weights(vt, wprev, sr, si, wop);
+        wprev[0] = wop[0];
+        wprev[1] = wop[1];
+        read_v(st, 0, vt);
+        // block 1
+        scores_pipe(st, 1, ka, sr, si);
+        stage_barrier();
+        dma_global(gs + 2, bufs[(j + 2) & 3]);
+        read_k_re(bufs[(j + 1) & 3], 0, ka);   // the next stage's first block (unused past the last full stage)
+        values_and_weights(vt, wprev, sr, si, wop);
+        wprev[0] = wop[0];
+        wprev[1] = wop[1];
+        read_v(st, 1, vt);
+    };
 
-        const bool wave_live = qt0 < T;
-        auto compute_stage = [&](int k0, const char *st) {
-            if (!wave_live) return;
+    // Stages with a mask or skipped blocks (the causal diagonal region, a
+    // ragged tail), one block after another straight from LDS; then the
+    // stage's barrier and the loads two stages ahead.
+    auto rest_stage = [&](auto J, int gs, int s, int qt0, bool wave_live) {
+        constexpr int j = decltype(J)::value;
+        const char *st = bufs[j];
+        if (wave_live) {
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                const int kb0 = k0 + 32 * sb;
+                const int kb0 = s * BN + 32 * sb;
                 const bool skip = kb0 >= T || (p.causal && kb0 > qt0);
                 const bool full = (!p.causal || kb0 + 32 <= qt0) && kb0 + 32 <= T;
-                if (full) {
-                    key_block(st, sb, false, 31);
-                } else if (!skip) {
-                    key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0));
+                if (!skip) {
+                    const int lim = full ? 31 : min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0);
+                    bf16x8 kb[8];
+                    read_k(st, sb, kb);
+                    f32x16 sr, si;
+                    scores_reg(kb, sr, si);
+                    u32x4 vb[8];
+                    read_v(st, sb, vb);
+                    bf16x8 wop[2];
+                    uint32_t pk[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pk[i] = weight_pair(sr, si, 2 * i, !full, lim);
+                    wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+                    wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) oacc[i >> 1] = mfma(as_bf16x8(vb[i]), wop[i & 1], oacc[i >> 1]);
                 }
             }
-        };
-
-        // Stage s lives in stage_a (s even) or stage_b (s odd).  At the top of
-        // stage s its loads have landed for every wave (barrier), and every
-        // wave is done reading the other buffer, which then takes stage s + 1.
-        if (!stage0_issued) {
-            loads_done_barrier();   // the previous row block is done with both buffers
-            issue_stage(0, stage_a);
         }
-        // with an even stage count the last stage sits in stage_b; from its top
-        // on stage_a is free and takes the next row block's first stage
-        const bool prefetch_next = blk + 1 < nblocks && (nstages & 1) == 0;
-        for (int s = 0; s < nstages; s += 2) {
-            loads_done_barrier();
-            if (s + 1 < nstages) issue_stage((s + 1) * BN, stage_b);
-            compute_stage(s * BN, stage_a);
-            if (s + 1 < nstages) {
-                loads_done_barrier();
-                if (s + 2 < nstages)
-                    issue_stage((s + 2) * BN, stage_a);
-                else if (prefetch_next)
-                    issue_stage(0, stage_a);
-                compute_stage((s + 1) * BN, stage_b);
+        stage_barrier();
+        dma_global(gs + 2, bufs[(j + 2) & 3]);
+    };
+
+    // ---- the row blocks ---------------------------------------------------
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    load_q(row_block(0) * BM + 32 * wave);
+    dma_stage(0, buf0, true);
+    dma_stage(BN, buf1, nst0 > 1);
+    stage_barrier();
+    int gbase = 0;   // the workgroup's stage index of this row block's stage 0
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const int m0 = row_block(blk) * BM;
+        const int qt0 = m0 + 32 * wave;   // first query of this wave's tile
+        const int nst = blk == 0 ? nst0 : nst1;
+        // full stages: causal, every key below the row block; otherwise every
+        // stage inside T.  They run in the pipeline in groups of four; the rest
+        // (at most four stages) take the masked path.
+        const int nfull = p.causal ? m0 / BN : T / BN;
+        const int nmain = nfull & ~3;
+
+#pragma unroll
+        for (int c = 0; c < 4; ++c) oacc[c] = f32x16{};
+        rsum[0] = rsum[1] = rsum[2] = rsum[3] = 0.f;
+        if (nmain > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vt[i] = u32x4{0u, 0u, 0u, 0u};   // no previous block: 0 x 0
+            wprev[0] = wprev[1] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+            read_k_re(buf0, 0, ka);
+            for (int s = 0; s < nmain; s += 4) {
+                // The read offsets are loop-invariant, and so is every address
+                // of a statically named buffer: left alone, the compiler hoists
+                // one register per address out of the loop.  Made opaque here,
+                // they are formed inside the loop, with the constant part in
+                // the instruction's offset field.
+                __asm__ __volatile__("" : "+v"(koff[0]), "+v"(koff[1]), "+v"(koff[2]), "+v"(koff[3]),
+                                     "+v"(voff[0]), "+v"(voff[1]));
+                main_stage(I0{}, gbase + s);
+                main_stage(I1{}, gbase + s + 1);
+                main_stage(I2{}, gbase + s + 2);
+                main_stage(I3{}, gbase + s + 3);
+            }
+            // the last block's value product
+#pragma unroll
+            for (int i = 0; i < 8; ++i) oacc[i >> 1] = mfma(as_bf16x8(vt[i]), wprev[i & 1], oacc[i >> 1]);
+        }
+        const bool wave_live = qt0 < T;
+        if (nmain < nst) rest_stage(I0{}, gbase + nmain, nmain, qt0, wave_live);
+        if (nmain + 1 < nst) rest_stage(I1{}, gbase + nmain + 1, nmain + 1, qt0, wave_live);
+        if (nmain + 2 < nst) rest_stage(I2{}, gbase + nmain + 2, nmain + 2, qt0, wave_live);
+        if (nmain + 3 < nst) rest_stage(I3{}, gbase + nmain + 3, nmain + 3, qt0, wave_live);
+
+        if (blk + 1 < nblocks) {
+            load_q(row_block(blk + 1) * BM + 32 * wave);   // in flight during the epilogue
+            if (!seamless) {
+                // restart the stream: every wave is past its last read (the
+                // barrier ending the last stage), so buffers 0 and 1 are free
+                dma_stage(0, buf0, true);
+                dma_stage(BN, buf1, nst1 > 1);
             }
         }
-        stage0_issued = prefetch_next;
-        if (blk + 1 < nblocks) load_q(tile_of(blk + 1));   // in flight during the epilogue
 
         // ---- epilogue: O = acc / (sum w + eps), bf16 planes ----------------
-        const float den = rsum + __shfl_xor(rsum, 32) + p.eps;   // both lane halves hold this query
+        const float rs = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+        const float den = rs + __shfl_xor(rs, 32) + p.eps;   // both lane halves hold this query
         const float inv = den != 0.f ? 1.f / den : 0.f;
         const int q = qt0 + l32;
         if (q < T) {
@@ -324,7 +481,12 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
             }
             if (p.row_den && h == 0) p.row_den[(int64_t)bh * T + q] = den;
         }
+        if (blk + 1 < nblocks && !seamless) stage_barrier();   // the restarted stream's first stage
+        gbase += nst;
     }
+    // Loads past the stream's end (extent 0) still write zeros into LDS: let
+    // them land before the workgroup's LDS can be handed to another.
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
 }
 
 }  // namespace

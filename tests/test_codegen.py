@@ -30,14 +30,17 @@ def device_asm(src, tmp_path):
     return out.read_text(), r.stderr
 
 
-def test_no_inline_asm_besides_compiler_barriers():
-    # the only inline asm allowed in the kernels is the empty compiler barrier
+def test_no_inline_asm_emits_instructions():
+    # inline asm in the kernels is only ever empty: a compiler barrier, or an
+    # empty statement that makes a value opaque to the optimiser; it emits no
+    # instruction, so the compiler keeps full knowledge of registers, M0 and
+    # the memory counters
     for name in sorted(os.listdir(CSRC)):
         if not name.endswith((".hip", ".h")):
             continue
         text = open(os.path.join(CSRC, name)).read()
-        for m in re.finditer(r"__asm__\s*__volatile__\s*\(([^;]*)\);", text):
-            assert re.fullmatch(r'\s*""\s*:::\s*"memory"\s*', m.group(1)), (name, m.group(0))
+        for m in re.finditer(r"\b(?:__asm__|asm)\s*(?:__volatile__|volatile)?\s*\(\s*(\"[^\"]*\")", text):
+            assert m.group(1) == '""', (name, m.group(0))
 
 
 def test_bf16_backward_lds_direct_loads_use_sgpr_base(tmp_path):
