@@ -21,6 +21,10 @@ differentiating O = N / l and w = S conj(S) gives, for j in J(k):
     dQ[k]   = sum_j 2 D[k, j] S[k, j] K[j]
     dK[j]   = sum_k 2 D[k, j] conj(S[k, j]) Q[k]
 
+With the per-head decay (the reading in :mod:`oracle.born`) the weight is
+f[k, j] |S[k, j]|^2 with the constant f = gamma^(k - j): every line above takes
+f[k, j] as one more factor (in A and in D), since f does not depend on Q or K.
+
 The derivation: dw = 2 Re(conj(S) dS), dS[k, j] = sum_m dQ[k, m] conj(K[j, m]) +
 Q[k, m] conj(dK[j, m]); collecting the coefficient of each conj(dz) gives the
 lines above.  A row whose denominator l[k] is 0 has O[k] = 0 by definition and
@@ -35,20 +39,24 @@ from __future__ import annotations
 
 import numpy as np
 
-from .born import born_attention
+from .born import born_attention, decay_factors
 
 
-def born_attention_bwd(q, k, v, g, causal: bool = True, eps: float = 0.0):
-    """(dQ, dK, dV) for complex arrays [..., T, d_h]; g = dL/d(conj O)."""
+def born_attention_bwd(q, k, v, g, causal: bool = True, eps: float = 0.0, decay=None):
+    """(dQ, dK, dV) for complex arrays [..., T, d_h]; g = dL/d(conj O); decay
+    as for the forward (causal only)."""
     q = np.asarray(q, dtype=np.complex128)
     k = np.asarray(k, dtype=np.complex128)
     v = np.asarray(v, dtype=np.complex128)
     g = np.asarray(g, dtype=np.complex128)
     T = q.shape[-2]
-    o, den = born_attention(q, k, v, causal=causal, eps=eps, return_den=True)
+    o, den = born_attention(q, k, v, causal=causal, eps=eps, return_den=True, decay=decay)
     S = q @ np.swapaxes(k.conj(), -1, -2)                      # S[k, j]
     w = S.real ** 2 + S.imag ** 2
-    mask = np.tril(np.ones((T, T))) if causal else np.ones((T, T))
+    if decay is not None:
+        mask = decay_factors(decay, T)                         # gamma^(k - j) on j <= k
+    else:
+        mask = np.tril(np.ones((T, T))) if causal else np.ones((T, T))
     live = den != 0.0
     inv = np.where(live, 1.0 / np.where(live, den, 1.0), 0.0)  # 1 / l, 0 for a dead row
     A = w * mask * inv[..., None]                               # w / l on J(k)

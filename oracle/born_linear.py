@@ -17,6 +17,15 @@ where the states at token t hold every key j <= t (the carried state plus the
 tokens of the current call up to t).  Arrays here are per head: q, k, v
 [T, d]; Z [d, d]; M [d, d, d] indexed M[c, a, b].
 
+Decay (the reading of BornAttention's fixed per-head decay, see
+:mod:`oracle.born`): with gamma in (0, 1] each token first scales the state
+by gamma and then adds its own outer product,
+
+    Z_t = gamma Z_{t-1} + k_t k_t^H,   M_t[c] = gamma M_{t-1}[c] + V[t, c] k_t k_t^H,
+
+so Z_t = sum_{j <= t} gamma^(t - j) k_j k_j^H and the read-out q_t^H M_t q_t /
+q_t^H Z_t q_t is the decayed quadratic form.  gamma = 1 is the plain state.
+
 Packed real form of the state (the layout the device library carries).  Z is
 Hermitian and each M[c] splits into two Hermitian parts,
 M[c] = X_c + i X_{d+c} with X_c = (M[c] + M[c]^H) / 2 and
@@ -35,24 +44,34 @@ def _c(x):
     return np.asarray(x, dtype=np.complex128)
 
 
-def born_state(k, v, Z0=None, M0=None):
-    """(Z, M) after adding every token of k, v [T, d] to the state (Z0, M0) (zero if None)."""
+def _gamma(gamma):
+    g = float(gamma)
+    if not (0.0 < g <= 1.0):
+        raise ValueError("decay must lie in (0, 1]")
+    return g
+
+
+def born_state(k, v, Z0=None, M0=None, gamma: float = 1.0):
+    """(Z, M) after adding every token of k, v [T, d] to the state (Z0, M0)
+    (zero if None), one token at a time: scale by gamma, add k k^H."""
+    g = _gamma(gamma)
     k, v = _c(k), _c(v)
     d = k.shape[-1]
     Z = np.zeros((d, d), np.complex128) if Z0 is None else _c(Z0).copy()
     M = np.zeros((d, d, d), np.complex128) if M0 is None else _c(M0).copy()
     for j in range(k.shape[0]):
         rho = np.outer(k[j], k[j].conj())
-        Z += rho
-        M += v[j][:, None, None] * rho[None, :, :]
+        Z = g * Z + rho
+        M = g * M + v[j][:, None, None] * rho[None, :, :]
     return Z, M
 
 
-def born_step(q, k, v, Z, M, eps: float = 0.0):
-    """One token: add (k, v) to the state, then read out q.  q, k, v [d].
-    Returns (o [d], Z', M'); o = 0 when the denominator is 0."""
+def born_step(q, k, v, Z, M, eps: float = 0.0, gamma: float = 1.0):
+    """One token: add (k, v) to the state (after scaling it by gamma), then
+    read out q.  q, k, v [d].  Returns (o [d], Z', M'); o = 0 when the
+    denominator is 0."""
     q = _c(q)
-    Z, M = born_state(_c(k)[None, :], _c(v)[None, :], Z, M)
+    Z, M = born_state(_c(k)[None, :], _c(v)[None, :], Z, M, gamma)
     den = (q.conj() @ Z @ q).real + eps
     if den == 0.0:
         return np.zeros(q.shape[-1], np.complex128), Z, M
@@ -60,7 +79,7 @@ def born_step(q, k, v, Z, M, eps: float = 0.0):
     return num / den, Z, M
 
 
-def born_prefill(q, k, v, Z0=None, M0=None, eps: float = 0.0):
+def born_prefill(q, k, v, Z0=None, M0=None, eps: float = 0.0, gamma: float = 1.0):
     """Causal Born over a sequence whose keys before token 0 are summarised by
     the state (Z0, M0): each token is one step.  Returns (O [T, d], Z, M)."""
     q, k, v = _c(q), _c(k), _c(v)
@@ -69,7 +88,7 @@ def born_prefill(q, k, v, Z0=None, M0=None, eps: float = 0.0):
     M = np.zeros((d, d, d), np.complex128) if M0 is None else _c(M0)
     out = np.zeros(q.shape, np.complex128)
     for t in range(q.shape[0]):
-        out[t], Z, M = born_step(q[t], k[t], v[t], Z, M, eps)
+        out[t], Z, M = born_step(q[t], k[t], v[t], Z, M, eps, gamma)
     return out, Z, M
 
 
