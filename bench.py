@@ -42,18 +42,8 @@ PEAK_HBM_GBS = 8000.0
 # --copy-probe kernel.  Valid only for the kernel source it was measured on:
 # any other source gives traffic = null.
 MEASURED_TRAFFIC = {
-    # one-token step with the carried state: born_step_kernel
-    "step:born_causal_bf16_b8h16t4096d64_rotary": {
-        "source": "complex_valued_attention_amd/csrc/kernel_born_linear.hip",
-        "sha256": "ea5dde56a44f154b865254f447d35d310cf03233ba5974324f701c40b4ece0c2",
-        "bytes": 542.3e6,   # read 271.5 MB + write 270.8 MB
-    },
-    # chunked prefill, chunk 4096: the state build born_state_bf16_d64_kernel
-    "linear:born_causal_bf16_b1h16t32768d64_rotary:4096": {
-        "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
-        "sha256": "271ea31f2ac5745f9f36fc050d6e22f98ca416bb5d0ed499f969d5fc3ad43ee1",
-        "bytes": 96.6e6,    # read 62.8 MB + write 33.8 MB
-    },
+    # name -> {"source": kernel file, "sha256": its hash when the counters were
+    # taken, "bytes": FETCH_SIZE + WRITE_SIZE per launch, scaled by the copy probe}
 }
 
 
@@ -461,22 +451,23 @@ def main_linear(args, w):
     print(json.dumps(rec), flush=True)
 
 
-def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid"):
+def run_gpu(w, steps: int, warmup: int, gate: str = "sigmoid", born_opts=None, inp=None):
     import torch
     from complex_valued_attention_amd import cattn, inputs as gen
     from complex_valued_attention_amd.check import from_device, to_device
 
     cattn.lib()  # fails loudly if the HIP library is not built
-    t0 = time.time()
-    inp = gen.make_inputs(w)
-    log(f"[bench] inputs {w.name}: {time.time() - t0:.1f} s")
+    if inp is None:
+        t0 = time.time()
+        inp = gen.make_inputs(w)
+        log(f"[bench] inputs {w.name}: {time.time() - t0:.1f} s")
     q, k, v = to_device(inp)
     if w.layout == "c64":
         out = torch.empty_like(q)
     else:
         out = (torch.empty_like(q[0]), torch.empty_like(q[0]))
     if w.op == "born":
-        step = lambda: cattn.born_fwd(q, k, v, causal=w.causal, out=out)
+        step = lambda: cattn.born_fwd(q, k, v, causal=w.causal, out=out, **(born_opts or {}))
     elif gate == "sigmoid":
         step = lambda: cattn.pct_fwd(q, k, v, causal=w.causal, out=out)
     else:   # screening with r = 1, t = 0.5 (a threshold inside the score range)
@@ -590,6 +581,44 @@ def config_record(w, got, inp, ms, per, n_rows: int = 48) -> dict:
             "parity_pass": bool(err <= TOL[w.layout])}
 
 
+def option_records(w, inp, plain_ms: float, steps: int, warmup: int) -> dict:
+    """The Born options on the headline workload, timed like it: the per-head
+    decay (the fixed schedule of inputs.decay_gammas) and Q rotated at load
+    (base 10000), each with sampled-row oracle parity."""
+    import oracle
+    from complex_valued_attention_amd import inputs as gen
+    from complex_valued_attention_amd.check import TOL, rowwise_rel_err, sample_rows
+    alg = algorithmic_flops(w)
+    rows = sample_rows(w.B, w.H, w.T, 32, seed=w.seed)
+    gam = gen.decay_gammas(w.H).astype(np.float32)
+    out = {}
+    for key, opts in (("decay", {"decay": gam}), ("rotary_q", {"rotary_base": 10000.0})):
+        _, got, ms, per, _ = run_gpu(w, steps, warmup, born_opts=opts, inp=inp)
+        if key == "decay":
+            ref = oracle.born_attention_rows(inp.q64, inp.k64, inp.v64, rows, causal=w.causal,
+                                             decay=gam.astype(np.float64))
+        else:   # the oracle rotates the stored Q in fp64
+            q64 = np.empty_like(inp.q64)
+            for b in range(w.B):
+                q64[b] = oracle.rotary(inp.q64[b], pos0=0, base=10000.0)
+            ref = oracle.born_attention_rows(q64, inp.k64, inp.v64, rows, causal=w.causal)
+            del q64
+        err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
+        kernel_ms = float(np.mean(per))
+        achieved = alg / (kernel_ms * 1e-3) / 1e12
+        out[key] = {"kernel": kernel_name(w), "kernel_ms_mean": kernel_ms, "kernel_ms_median": float(np.median(per)),
+                    "tflops_algorithmic": achieved, "frac": achieved / PEAK_TFLOPS[w.layout],
+                    "time_vs_plain": kernel_ms / plain_ms,
+                    "rows_checked": int(len(rows)), "rowwise_rel_err": err, "tol": TOL[w.layout],
+                    "parity_pass": bool(err <= TOL[w.layout])}
+        if key == "decay":
+            out[key]["gammas"] = "1 - 2^-(5 + 8 h / (H - 1)), h = 0..H-1 (0.969 .. 0.99988)"
+        log(f"[bench] option {key}: {kernel_ms:.4f} ms ({kernel_ms / plain_ms:.3f} x plain), "
+            f"frac {achieved / PEAK_TFLOPS[w.layout]:.3f}, parity {err:.2e}")
+        del got
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -678,6 +707,8 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, got, gate=args.gate)
         log(f"[bench] cpu baseline {rec['cpu_baseline']}")
+    if args.workload is None and not args.no_configs and w.op == "born":
+        rec["options"] = option_records(w, inp, kernel_ms, args.steps, args.warmup)
     if args.workload is None and not args.no_configs:
         # every workload of the metric's config list, timed in this run (the
         # headline's own entry repeats the numbers above)

@@ -9,6 +9,12 @@ Tensors are ``[B, H, T, d_h]`` on one ROCm device:
 * complex64: ``q, k, v`` are ``torch.complex64`` tensors;
 * bf16 planes: ``q, k, v`` are ``(re, im)`` pairs of ``torch.bfloat16`` tensors.
 
+Born options: ``decay`` (one gamma in (0, 1] per head, causal only: the
+weight of key j for query k is gamma^(k - j) |<q_k, k_j>|^2, and the carried
+state advances as Z <- gamma Z + k k^H) is accepted by the Born forward,
+backward and carried-state calls; the forward also rotates Q at load when
+given ``rotary_base`` (K is then expected already rotated).
+
 The forward calls take strided views (the last dimension contiguous, the two
 planes of a pair with equal strides), e.g. slices of one fused projection
 output; their strides go to the library as they are.  The backward, rotary
@@ -44,6 +50,12 @@ class Strides(ctypes.Structure):
     _fields_ = [("q", Stride), ("k", Stride), ("v", Stride), ("o", Stride)]
 
 
+class BornOpts(ctypes.Structure):
+    """cattn_born_opts: decay table (host float[H] or NULL) and rotary Q options."""
+    _fields_ = [("decay", ctypes.POINTER(ctypes.c_float)), ("rotary_base", ctypes.c_float),
+                ("rotary_pos0", ctypes.c_int64)]
+
+
 class CattnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -61,8 +73,9 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     sp = ctypes.POINTER(Strides)
+    fp = ctypes.POINTER(ctypes.c_float)
     L.cattn_born_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, sp,
-                                 ctypes.c_int, ctypes.c_float, vp, vp]
+                                 ctypes.c_int, ctypes.c_float, vp, ctypes.POINTER(BornOpts), vp]
     L.cattn_born_fwd.restype = ctypes.c_int
     L.cattn_pct_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, sp,
                                 ctypes.c_int, ctypes.c_float, vp]
@@ -72,14 +85,14 @@ def lib() -> ctypes.CDLL:
     L.cattn_pct_gate_fwd.restype = ctypes.c_int
     L.cattn_rotary.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
     L.cattn_rotary.restype = ctypes.c_int
-    L.cattn_born_state.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp]
+    L.cattn_born_state.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, fp, vp]
     L.cattn_born_state.restype = ctypes.c_int
-    L.cattn_born_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.cattn_born_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, fp, vp]
     L.cattn_born_merge.restype = ctypes.c_int
     L.cattn_born_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
-                                  ctypes.c_float, vp]
+                                  ctypes.c_float, fp, vp]
     L.cattn_born_step.restype = ctypes.c_int
-    L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
+    L.cattn_born_bwd.argtypes = [ctypes.c_int] + [vp] * 10 + [vp] + [vp] * 6 + [i64] * 4 + [ctypes.c_int, fp, vp]
     L.cattn_born_bwd.restype = ctypes.c_int
     L.cattn_pct_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [vp] * 6 + [i64] * 4 +
                                 [ctypes.c_int, ctypes.c_float, vp, vp])
@@ -203,14 +216,38 @@ def _sref(strides):
     return None if strides is None else ctypes.byref(strides)
 
 
-def born_fwd(q, k, v, causal: bool = True, eps: float = 0.0, out=None, row_den=None):
+def _decay(decay, H):
+    """A host float array of the H per-head decay values, or None."""
+    if decay is None:
+        return None
+    try:
+        import torch
+        if isinstance(decay, torch.Tensor):
+            decay = decay.detach().cpu().double().reshape(-1).tolist()
+    except ImportError:
+        pass
+    vals = [float(x) for x in (decay if hasattr(decay, "__len__") else [decay] * H)]
+    if len(vals) != H:
+        raise ValueError(f"decay must hold one value per head ({H}), got {len(vals)}")
+    return (ctypes.c_float * max(H, 1))(*vals)
+
+
+def born_fwd(q, k, v, causal: bool = True, eps: float = 0.0, out=None, row_den=None, decay=None,
+             rotary_base: float = 0.0, rotary_pos0: int = 0):
     """Born-rule attention forward (cattn_born_fwd).  Returns the output tensor(s).
     ``row_den`` (optional, float32 [B*H*T] on the inputs' device) receives the
-    row denominators."""
+    row denominators.  ``decay``: None, one gamma per head (a sequence or a
+    tensor) or one gamma for all heads; ``rotary_base`` > 0 rotates Q at load
+    from absolute position ``rotary_pos0``."""
     layout, ts, (B, H, T, d), out, strides = _prepare(q, k, v, out, strided=True)
     rd = None if row_den is None else _rows_f32(row_den, B * H * T, ts[0].device, "row_den")
+    dec = _decay(decay, H)
+    opts = None
+    if dec is not None or rotary_base:
+        opts = BornOpts(ctypes.cast(dec, ctypes.POINTER(ctypes.c_float)) if dec is not None else None,
+                        float(rotary_base), int(rotary_pos0))
     s = lib().cattn_born_fwd(layout, *[_ptr(t) for t in ts], B, H, T, d, _sref(strides), int(bool(causal)),
-                             float(eps), rd, _stream(ts[0]))
+                             float(eps), rd, None if opts is None else ctypes.byref(opts), _stream(ts[0]))
     _check(s)
     return out
 
@@ -274,8 +311,9 @@ def _state_ptr(S, B, H, d, device):
     return _ptr(S)
 
 
-def born_state(k, v, S, accumulate: bool = False):
-    """cattn_born_state: the packed state of the tokens of k, v (added to S's contents if accumulate)."""
+def born_state(k, v, S, accumulate: bool = False, decay=None):
+    """cattn_born_state: the packed state of the tokens of k, v (added to S's contents if accumulate;
+    under ``decay`` the old contents first scale by gamma^T)."""
     lk, kre, kim, shape = _unpack(k, "k")
     lv, vre, vim, sv = _unpack(v, "v")
     if lk != lv or shape != sv or len(shape) != 4:
@@ -284,12 +322,14 @@ def born_state(k, v, S, accumulate: bool = False):
         raise ValueError("k and v must be on one device")
     B, H, T, d = shape
     _check(lib().cattn_born_state(lk, _ptr(kre), _ptr(kim), _ptr(vre), _ptr(vim), B, H, T, d,
-                                  _state_ptr(S, B, H, d, kre.device), int(bool(accumulate)), _stream(kre)))
+                                  _state_ptr(S, B, H, d, kre.device), int(bool(accumulate)), _decay(decay, H),
+                                  _stream(kre)))
     return S
 
 
-def born_merge(q, S, o, row_den):
-    """cattn_born_merge: fold the incoming state S into a causal forward's o and row_den, in place."""
+def born_merge(q, S, o, row_den, decay=None):
+    """cattn_born_merge: fold the incoming state S into a causal forward's o and row_den, in place
+    (under ``decay`` the state counts gamma^(t+1) at token t)."""
     lq, qre, qim, shape = _unpack(q, "q")
     lo, ore, oim, so = _unpack(o, "o")
     if lq != lo or shape != so or len(shape) != 4:
@@ -299,12 +339,13 @@ def born_merge(q, S, o, row_den):
     B, H, T, d = shape
     rd = _rows_f32(row_den, B * H * T, qre.device, "row_den")
     _check(lib().cattn_born_merge(lq, _ptr(qre), _ptr(qim), _state_ptr(S, B, H, d, qre.device), _ptr(ore),
-                                  _ptr(oim), rd, B, H, T, d, _stream(qre)))
+                                  _ptr(oim), rd, B, H, T, d, _decay(decay, H), _stream(qre)))
     return o, row_den
 
 
-def born_step(q, k, v, S, eps: float = 0.0, out=None, row_den=None):
-    """cattn_born_step: one token per head ([B, H, 1, d]); updates S in place, returns (o, row_den)."""
+def born_step(q, k, v, S, eps: float = 0.0, out=None, row_den=None, decay=None):
+    """cattn_born_step: one token per head ([B, H, 1, d]); updates S in place (scaled by gamma first
+    under ``decay``), returns (o, row_den)."""
     import torch
     layout, ts, (B, H, T, d), out, _ = _prepare(q, k, v, out)
     if T != 1:
@@ -313,7 +354,7 @@ def born_step(q, k, v, S, eps: float = 0.0, out=None, row_den=None):
         row_den = torch.empty(B * H, dtype=torch.float32, device=ts[0].device)
     rd = _rows_f32(row_den, B * H, ts[0].device, "row_den")
     _check(lib().cattn_born_step(layout, *[_ptr(t) for t in ts], _state_ptr(S, B, H, d, ts[0].device), rd, B, H,
-                                 d, float(eps), _stream(ts[0])))
+                                 d, float(eps), _decay(decay, H), _stream(ts[0])))
     return out, row_den
 
 
@@ -342,12 +383,13 @@ def _bwd_outs(q, grads):
     return grads, [t for g, n in zip((dq, dk, dv), ("dq", "dk", "dv")) for t in _same(g, q, n)]
 
 
-def born_bwd(q, k, v, o, g, row_den, causal: bool = True, grads=None):
+def born_bwd(q, k, v, o, g, row_den, causal: bool = True, grads=None, decay=None):
     """Born-rule attention backward (cattn_born_bwd).
 
     ``o`` and ``row_den`` come from the forward (``born_fwd(..., row_den=...)``);
     ``g`` is dL/d(conj O) (or the real-pair gradient, which gives real-pair
-    gradients back).  Returns ``(dq, dk, dv)`` in the inputs' layout.
+    gradients back).  ``decay`` is the forward's.  Returns ``(dq, dk, dv)``
+    in the inputs' layout.
     """
     layout, ts, (B, H, T, d), _, _ = _prepare(q, k, v, _like(q))
     ore, oim = _same(o, q, "o")
@@ -357,7 +399,7 @@ def born_bwd(q, k, v, o, g, row_den, causal: bool = True, grads=None):
     rd = _rows_f32(row_den, B * H * T, ts[0].device, "row_den")
     grads, outs = _bwd_outs(q, grads)
     s = lib().cattn_born_bwd(layout, *[_ptr(t) for t in ts[:6]], _ptr(ore), _ptr(oim), _ptr(gre), _ptr(gim),
-                             rd, *[_ptr(t) for t in outs], B, H, T, d, int(bool(causal)),
+                             rd, *[_ptr(t) for t in outs], B, H, T, d, int(bool(causal)), _decay(decay, H),
                              _stream(ts[0]))
     _check(s)
     return grads

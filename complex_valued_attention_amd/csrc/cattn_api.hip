@@ -61,6 +61,22 @@ bool rows_disjoint(const cattn::Str3 &s, int64_t B, int64_t H, int64_t T, int64_
     return true;
 }
 
+// Reads a host decay table of H values into `out` (lg2 = log2 gamma in
+// double precision).  NULL: no decay.
+cattn_status resolve_decay(const float *decay, int64_t H, int causal, cattn::Decay *out) {
+    out->on = 0;
+    if (!decay) return CATTN_OK;
+    if (!causal) return CATTN_E_ARG;
+    if (H > CATTN_MAX_DECAY_HEADS) return CATTN_E_UNSUPPORTED;
+    for (int64_t h = 0; h < H; ++h) {
+        const float g = decay[h];
+        if (!(g > 0.f) || !(g <= 1.f)) return CATTN_E_ARG;   // NaN fails both
+        out->lg2[h] = (float)log2((double)g);
+    }
+    out->on = 1;
+    return CATTN_OK;
+}
+
 // Validates a call and fills `p`.  Returns CATTN_OK, or the first error found.
 // `empty` is set when B*H*T == 0 (valid, nothing to do).
 cattn_status validate(int op, int layout, const void *q_re, const void *q_im, const void *k_re,
@@ -240,6 +256,7 @@ cattn_status validate_bwd(int op, int layout, const void *const in_re[5], const 
     p->dv_re = out_re[2]; p->dv_im = out_im[2];
     p->db_rows = db_rows;
     p->BH = (int)BH;
+    p->H = (int)H;
     p->T = (int)T;
     p->d = (int)d_h;
     p->causal = causal != 0;
@@ -268,12 +285,24 @@ extern "C" {
 cattn_status cattn_born_fwd(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
                             const void *v_re, const void *v_im, void *o_re, void *o_im, int64_t B, int64_t H,
                             int64_t T, int64_t d_h, const cattn_strides *strides, int causal, float eps,
-                            float *row_den, void *stream) {
+                            float *row_den, const cattn_born_opts *opts, void *stream) {
     Problem p{};
     bool empty = false;
-    const cattn_status s = validate(cattn::OP_BORN, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H,
-                                    T, d_h, strides, causal, eps, 0.f, row_den, stream, &p, &empty);
-    if (s != CATTN_OK || empty) return s;
+    cattn_status s = validate(cattn::OP_BORN, layout, q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im, B, H, T,
+                              d_h, strides, causal, eps, 0.f, row_den, stream, &p, &empty);
+    if (s != CATTN_OK) return s;
+    if (opts) {
+        if (!isfinite(opts->rotary_base) || opts->rotary_base < 0.f) return CATTN_E_ARG;
+        if (opts->rotary_pos0 < 0 || opts->rotary_pos0 > ((int64_t)1 << 40)) return CATTN_E_ARG;
+        s = resolve_decay(opts->decay, H, causal, &p.decay);
+        if (s != CATTN_OK) return s;
+        if (opts->rotary_base > 0.f) {
+            p.rot = 1;
+            p.rot_pos0 = opts->rotary_pos0;
+            p.rot_log_base = log((double)opts->rotary_base);
+        }
+    }
+    if (empty) return CATTN_OK;
     return run(p);
 }
 
@@ -313,15 +342,17 @@ cattn_status cattn_born_bwd(int layout, const void *q_re, const void *q_im, cons
                             const void *v_re, const void *v_im, const void *o_re, const void *o_im,
                             const void *g_re, const void *g_im, const float *row_den, void *dq_re, void *dq_im,
                             void *dk_re, void *dk_im, void *dv_re, void *dv_im, int64_t B, int64_t H, int64_t T,
-                            int64_t d_h, int causal, void *stream) {
+                            int64_t d_h, int causal, const float *decay, void *stream) {
     const void *const in_re[5] = {q_re, k_re, v_re, o_re, g_re};
     const void *const in_im[5] = {q_im, k_im, v_im, o_im, g_im};
     void *const out_re[3] = {dq_re, dk_re, dv_re};
     void *const out_im[3] = {dq_im, dk_im, dv_im};
     cattn::BwdProblem p{};
     bool empty = false;
-    const cattn_status s = validate_bwd(cattn::OP_BORN, layout, in_re, in_im, row_den, out_re, out_im, nullptr, B,
-                                        H, T, d_h, causal, 0.f, stream, &p, &empty);
+    cattn_status s = validate_bwd(cattn::OP_BORN, layout, in_re, in_im, row_den, out_re, out_im, nullptr, B, H,
+                                  T, d_h, causal, 0.f, stream, &p, &empty);
+    if (s != CATTN_OK) return s;
+    s = resolve_decay(decay, H, causal, &p.decay);
     if (s != CATTN_OK || empty) return s;
     return run_bwd(p);
 }
@@ -429,6 +460,7 @@ cattn_status check_linear(int layout, int64_t B, int64_t H, int64_t T, int64_t d
                 return CATTN_E_ALIAS;
     p->layout = c64 ? cattn::LAYOUT_C64 : cattn::LAYOUT_BF16;
     p->BH = (int)BH;
+    p->H = (int)H;
     p->T = (int)T;
     p->d = (int)d_h;
     return CATTN_OK;
@@ -439,12 +471,17 @@ uintptr_t s_bytes(int64_t B, int64_t H, int64_t d) { return (uintptr_t)(B * H * 
 }  // namespace
 
 cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, const void *v_re, const void *v_im,
-                              int64_t B, int64_t H, int64_t T, int64_t d_h, float *S, int accumulate, void *stream) {
+                              int64_t B, int64_t H, int64_t T, int64_t d_h, float *S, int accumulate,
+                              const float *decay, void *stream) {
     const void *cre[2] = {k_re, v_re}, *cim[2] = {k_im, v_im};
     const bool cw[2] = {false, false};
     const Buf extra[1] = {{S, s_bytes(B, H, d_h), true}};
     cattn::LinearProblem p{};
     bool empty = false;
+    if (H >= 0) {
+        const cattn_status s = resolve_decay(decay, H, 1, &p.decay);
+        if (s != CATTN_OK) return s;
+    }
     if (T == 0 && !accumulate) {
         // no tokens, overwrite: the state becomes zero (k and v are not read)
         const cattn_status s = check_linear(layout, B, H, 1, d_h, nullptr, nullptr, nullptr, 0, extra, 1, &p, &empty);
@@ -466,12 +503,16 @@ cattn_status cattn_born_state(int layout, const void *k_re, const void *k_im, co
 
 cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, const float *S, void *o_re,
                               void *o_im, float *row_den, int64_t B, int64_t H, int64_t T, int64_t d_h,
-                              void *stream) {
+                              const float *decay, void *stream) {
     const void *cre[2] = {q_re, o_re}, *cim[2] = {q_im, o_im};
     const bool cw[2] = {false, true};
     const Buf extra[2] = {{S, s_bytes(B, H, d_h), false}, {row_den, (uintptr_t)(B * H * T * 4), true}};
     cattn::LinearProblem p{};
     bool empty = false;
+    if (H >= 0) {
+        const cattn_status s = resolve_decay(decay, H, 1, &p.decay);
+        if (s != CATTN_OK) return s;
+    }
     const cattn_status s = check_linear(layout, B, H, T, d_h, cre, cim, cw, 2, extra, 2, &p, &empty);
     if (s != CATTN_OK || empty) return s;
     p.q_re = q_re; p.q_im = q_im; p.o_re = o_re; p.o_im = o_im;
@@ -486,12 +527,17 @@ cattn_status cattn_born_merge(int layout, const void *q_re, const void *q_im, co
 
 cattn_status cattn_born_step(int layout, const void *q_re, const void *q_im, const void *k_re, const void *k_im,
                              const void *v_re, const void *v_im, void *o_re, void *o_im, float *S,
-                             float *row_den, int64_t B, int64_t H, int64_t d_h, float eps, void *stream) {
+                             float *row_den, int64_t B, int64_t H, int64_t d_h, float eps, const float *decay,
+                             void *stream) {
     if (!isfinite(eps) || eps < 0.f) return CATTN_E_ARG;
+    cattn::LinearProblem p{};
+    if (H >= 0) {
+        const cattn_status s = resolve_decay(decay, H, 1, &p.decay);
+        if (s != CATTN_OK) return s;
+    }
     const void *cre[4] = {q_re, k_re, v_re, o_re}, *cim[4] = {q_im, k_im, v_im, o_im};
     const bool cw[4] = {false, false, false, true};
     const Buf extra[2] = {{S, s_bytes(B, H, d_h), true}, {row_den, (uintptr_t)(B * H * 4), true}};
-    cattn::LinearProblem p{};
     bool empty = false;
     const cattn_status s = check_linear(layout, B, H, 1, d_h, cre, cim, cw, 4, extra, 2, &p, &empty);
     if (s != CATTN_OK || empty) return s;
@@ -511,13 +557,13 @@ const char *cattn_status_str(cattn_status status) {
         case CATTN_E_LAYOUT: return "unknown layout";
         case CATTN_E_ALIGN: return "pointer not 16-byte aligned";
         case CATTN_E_ALIAS: return "an output overlaps an input or another output";
-        case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128 (1..64 for the carried-state calls)";
+        case CATTN_E_UNSUPPORTED: return "head width d_h outside 1..128 (1..64 for the carried-state calls), or too many heads for a decay table";
         case CATTN_E_LAUNCH: return "HIP kernel launch failed";
-        case CATTN_E_ARG: return "a scalar argument out of range (eps, bias, gate parameters, rotary base or position) or an unknown gate";
+        case CATTN_E_ARG: return "a scalar argument out of range (eps, bias, gate parameters, rotary base or position, a decay value), decay on a non-causal call, or an unknown gate";
         default: return "unknown status";
     }
 }
 
-int cattn_abi_version(void) { return 7; }
+int cattn_abi_version(void) { return 8; }
 
 }  // extern "C"

@@ -43,6 +43,19 @@ __host__ __device__ inline int64_t head_offset(const Str3 &s, int bh, int H) {
     return (int64_t)(bh / H) * s.b + (int64_t)(bh % H) * s.h;
 }
 
+// Per-head decay of the causal Born weights, w[k, j] = gamma_h^(k - j) |S|^2:
+// lg2[h] = log2(gamma_h) <= 0 (formed on the host in double precision) for
+// the H heads of the call; on == 0 means no decay.  Powers are formed as
+// exp2(n * lg2[h]).  Passed by value in the kernel arguments.
+#define CATTN_DECAY_MAXH 256
+struct Decay {
+    int on;
+    float lg2[CATTN_DECAY_MAXH];
+};
+
+// gamma_h^n, n >= 0
+__device__ inline float decay_pow(float lg2, int n) { return __builtin_amdgcn_exp2f(lg2 * (float)n); }
+
 // One validated forward call.  Pointers are device pointers; operand x of
 // head bh, token t starts at x + head_offset(sx, bh, H) + t * sx.t (in
 // elements of the layout).  B and H are folded into BH; heads never interact.
@@ -64,6 +77,11 @@ struct Problem {
     float gate_r;       // screening gate: r
     float gate_t;       // screening gate: t
     hipStream_t stream;
+    // Born options (kept last: large and rarely read)
+    int rot;            // rotate Q at load (the rotary phase of cattn_rotary)
+    int64_t rot_pos0;
+    double rot_log_base;
+    Decay decay;
 };
 
 // Each launcher enqueues the whole forward for `p` and returns the launch
@@ -97,6 +115,8 @@ struct BwdProblem {
     int causal;
     float bias;                  // PCT
     hipStream_t stream;
+    int H;
+    Decay decay;                 // Born
 };
 
 hipError_t launch_bwd_generic(const BwdProblem &p);        // both kernels
@@ -139,6 +159,8 @@ struct LinearProblem {
     int accumulate;    // state build: add to the state instead of overwriting it
     float eps;         // step
     hipStream_t stream;
+    int H;
+    Decay decay;
 };
 
 hipError_t launch_born_state(const LinearProblem &p);

@@ -23,7 +23,12 @@
 // [2 d_h][BN] with the key order the W^T operand uses, so both are read with
 // one 16-byte LDS load per lane per MFMA.  Stages above a tile's causal
 // diagonal are skipped; the diagonal 32x32 block is masked in registers.
+//
+// Born options (instances of their own): a per-head decay multiplies each
+// weight by gamma^(k - j), formed per weight; a rotary Q is rotated as it is
+// loaded, with the arithmetic of the rotary pass (rotary_math.h).
 #include "cattn_internal.h"
+#include "rotary_math.h"
 
 namespace cattn {
 namespace {
@@ -74,7 +79,7 @@ __device__ inline int vt_key_of_pos(int pos) {   // pos in 0..31 -> key in 0..31
     return 16 * m + 8 * (s >> 2) + 4 * h + (s & 3);
 }
 
-template <int D, int NQT, int NW, int BN>
+template <int D, int NQT, int NW, int BN, bool OPT>
 __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int nrb) {
     using C = BornCfg<D, NQT, NW, BN>;
     extern __shared__ __align__(16) __bf16 smem[];
@@ -119,18 +124,40 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
         const int q = m0 + 32 * (NQT * wave + t) + l32;
+        u32x4 x[C::KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
             const int col = 16 * ks + 8 * h;
-            u32x4 x = {0u, 0u, 0u, 0u};
+            x[ks] = u32x4{0u, 0u, 0u, 0u};
             if (q < T) {
                 const uint16_t *src = col < D ? qre + (int64_t)q * tq + col : qim + (int64_t)q * tq + (col - D);
-                x = *reinterpret_cast<const u32x4 *>(src);
+                x[ks] = *reinterpret_cast<const u32x4 *>(src);
             }
-            qb[t][ks] = as_bf16x8(x);
-            if (ks < C::KSTEPS / 2) qneg[t][ks] = as_bf16x8(x ^ 0x80008000u);
+        }
+        if (OPT && p.rot && q < T) {
+            // chunk ks < KSTEPS / 2 holds Re of channels 16 ks + 8 h + e, chunk ks + KSTEPS / 2 their Im
+            const double pos = (double)(p.rot_pos0 + q);
+#pragma unroll
+            for (int ks = 0; ks < C::KSTEPS / 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sh = 16 * (e & 1);
+                    const uint32_t rw = x[ks][e >> 1], iw = x[ks + C::KSTEPS / 2][e >> 1];
+                    float c, sn, yr, yi;
+                    rotary_phase(pos, rotary_theta(16 * ks + 8 * h + e, p.rot_log_base, D), c, sn);
+                    rotary_apply(__uint_as_float(((rw >> sh) & 0xffffu) << 16),
+                                 __uint_as_float(((iw >> sh) & 0xffffu) << 16), c, sn, yr, yi);
+                    x[ks][e >> 1] = (rw & ~(0xffffu << sh)) | ((uint32_t)rotary_bf16(yr) << sh);
+                    x[ks + C::KSTEPS / 2][e >> 1] = (iw & ~(0xffffu << sh)) | ((uint32_t)rotary_bf16(yi) << sh);
+                }
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            qb[t][ks] = as_bf16x8(x[ks]);
+            if (ks < C::KSTEPS / 2) qneg[t][ks] = as_bf16x8(x[ks] ^ 0x80008000u);
         }
     }
+    const float lg2 = OPT && p.decay.on ? p.decay.lg2[bh % p.H] : 0.f;
 
     f32x16 oacc[NQT][C::CT];
     float rsum[NQT];
@@ -268,6 +295,12 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
                 for (int r = 0; r < 16; r += 2) {
                     float w0 = sr[t][r] * sr[t][r] + si[t][r] * si[t][r];
                     float w1 = sr[t][r + 1] * sr[t][r + 1] + si[t][r + 1] * si[t][r + 1];
+                    if (OPT && p.decay.on) {
+                        // gamma^(k - j); negative distances only on keys the mask zeroes
+                        const int n = m0 + 32 * (NQT * wave + t) + l32 - kb0 - (8 * (r >> 2) + 4 * h + (r & 3));
+                        w0 *= decay_pow(lg2, max(n, 0));
+                        w1 *= decay_pow(lg2, max(n - 1, 0));
+                    }
                     if (diag[t]) {
                         const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);   // key row of register r
                         if (key0 > l32) w0 = 0.f;
@@ -329,9 +362,10 @@ __global__ __launch_bounds__(64 * NW) void born_bf16_mfma_kernel(Problem p, int 
 template <int D, int NQT, int NW, int BN>
 hipError_t launch_cfg(const Problem &p) {
     using C = BornCfg<D, NQT, NW, BN>;
-    auto kern = born_bf16_mfma_kernel<D, NQT, NW, BN>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
+    const bool opt = p.decay.on || p.rot;
+    auto kern = opt ? born_bf16_mfma_kernel<D, NQT, NW, BN, true> : born_bf16_mfma_kernel<D, NQT, NW, BN, false>;
+    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};   // per instance
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set[opt]);
     if (e != hipSuccess) return e;
     const int nrb = (p.T + C::BM - 1) / C::BM;
     const int64_t blocks = (int64_t)p.BH * nrb;

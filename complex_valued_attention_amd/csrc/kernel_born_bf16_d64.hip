@@ -37,7 +37,21 @@
 // drains evenly.  Key blocks of 32 strictly below a tile's diagonal take a
 // path with no mask arithmetic; the diagonal block (and a ragged tail) is
 // masked; blocks above the diagonal are skipped.
+//
+// Born options, in instances of their own (the plain kernel carries none of
+// their registers).  Decay (causal): the weight of key j for query k is
+// multiplied by gamma^(k - j).  On a full block the distance of register r
+// (key 8 (r/4) + 4 h + r%4 of the block) splits into a part fixed per lane,
+// block and group of four registers (query offset, lane half, block start,
+// r/4) and a part fixed per register within its group (r%4):
+// gamma^(k - j) = mu[r/4] * sigma[r%4], all at most 1 on a full block; mu is
+// formed per block and lane (four exponentials), sigma once per kernel, so
+// each weight takes two extra multiplies.  Masked blocks
+// form gamma^(k - j) per weight.  Rotary Q: each query operand is rotated as it is loaded (the
+// arithmetic of the rotary pass, rotary_math.h), with the channel
+// frequencies in a small LDS table formed once per workgroup.
 #include "cattn_internal.h"
+#include "rotary_math.h"
 
 
 
@@ -99,6 +113,7 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // gfx9 raw-buffer descriptor format word (dword 3)
 constexpr int RSRC_WORD3 = 0x00020000;
 
+template <bool DECAY, bool ROT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     // Four stage buffers, each its own LDS variable: every access names its
@@ -226,18 +241,54 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     // Q operands (B operand of the score products): k-step kk, lane
     // (query l32, half h) holds Q'[q][16 kk + 8 h .. + 8].
     bf16x8 qb[8];
+    // ROT: theta_m of the 64 channels
+    __shared__ double rtheta[D];
     auto load_q = [&](int qt0) {
         const int q = qt0 + l32;
+        u32x4 x[8];
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            u32x4 x = {0u, 0u, 0u, 0u};
+            x[kk] = u32x4{0u, 0u, 0u, 0u};
             if (q < T) {
                 const uint16_t *src = (kk < 4 ? qre : qim) + (int64_t)q * tq + 16 * (kk & 3) + 8 * h;
-                x = *reinterpret_cast<const u32x4 *>(src);
+                x[kk] = *reinterpret_cast<const u32x4 *>(src);
             }
-            qb[kk] = as_bf16x8(x);
         }
+        if (ROT && q < T) {
+            // (Re, Im) of channel 16 kk + 8 h + e: element e of chunks kk and kk + 4
+            const double pos = (double)(p.rot_pos0 + q);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sh = 16 * (e & 1);
+                    const uint32_t rw = x[kk][e >> 1], iw = x[kk + 4][e >> 1];
+                    float c, sn, yr, yi;
+                    rotary_phase(pos, rtheta[16 * kk + 8 * h + e], c, sn);
+                    rotary_apply(__uint_as_float(((rw >> sh) & 0xffffu) << 16),
+                                 __uint_as_float(((iw >> sh) & 0xffffu) << 16), c, sn, yr, yi);
+                    x[kk][e >> 1] = (rw & ~(0xffffu << sh)) | ((uint32_t)rotary_bf16(yr) << sh);
+                    x[kk + 4][e >> 1] = (iw & ~(0xffffu << sh)) | ((uint32_t)rotary_bf16(yi) << sh);
+                }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qb[kk] = as_bf16x8(x[kk]);
     };
+
+    // DECAY: log2 gamma of the head, sigma[b] = gamma^(3 - b), and per row
+    // block the lane's part of the exponent of mu (see the note at the top).
+    const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
+    float sig[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        sig[b] = 1.f;
+        if (DECAY) {
+            const float x = decay_pow(lg2, 3 - b);
+            sig[b] = x;
+        }
+    }
+    int dq0 = 0;     // qt0 + l32 - 4 h - 3 of the current row block
+    int gbase = 0;   // the workgroup's stage index of this row block's stage 0
 
     f32x16 oacc[4];
     // The row sum of the weights in four independent partial sums: one
@@ -304,10 +355,15 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         }
     };
     // w = |S|^2 of one pair of keys packed to bf16, added to the row sum;
-    // register r of lane half h is key 8 (r/4) + 4 h + r % 4.
-    auto weight_pair = [&](const f32x16 &sr, const f32x16 &si, int r, bool masked, int lim) {
+    // register r of lane half h is key 8 (r/4) + 4 h + r % 4.  DECAY: times
+    // the factors f0, f1 of the two keys.
+    auto weight_pair = [&](const f32x16 &sr, const f32x16 &si, int r, bool masked, int lim, float f0, float f1) {
         float w0 = sr[r] * sr[r] + si[r] * si[r];
         float w1 = sr[r + 1] * sr[r + 1] + si[r + 1] * si[r + 1];
+        if (DECAY) {
+            w0 *= f0;
+            w1 *= f1;
+        }
         if (masked) {
             const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);
             w0 = key0 > lim ? 0.f : w0;
@@ -320,13 +376,19 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     // The value product of the previous block (operands vt, wprev) interleaved
     // with the weights of this block (scores sr, si -> wop): one product, then
     // the vector work of one pair of keys.
+    // DECAY: kb0 is the block's first key (a full block: every factor <= 1).
     auto values_and_weights = [&](const u32x4 (&vt)[8], const bf16x8 (&wprev)[2], const f32x16 &sr,
-                                  const f32x16 &si, bf16x8 (&wop)[2]) {
+                                  const f32x16 &si, bf16x8 (&wop)[2], int kb0) {
+        float mu[4];   // gamma^(qt0 + l32 - kb0 - 8 a - 4 h - 3) for register group a
+#pragma unroll
+        for (int a = 0; a < 4; ++a) mu[a] = DECAY ? decay_pow(lg2, dq0 - kb0 - 8 * a) : 1.f;
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             oacc[i >> 1] = mfma(as_bf16x8(vt[i]), wprev[i & 1], oacc[i >> 1]);
-            pk[i] = weight_pair(sr, si, 2 * i, false, 31);
+            // registers 2 i, 2 i + 1: group i / 2, places 2 (i % 2) and 2 (i % 2) + 1
+            pk[i] = weight_pair(sr, si, 2 * i, false, 31, mu[i >> 1] * sig[2 * (i & 1)],
+                                mu[i >> 1] * sig[2 * (i & 1) + 1]);
         }
         wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
         wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
@@ -346,12 +408,13 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     auto main_stage = [&](auto J, int gs) {
         constexpr int j = decltype(J)::value;
         const char *st = bufs[j];
+        const int k0 = (gs - gbase) * BN;   // the stage's first key
         f32x16 sr, si;
         bf16x8 wop[2];
         // block 0
         scores_pipe(st, 0, ka, sr, si);
         read_k_re(st, 1, ka);
-        values_and_weights(vt, wprev, sr, si, wop);
+        values_and_weights(vt, wprev, sr, si, wop, k0);
         wprev[0] = wop[0];
         wprev[1] = wop[1];
         read_v(st, 0, vt);
@@ -360,7 +423,7 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
         stage_barrier();
         dma_global(gs + 2, bufs[(j + 2) & 3]);
         read_k_re(bufs[(j + 1) & 3], 0, ka);   // the next stage's first block (unused past the last full stage)
-        values_and_weights(vt, wprev, sr, si, wop);
+        values_and_weights(vt, wprev, sr, si, wop, k0 + 32);
         wprev[0] = wop[0];
         wprev[1] = wop[1];
         read_v(st, 1, vt);
@@ -389,7 +452,14 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
                     bf16x8 wop[2];
                     uint32_t pk[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pk[i] = weight_pair(sr, si, 2 * i, !full, lim);
+                    for (int i = 0; i < 8; ++i) {
+                        // DECAY: gamma^(k - j) per weight; masked keys (negative distance) are zeroed
+                        const int key0 = 8 * (i >> 1) + 4 * h + 2 * (i & 1);
+                        const int n0 = qt0 + l32 - kb0 - key0;
+                        const float f0 = DECAY ? decay_pow(lg2, max(n0, 0)) : 1.f;
+                        const float f1 = DECAY ? decay_pow(lg2, max(n0 - 1, 0)) : 1.f;
+                        pk[i] = weight_pair(sr, si, 2 * i, !full, lim, f0, f1);
+                    }
                     wop[0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
                     wop[1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
 #pragma unroll
@@ -407,14 +477,19 @@ void born_bf16_d64_kernel(Problem p, int nrb, int nwork) {
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
 
+    if (ROT) {
+        if (tid < D) rtheta[tid] = rotary_theta(tid, p.rot_log_base, D);
+        __syncthreads();
+    }
     load_q(row_block(0) * BM + 32 * wave);
     dma_stage(0, buf0, true);
     dma_stage(BN, buf1, nst0 > 1);
     stage_barrier();
-    int gbase = 0;   // the workgroup's stage index of this row block's stage 0
+    gbase = 0;
     for (int blk = 0; blk < nblocks; ++blk) {
         const int m0 = row_block(blk) * BM;
         const int qt0 = m0 + 32 * wave;   // first query of this wave's tile
+        dq0 = qt0 + l32 - 4 * h - 3;
         const int nst = blk == 0 ? nst0 : nst1;
         // full stages: causal, every key below the row block; otherwise every
         // stage inside T.  They run in the pipeline in groups of four; the rest
@@ -500,7 +575,9 @@ hipError_t launch_born_bf16_d64(const Problem &p) {
     const int nwork = p.causal ? (nrb + 1) / 2 : nrb;   // causal: mirrored pairs of row blocks
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_bf16_d64_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nrb, nwork);
+    auto kern = p.decay.on ? (p.rot ? born_bf16_d64_kernel<true, true> : born_bf16_d64_kernel<true, false>)
+                           : (p.rot ? born_bf16_d64_kernel<false, true> : born_bf16_d64_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nrb, nwork);
     return hipGetLastError();
 }
 

@@ -636,7 +636,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 }  // namespace
 
 bool supports_born_bf16_d64_bwd(const BwdProblem &p) {
-    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D;
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D && !p.decay.on;
 }
 
 hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {

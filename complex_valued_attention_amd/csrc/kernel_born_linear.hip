@@ -25,6 +25,10 @@
 //    64-token tile), a thread per (token, group of matrices);
 //  * step: one token per head, HBM-bound (the state read and written once);
 //    then the division by the denominator.
+// With a per-head decay gamma every token first scales the state by gamma:
+// the state build weighs token t of T by gamma^(T-1-t) and an accumulated
+// state by gamma^T, the merge counts the incoming state gamma^(t+1) at token
+// t, and the step scales the state by gamma before adding the token.
 #include "cattn_internal.h"
 
 namespace cattn {
@@ -102,6 +106,8 @@ __global__ __launch_bounds__(NT) void born_state_kernel(LinearProblem p) {
     const int a = tid / 4, b0 = 16 * (tid % 4);
     const bool active = a < d && b0 < d;
     const int64_t base = bh * p.T * d;
+    const float lg2 = p.decay.on ? p.decay.lg2[bh % p.H] : 0.f;
+    const float carry = p.decay.on ? decay_pow(lg2, p.T) : 1.f;   // gamma^T on the old state
 
     float acc[SG_G][16];
 #pragma unroll
@@ -109,7 +115,8 @@ __global__ __launch_bounds__(NT) void born_state_kernel(LinearProblem p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int n = n0 + g, b = b0 + j;
-            acc[g][j] = (p.accumulate && active && n <= 2 * d && b < d) ? state_matrix(p, bh, n)[a * d + b] : 0.f;
+            acc[g][j] = (p.accumulate && active && n <= 2 * d && b < d) ? carry * state_matrix(p, bh, n)[a * d + b]
+                                                                        : 0.f;
         }
     // which table each column reads: the pair on or above the diagonal, the rotated pair below
     const float2(*tab[16]);
@@ -128,8 +135,10 @@ __global__ __launch_bounds__(NT) void born_state_kernel(LinearProblem p) {
         for (int i = tid; i < TT * SG_G; i += NT) {
             const int r = i / SG_G, g = i % SG_G;
             const int n = n0 + g;
-            wv[r][g] = (t0 + r < p.T && n <= 2 * d)
-                           ? col_weight(p.layout, p.v_re, p.v_im, base + (int64_t)(t0 + r) * d, n, d) : 0.f;
+            float w = (t0 + r < p.T && n <= 2 * d)
+                          ? col_weight(p.layout, p.v_re, p.v_im, base + (int64_t)(t0 + r) * d, n, d) : 0.f;
+            if (p.decay.on && t0 + r < p.T) w *= decay_pow(lg2, p.T - 1 - (t0 + r));
+            wv[r][g] = w;
         }
         __syncthreads();
         if (!active) continue;
@@ -222,23 +231,27 @@ __global__ __launch_bounds__(NT) void born_merge_kernel(LinearProblem p) {
 #pragma unroll
     for (int i = 0; i < MG_NG; ++i) res[t][g * MG_NG + i] = acc[i];
     __syncthreads();
+    // with decay the incoming state counts gamma^(t+1) at token t
+    const float lg2 = p.decay.on ? p.decay.lg2[bh % p.H] : 0.f;
+    auto carry = [&](int tq) { return p.decay.on ? decay_pow(lg2, tq + 1) : 1.f; };
     // O <- (O l + num) / (l + den); l from the forward (eps included)
     for (int i = tid; i < TT * d; i += NT) {
         const int r = i / d, c = i % d;
         const int tq = t0 + r;
         if (tq >= p.T) continue;
+        const float g = carry(tq);
         const float l = p.row_den[bh * p.T + tq];
-        const float D = l + res[r][2 * d];
+        const float D = l + g * res[r][2 * d];
         const float inv = D != 0.f ? 1.f / D : 0.f;
         const int64_t idx = base + (int64_t)tq * d + c;
         const float2 o = ld(p.layout, p.o_re, p.o_im, idx);
         st(p.layout, p.o_re, p.o_im, idx,
-           make_float2((o.x * l + res[r][c]) * inv, (o.y * l + res[r][d + c]) * inv));
+           make_float2((o.x * l + g * res[r][c]) * inv, (o.y * l + g * res[r][d + c]) * inv));
     }
     __syncthreads();
     for (int r = tid; r < TT; r += NT) {
         const int tq = t0 + r;
-        if (tq < p.T) p.row_den[bh * p.T + tq] += res[r][2 * d];
+        if (tq < p.T) p.row_den[bh * p.T + tq] += carry(tq) * res[r][2 * d];
     }
 }
 
@@ -280,6 +293,7 @@ __global__ __launch_bounds__(NT) void born_step_kernel(LinearProblem p) {
                 fq[i][e] = (a == b ? 1.f : 2.f) * phi(q[a], q[b], a <= b);
             }
         }
+    const float gam = p.decay.on ? decay_pow(p.decay.lg2[bh % p.H], 1) : 1.f;   // the state's scale per token
     float r[SGN];
 #pragma unroll
     for (int s = 0; s < SGN; ++s) {
@@ -306,7 +320,7 @@ __global__ __launch_bounds__(NT) void born_step_kernel(LinearProblem p) {
             if (v * VW >= dd) continue;
 #pragma unroll
             for (int c = 0; c < VW; ++c) {
-                e[i][c] += w * fk[i][c];
+                e[i][c] = fmaf(w, fk[i][c], gam * e[i][c]);
                 r[s] += fq[i][c] * e[i][c];
             }
             if (VW == 4)

@@ -31,6 +31,11 @@
 // (-Im, Re) of the workgroup's four feature rows for the features below the
 // diagonal.  Workgroup: 4 waves, wave w owns feature row a = 4 g + w (64
 // features, two column tiles).
+//
+// Decay (per head gamma): the state build weighs token t of T by
+// gamma^(T-1-t) on the feature operand (a per-stage table of the 64 token
+// factors in LDS; an instance of its own) and an accumulated state by
+// gamma^T; the merge counts the incoming state gamma^(t+1) at token t.
 #include "cattn_internal.h"
 
 namespace cattn {
@@ -240,7 +245,9 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
         if (tq >= T) continue;
         const int64_t rowi = bh * (int64_t)T + tq;
         const float l = p.row_den[rowi];
-        const float Dn = l + den;
+        // decay: the incoming state counts gamma^(t+1) at token t
+        const float gc = p.decay.on ? decay_pow(p.decay.lg2[bh % p.H], tq + 1) : 1.f;
+        const float Dn = l + gc * den;
         const float inv = Dn != 0.f ? 1.f / Dn : 0.f;
         const int64_t ob = base + (int64_t)tq * D;
 #pragma unroll
@@ -256,8 +263,8 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
                 for (int e = 0; e < 4; ++e) {
                     const float o_r = __uint_as_float((e & 1 ? wr[e >> 1] >> 16 : wr[e >> 1] & 0xffffu) << 16);
                     const float o_i = __uint_as_float((e & 1 ? wi[e >> 1] >> 16 : wi[e >> 1] & 0xffffu) << 16);
-                    vr[e] = (o_r * l + acc[s][ti][4 * g + e]) * inv;
-                    vi[e] = (o_i * l + acc[s][ti + 2][4 * g + e]) * inv;
+                    vr[e] = (o_r * l + gc * acc[s][ti][4 * g + e]) * inv;
+                    vi[e] = (o_i * l + gc * acc[s][ti + 2][4 * g + e]) * inv;
                 }
                 *reinterpret_cast<uint2 *>(ore + ob + c0) = make_uint2(pack_bf16x2(vr[0], vr[1]), pack_bf16x2(vr[2], vr[3]));
                 *reinterpret_cast<uint2 *>(oim + ob + c0) = make_uint2(pack_bf16x2(vi[0], vi[1]), pack_bf16x2(vi[2], vi[3]));
@@ -283,6 +290,7 @@ struct StateStage {
     uint32_t KT[D][KROW];                // (Re k, Im k) pairs, [channel][token]
     uint32_t KR[ROWS_PER_WG][KROW];      // (-Im k, Re k) of this workgroup's feature rows
     char V[2][VREGION];                  // value planes, token-major, 16-byte chunks swizzled by token
+    float F[ST_TOK];                     // decay: gamma^(T-1-t) of the stage's tokens
 };
 
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
@@ -300,6 +308,7 @@ __device__ inline void loads_done_barrier() {
     __asm__ __volatile__("" ::: "memory");
 }
 
+template <bool DECAY>
 __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p) {
     __shared__ __align__(16) StateStage st[2];
 
@@ -337,7 +346,9 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
             }
         }
     };
-    auto store_keys = [&](StateStage &S_) {
+    const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
+    auto store_keys = [&](StateStage &S_, int t0) {
+        if (DECAY && tid < ST_TOK) S_.F[tid] = t0 + tid < T ? decay_pow(lg2, T - 1 - (t0 + tid)) : 0.f;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int g = tid + i * NT;
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
     if (nst > 0) {
         issue_values(0, st[0]);
         load_keys(0);
-        store_keys(st[0]);
+        store_keys(st[0], 0);
     }
     loads_done_barrier();
     for (int s = 0; s < nst; ++s) {
@@ -427,6 +438,12 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
             }
             wa[NTILE - 1] = zrow;
             const int tb = (16 * ks + 4 * h) * 4;   // byte offset of this lane's first token in a key row
+            // decay: the factors of the lane's tokens 16 ks + 4 h + e and 16 ks + 8 + 4 h + e
+            float4 fa = make_float4(1.f, 1.f, 1.f, 1.f), fb = fa;
+            if (DECAY) {
+                fa = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 4 * h]);
+                fb = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 8 + 4 * h]);
+            }
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {
                 const u32x4 x0 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb);
@@ -434,21 +451,30 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb);
                 const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb + 32);
                 uint32_t pk[4];
-                pk[0] = pack_bf16x2(dot2(x0[0], kb0[0]), dot2(x0[1], kb0[1]));
-                pk[1] = pack_bf16x2(dot2(x0[2], kb0[2]), dot2(x0[3], kb0[3]));
-                pk[2] = pack_bf16x2(dot2(x1[0], kb1[0]), dot2(x1[1], kb1[1]));
-                pk[3] = pack_bf16x2(dot2(x1[2], kb1[2]), dot2(x1[3], kb1[3]));
+                if (DECAY) {
+                    pk[0] = pack_bf16x2(fa.x * dot2(x0[0], kb0[0]), fa.y * dot2(x0[1], kb0[1]));
+                    pk[1] = pack_bf16x2(fa.z * dot2(x0[2], kb0[2]), fa.w * dot2(x0[3], kb0[3]));
+                    pk[2] = pack_bf16x2(fb.x * dot2(x1[0], kb1[0]), fb.y * dot2(x1[1], kb1[1]));
+                    pk[3] = pack_bf16x2(fb.z * dot2(x1[2], kb1[2]), fb.w * dot2(x1[3], kb1[3]));
+                } else {
+                    pk[0] = pack_bf16x2(dot2(x0[0], kb0[0]), dot2(x0[1], kb0[1]));
+                    pk[1] = pack_bf16x2(dot2(x0[2], kb0[2]), dot2(x0[3], kb0[3]));
+                    pk[2] = pack_bf16x2(dot2(x1[0], kb1[0]), dot2(x1[1], kb1[1]));
+                    pk[3] = pack_bf16x2(dot2(x1[2], kb1[2]), dot2(x1[3], kb1[3]));
+                }
                 const bf16x8 fk = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
                 for (int ti = 0; ti < NTILE; ++ti) acc[ft][ti] = mfma(wa[ti], fk, acc[ft][ti]);
             }
         }
-        if (s + 1 < nst) store_keys(st[(s + 1) & 1]);
+        if (s + 1 < nst) store_keys(st[(s + 1) & 1], (s + 1) * ST_TOK);
         loads_done_barrier();
     }
 
     // write S[n][a * 64 + b]: lane (column b = 32 ft + l32, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4
+    // (an accumulated state first decays by gamma^T)
     float *Sh = p.S + bh * (int64_t)NM * D * D;
+    const float carry = DECAY ? decay_pow(lg2, T) : 1.f;
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
@@ -458,7 +484,7 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 const int n = 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (n >= NM) continue;
                 float *dst = Sh + ((int64_t)n * D + a) * D + 32 * ft + l32;
-                *dst = p.accumulate ? *dst + acc[ft][ti][r] : acc[ft][ti][r];
+                *dst = p.accumulate ? carry * *dst + acc[ft][ti][r] : acc[ft][ti][r];
             }
 }
 
@@ -483,7 +509,8 @@ namespace cattn {
 hipError_t launch_born_state_bf16_d64(const LinearProblem &p) {
     const int64_t blocks = (int64_t)p.BH * (D / ROWS_PER_WG);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_state_bf16_d64_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
+    auto kern = p.decay.on ? born_state_bf16_d64_kernel<true> : born_state_bf16_d64_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
     return hipGetLastError();
 }
 

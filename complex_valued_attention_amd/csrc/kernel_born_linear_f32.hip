@@ -78,7 +78,10 @@ __device__ inline void st2(void *re, void *im, int64_t i, float2 v) {
     }
 }
 
-template <int D, int LAY>
+// DECAY: token t of T weighs gamma^(T-1-t) (on the feature operand, so the
+// value rows and the constant row of Z alike) and an accumulated state
+// gamma^T.
+template <int D, int LAY, bool DECAY>
 __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int groups) {
     using C = LCfg<D>;
     __shared__ __align__(16) StateSmem<D> sm;
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
 #pragma unroll
         for (int ft = 0; ft < SFT; ++ft) acc[ti][ft] = f32x16{};
     const float zrow = l32 == 0 ? 1.f : 0.f;   // Z tile: the constant 1 in its first row
+    const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
 
     // a stage's (k, v) pairs go global -> registers one stage ahead, then
     // registers -> LDS once the previous stage is consumed
@@ -146,11 +150,14 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
 #pragma unroll
             for (int ti = 0; ti < C::NTI - 1; ++ti) w[ti] = sm.W[t][32 * ti + l32];
             w[C::NTI - 1] = zrow;
+            // tokens past T have zero features; clamp their exponent
+            const float fdec = DECAY ? decay_pow(lg2, max(T - 1 - (t0 + t), 0)) : 1.f;
 #pragma unroll
             for (int ft = 0; ft < SFT; ++ft) {
                 const float2 x = upper[ft] ? sm.Kp[t][fa[ft]] : sm.Kr[t][fa[ft]];
                 const float2 kb = sm.Kp[t][fb[ft]];
-                const float phi = x.x * kb.x + x.y * kb.y;
+                float phi = x.x * kb.x + x.y * kb.y;
+                if (DECAY) phi *= fdec;
 #pragma unroll
                 for (int ti = 0; ti < C::NTI; ++ti) mfma(w[ti], phi, acc[ti][ft]);
             }
@@ -159,6 +166,7 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
 
     // write S[n][f]: lane (feature column l32, half h) holds rows n = 32 ti + 8 (r/4) + 4 h + r % 4
     float *Sh = p.S + bh * (int64_t)C::NM * C::F;
+    const float carry = DECAY ? decay_pow(lg2, T) : 1.f;
 #pragma unroll
     for (int ti = 0; ti < C::NTI; ++ti)
 #pragma unroll
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(NT) void born_state_f32_kernel(LinearProblem p, int
                 const int n = 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (n >= C::NM) continue;
                 float *dst = Sh + (int64_t)n * C::F + f0 + 32 * ft + l32;
-                *dst = p.accumulate ? *dst + acc[ti][ft][r] : acc[ti][ft][r];
+                *dst = p.accumulate ? carry * *dst + acc[ti][ft][r] : acc[ti][ft][r];
             }
 }
 
@@ -316,7 +324,9 @@ __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int
     if (tq >= T) return;
     const int64_t rowi = bh * (int64_t)T + tq;
     const float l = p.row_den[rowi];
-    const float Dn = l + den;
+    // decay: the incoming state counts gamma^(t+1) at token t
+    const float gc = p.decay.on ? decay_pow(p.decay.lg2[bh % p.H], tq + 1) : 1.f;
+    const float Dn = l + gc * den;
     const float inv = Dn != 0.f ? 1.f / Dn : 0.f;
     const int64_t orow = base + (int64_t)tq * D;
 #pragma unroll
@@ -328,7 +338,8 @@ __global__ __launch_bounds__(NT) void born_merge_f32_kernel(LinearProblem p, int
             // the imaginary row d + c sits D / 32 tiles (D >= 32) or 16 rows (D = 16) further on
             const float im = D >= 32 ? acc[ti + D / 32][r] : acc[ti][r + 8];
             const float2 o = ld2<LAY>(p.o_re, p.o_im, orow + c);
-            st2<LAY>(p.o_re, p.o_im, orow + c, make_float2((o.x * l + acc[ti][r]) * inv, (o.y * l + im) * inv));
+            st2<LAY>(p.o_re, p.o_im, orow + c,
+                     make_float2((o.x * l + gc * acc[ti][r]) * inv, (o.y * l + gc * im) * inv));
         }
     if (h == 0) p.row_den[rowi] = Dn;
 }
@@ -338,7 +349,8 @@ hipError_t launch_state_d(const LinearProblem &p) {
     const int groups = LCfg<D>::F / (32 * NW * SFT);
     const int64_t blocks = (int64_t)p.BH * groups;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((born_state_f32_kernel<D, LAY>), dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, groups);
+    auto kern = p.decay.on ? born_state_f32_kernel<D, LAY, true> : born_state_f32_kernel<D, LAY, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, groups);
     return hipGetLastError();
 }
 

@@ -562,7 +562,7 @@ hipError_t launch_d(const BwdProblem &p) {
 bool supports_bwd_f32_mfma(const BwdProblem &p) {
     // complex64, or bf16 planes widened to fp32 on load (bf16 Born at width 64
     // has its own bf16 matrix-core pair, tried first)
-    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64);
+    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64) && !p.decay.on;
 }
 
 hipError_t launch_bwd_f32_mfma(const BwdProblem &p) {

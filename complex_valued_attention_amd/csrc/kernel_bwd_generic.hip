@@ -9,6 +9,8 @@
 // S = Q K^H, w = |S|^2, l the forward's row denominators, delta = Re(G^H O)
 // per row and D = (Re(G^H V) - delta) / l on the causal support:
 //     dV = (w / l)^T G,   dQ = (2 D o S) K,   dK = (2 D o S)^H Q.
+// Under a per-head decay every w and D on the causal support carries the
+// factor gamma^(k - j) of the forward's weight.
 // PCT ("Complex-valued Phase-Coherent Transformers", section 1 and Appendix
 // D.2), with qh, kh the unit-normalised rows, s = sqrt(d_h) Re(qh kh^H),
 // w = sigmoid(s + b), ds = Re(G^H V) w (1 - w):
@@ -155,7 +157,7 @@ __device__ inline void load_key_tile(const BwdProblem &p, BwdSmem<DP> &s, int64_
 // Returns this thread's sum of ds over its pairs (PCT bias gradient; the
 // pairs of one thread share a query row).
 template <int DP>
-__device__ inline float pair_tile(const BwdProblem &p, BwdSmem<DP> &s, int q0, int k0) {
+__device__ inline float pair_tile(const BwdProblem &p, BwdSmem<DP> &s, int q0, int k0, int bh) {
     constexpr int B = BwdTile<DP>::B, PPT = BwdTile<DP>::PPT;
     constexpr int TPR = B / PPT;   // threads per query row in the pair tile
     const int tid = threadIdx.x;
@@ -191,7 +193,9 @@ __device__ inline float pair_tile(const BwdProblem &p, BwdSmem<DP> &s, int q0, i
         float2 pp = make_float2(0.f, 0.f);
         if (live) {
             if (p.op == OP_BORN) {
-                const float inv = s.qa[r];
+                // 1 / l, times gamma^(k - j) under the decay: both the weight and D carry it
+                float inv = s.qa[r];
+                if (p.decay.on) inv *= decay_pow(p.decay.lg2[bh % p.H], qi - kj);
                 const float w = S[i].x * S[i].x + S[i].y * S[i].y;
                 a = w * inv;
                 const float D2 = 2.f * (E[i] - s.qb[r]) * inv;
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdProblem p) {
         __syncthreads();   // previous tile fully consumed
         load_query_tile<DP>(p, s, base, q0);
         __syncthreads();
-        pair_tile<DP>(p, s, q0, k0);
+        pair_tile<DP>(p, s, q0, k0, bh);
         __syncthreads();
 #pragma unroll 2
         for (int r = 0; r < B; ++r) {
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdProblem p) {
         __syncthreads();
         load_key_tile<DP>(p, s, base, k0);
         __syncthreads();
-        dsum += pair_tile<DP>(p, s, q0, k0);
+        dsum += pair_tile<DP>(p, s, q0, k0, bh);
         __syncthreads();
 #pragma unroll 2
         for (int c = 0; c < B; ++c) {

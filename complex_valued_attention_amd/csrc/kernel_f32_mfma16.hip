@@ -47,7 +47,13 @@
 // lane writes its key row's 16-byte chunks c + 8 i, rotated by 7 chunks on odd
 // key rows, so the 16 lanes of one write, two key rows, cover all 64 banks
 // (widths 32 and 64; at 16 the writes stay two-way).
+//
+// Born options.  A per-head decay multiplies each weight by gamma^(k - j),
+// formed per weight as exp2((k - j) log2 gamma) (the diagonal block's masked
+// weights are zeroed after it).  A rotary Q is rotated as its operands are
+// loaded, with the arithmetic of the rotary pass (rotary_math.h).
 #include "cattn_internal.h"
+#include "rotary_math.h"
 
 namespace cattn {
 namespace {
@@ -114,7 +120,9 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 // bf16 planes per operand, widened to the same interleaved fp32 rows while K
 // and V are staged and Q is loaded, and rounded back to bf16 planes on store
 // (round to nearest even); all arithmetic stays fp32.
-template <int D, int OP, int LAY>
+// OPT: the Born options (decay, rotary Q) may be on; a separate instance, so
+// the plain kernel carries none of their registers.
+template <int D, int OP, int LAY, bool OPT>
 __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb, int nwork) {
     using C = Cfg16<D>;
     static_assert(C::CPT >= 1, "head width too small for this staging split");
@@ -143,6 +151,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     const int64_t hq = head_offset(p.sq, bh, p.H), hk = head_offset(p.sk, bh, p.H);
     const int64_t hv = head_offset(p.sv, bh, p.H), ho = head_offset(p.so, bh, p.H);
     const int64_t rsq = p.sq.t, rsk = p.sk.t, rsv = p.sv.t, rso = p.so.t;
+    const float lg2 = OPT && p.decay.on ? p.decay.lg2[bh % p.H] : 0.f;
     const float *qg = reinterpret_cast<const float *>(p.q_re) + 2 * hq;
     const float *kg = reinterpret_cast<const float *>(p.k_re) + 2 * hk;
     const float *vg = reinterpret_cast<const float *>(p.v_re) + 2 * hv;
@@ -244,6 +253,21 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
                 else
                     x[i] = widen2(bq_re, bq_im, (int64_t)qr * rsq + g * (C::KQ / 2) + 2 * i);
             }
+        }
+        if (OPT && p.rot && ok && qr < T) {
+            // complex channels g KQ / 2 + 2 i + e of query qr
+            const double pos = (double)(p.rot_pos0 + qr);
+#pragma unroll
+            for (int i = 0; i < C::KQ / 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float c, sn;
+                    rotary_phase(pos, rotary_theta(g * (C::KQ / 2) + 2 * i + e, p.rot_log_base, D), c, sn);
+                    float yr, yi;
+                    rotary_apply(x[i][2 * e], x[i][2 * e + 1], c, sn, yr, yi);
+                    x[i][2 * e] = yr;
+                    x[i][2 * e + 1] = yi;
+                }
         }
 #pragma unroll
         for (int i = 0; i < C::KQ / 4; ++i) {
@@ -391,6 +415,10 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             if (OP == OP_BORN) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) w[r] = sr[r] * sr[r] + si[r] * si[r];
+                if (OPT && p.decay.on) {   // gamma^(k - j); negative distances only on masked keys
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] *= decay_pow(lg2, max(qt_cur + j16 - kb0 - 4 * g - r, 0));
+                }
             } else {
                 const f32x4 rkv = *reinterpret_cast<const f32x4 *>(rk + 16 * sb + 4 * g);
 #pragma unroll
@@ -465,10 +493,10 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     if (!helping && live_cur) write_out(qt_cur);
 }
 
-template <int D, int OP, int LAY>
+template <int D, int OP, int LAY, bool OPT = false>
 hipError_t launch_cfg16(const Problem &p) {
     using C = Cfg16<D>;
-    auto kern = attn_f32_mfma16_kernel<D, OP, LAY>;
+    auto kern = attn_f32_mfma16_kernel<D, OP, LAY, OPT>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -484,7 +512,10 @@ template <int D, int LAY>
 hipError_t launch_op16(const Problem &p) {
     switch (p.op) {
         case OP_BORN:   // bf16 Born runs on the bf16 matrix-core kernels
-            if constexpr (LAY == LAYOUT_C64) return launch_cfg16<D, OP_BORN, LAY>(p);
+            if constexpr (LAY == LAYOUT_C64) {
+                if (p.decay.on || p.rot) return launch_cfg16<D, OP_BORN, LAY, true>(p);
+                return launch_cfg16<D, OP_BORN, LAY>(p);
+            }
             return hipErrorNotSupported;
         case OP_PCT: return launch_cfg16<D, OP_PCT, LAY>(p);
         case OP_PCT_SOFTMAX: return launch_cfg16<D, OP_PCT_SOFTMAX, LAY>(p);

@@ -6,7 +6,13 @@
 // BQ query rows of one (batch, head); key/value tiles of BK rows are staged
 // in LDS as fp32 (re, im) pairs, the BQ x BK weights are formed in LDS, and
 // each thread accumulates a few output components in registers.
+//
+// Born options: the per-head decay multiplies each causal weight by
+// gamma_h^(k - j); a rotary Q is rotated as it is staged (the arithmetic of
+// the rotary pass, rounded to bf16 for bf16 planes as that pass would store
+// it).
 #include "cattn_internal.h"
+#include "rotary_math.h"
 
 namespace cattn {
 namespace {
@@ -71,7 +77,16 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
     for (int i = tid; i < BQ * DP; i += NT) {
         const int r = i / DP, m = i % DP;
         float2 x = make_float2(0.f, 0.f);
-        if (m < d && q0 + r < p.T) x = load_c(p.layout, p.q_re, p.q_im, bq + (int64_t)(q0 + r) * p.sq.t + m);
+        if (m < d && q0 + r < p.T) {
+            x = load_c(p.layout, p.q_re, p.q_im, bq + (int64_t)(q0 + r) * p.sq.t + m);
+            if (p.rot) {
+                float c, sn;
+                rotary_phase((double)(p.rot_pos0 + q0 + r), rotary_theta(m, p.rot_log_base, d), c, sn);
+                rotary_apply(x.x, x.y, c, sn, x.x, x.y);
+                if (p.layout == LAYOUT_BF16)
+                    x = make_float2(bf16_bits_to_f32(rotary_bf16(x.x)), bf16_bits_to_f32(rotary_bf16(x.y)));
+            }
+        }
         Qs[r][m] = x;
     }
     __syncthreads();
@@ -122,6 +137,7 @@ __global__ __launch_bounds__(NT) void generic_fwd_kernel(Problem p) {
             float w;
             if (!pct) {
                 w = sr * sr + si * si;
+                if (p.decay.on && valid) w *= decay_pow(p.decay.lg2[bh % p.H], qi - kj);
             } else {
                 const float x = sr * rq[r] * rk[c];   // sqrt(d_h) Re<qh, kh>, |x| <= sqrt(d_h)
                 if (p.op == OP_PCT) {

@@ -4,33 +4,16 @@
 //
 // An elementwise pass bound by HBM bandwidth.  The phase depends on the
 // position and the channel only, so each thread forms it once and applies it
-// to a chunk of heads.
-// The angle (p0 + t) theta_m is formed and reduced modulo 2 pi in fp64: at
-// t ~ 1e4 an fp32 product would already carry ~1e-3 rad of error.  The
-// reduced angle lies in [-pi, pi], where the fp32 hardware sine and cosine are
-// accurate to ~1e-6.  In place (y == x) is allowed: every element is read and
-// written by one thread.
+// to a chunk of heads.  The phase arithmetic (angle reduced in fp64) lives in
+// rotary_math.h, shared with the forward kernels that rotate Q at load.  In
+// place (y == x) is allowed: every element is read and written by one thread.
 #include "cattn_internal.h"
+#include "rotary_math.h"
 
 namespace cattn {
 namespace {
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-
-__device__ inline uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// cos and sin of (p0 + t) theta, reduced in fp64
-__device__ inline void phase(double pos, double theta, float &c, float &s) {
-    const double a = pos * theta;
-    const double k = rint(a * 0.15915494309189535);                  // a / (2 pi), nearest integer
-    const double r = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, a));   // a - 2 pi k
-    __sincosf((float)r, &s, &c);
-}
 
 // VEC: channels per thread (2 complex64 values = 16 bytes; 8 bf16 per plane =
 // 16 bytes; 1 = scalar).  Thread g of a head covers row t = g / L, channels
@@ -47,8 +30,8 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryProblem p, int L, int
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         const int m = mg * VEC + e;
-        const double theta = m < p.d ? exp(-(double)m * p.log_base / (double)p.d) : 0.0;
-        phase(pos, theta, c[e], sn[e]);
+        const double theta = m < p.d ? rotary_theta(m, p.log_base, p.d) : 0.0;
+        rotary_phase(pos, theta, c[e], sn[e]);
     }
     const int64_t bh0 = (int64_t)blockIdx.y * hc;
     const int64_t bh1 = bh0 + hc < p.BH ? bh0 + hc : p.BH;
@@ -81,10 +64,7 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryProblem p, int L, int
                 if (u >= nh) break;
                 float yv[2 * VEC];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    yv[2 * e] = xv[u][2 * e] * c[e] - xv[u][2 * e + 1] * sn[e];
-                    yv[2 * e + 1] = xv[u][2 * e] * sn[e] + xv[u][2 * e + 1] * c[e];
-                }
+                for (int e = 0; e < VEC; ++e) rotary_apply(xv[u][2 * e], xv[u][2 * e + 1], c[e], sn[e], yv[2 * e], yv[2 * e + 1]);
                 float2 *dst = reinterpret_cast<float2 *>(p.y_re) + (b0 + u) * head + off;
                 if (VEC == 2) {
                     *reinterpret_cast<float4 *>(dst) = make_float4(yv[0], yv[1], yv[2], yv[3]);
@@ -123,9 +103,10 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryProblem p, int L, int
                 uint16_t yr[VEC], yi[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float a = bf16_to_f32(xr[u][e]), b = bf16_to_f32(xi[u][e]);
-                    yr[e] = f32_to_bf16(a * c[e] - b * sn[e]);
-                    yi[e] = f32_to_bf16(a * sn[e] + b * c[e]);
+                    float a, b;
+                    rotary_apply(bf16_to_f32(xr[u][e]), bf16_to_f32(xi[u][e]), c[e], sn[e], a, b);
+                    yr[e] = rotary_bf16(a);
+                    yi[e] = rotary_bf16(b);
                 }
                 uint16_t *dr = reinterpret_cast<uint16_t *>(p.y_re) + (b0 + u) * head + off;
                 uint16_t *di = reinterpret_cast<uint16_t *>(p.y_im) + (b0 + u) * head + off;

@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "BENCH_WORKLOAD", "make_inputs", "make_grad", "random_qkv",
-    "round_to_bf16_bits", "bf16_bits_to_f64", "attention_flops",
+    "round_to_bf16_bits", "bf16_bits_to_f64", "attention_flops", "decay_gammas",
 ]
 
 
@@ -79,6 +79,16 @@ WORKLOADS = {
     ]
 }
 BENCH_WORKLOAD = "born_causal_bf16_b8h16t4096d64_rotary"
+
+
+def decay_gammas(H: int) -> np.ndarray:
+    """Per-head decay values for the decayed Born workloads: a fixed geometric
+    schedule gamma_h = 1 - 2^-(5 + 8 h / (H - 1)), from 0.969 (a memory of
+    ~32 tokens) on head 0 to 0.99988 (~8192 tokens) on the last head, so the
+    heads span short to long ranges.  The pages fix no values."""
+    if H <= 1:
+        return np.array([1.0 - 2.0 ** -5])[:H]
+    return 1.0 - 2.0 ** -(5.0 + 8.0 * np.arange(H) / (H - 1))
 
 
 def attention_flops(T: int, d_h: int, causal: bool, heads: int = 1) -> float:

@@ -62,9 +62,11 @@ typedef enum {
     CATTN_E_LAYOUT = 3,      /* unknown layout value */
     CATTN_E_ALIGN = 4,       /* a pointer is misaligned: forward calls need element alignment, other calls 16 bytes */
     CATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
-    CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 (1..64 for the carried-state calls) */
+    CATTN_E_UNSUPPORTED = 6, /* d_h outside 1..128 (1..64 for the carried-state calls), or H above
+                                CATTN_MAX_DECAY_HEADS with a decay table */
     CATTN_E_LAUNCH = 7,      /* the HIP kernel launch failed */
-    CATTN_E_ARG = 8          /* a scalar out of range: eps, bias, a gate parameter, rotary base or position; or an unknown gate */
+    CATTN_E_ARG = 8          /* a scalar out of range: eps, bias, a gate parameter, rotary base or position,
+                                a decay value; decay on a non-causal call; or an unknown gate */
 } cattn_status;
 
 /* Gates on the PCT score path ("Complex-valued Phase-Coherent Transformers",
@@ -111,6 +113,44 @@ typedef struct {
     cattn_stride q, k, v, o;
 } cattn_strides;
 
+/* Largest head count H for which a per-head decay table is accepted. */
+#define CATTN_MAX_DECAY_HEADS 256
+
+/*
+ * Per-head decay (a reading of "Show HN: CNET", BornAttention: a fixed
+ * per-head decay that multiplies the score, the page's best fix for long
+ * contexts, run together with the linear mode; the page's formula is lost in
+ * its text).  For causal attention and gamma_h in (0, 1] the weight of key j
+ * for query k of head h becomes
+ *     w[k,j] = gamma_h^(k-j) |S[k,j]|^2,   j <= k,
+ * the one fixed per-head factor that a carried state reproduces by
+ * Z <- gamma_h Z + k k^H (cattn_born_state, _merge, _step below).  gamma_h = 1
+ * is plain Born attention.
+ * A decay table is a HOST array of H floats, read during the call and not
+ * kept; NULL means no decay.  Errors: CATTN_E_ARG if the call is not causal
+ * or a value lies outside (0, 1] (NaN included); CATTN_E_UNSUPPORTED if
+ * H > CATTN_MAX_DECAY_HEADS.
+ */
+
+/*
+ * Options of cattn_born_fwd (NULL: none of them).
+ *   decay         NULL or a decay table (above).
+ *   rotary_base   0: Q is used as given.  > 0 and finite: each query row t
+ *                 is rotated as it is loaded, q[t,m] exp(i (rotary_pos0 + t)
+ *                 theta_m) with theta_m = rotary_base^(-m/d_h), the
+ *                 arithmetic of cattn_rotary ("Show HN: CNET", RotaryEmbed);
+ *                 K is taken as given, i.e. already rotated (as a key cache
+ *                 holds it), so this replaces a cattn_rotary pass over Q.
+ *   rotary_pos0   absolute position of token 0, 0 <= rotary_pos0 <= 2^40.
+ * Errors: CATTN_E_ARG for a negative or non-finite rotary_base or a
+ * rotary_pos0 out of range.
+ */
+typedef struct {
+    const float *decay;
+    float rotary_base;
+    int64_t rotary_pos0;
+} cattn_born_opts;
+
 /*
  * Born-rule attention forward (definition above).
  *   layout        CATTN_LAYOUT_C64 or CATTN_LAYOUT_BF16_PLANES.
@@ -134,6 +174,7 @@ typedef struct {
  *   eps           added to each row denominator; >= 0 and finite.
  *   row_den       optional (NULL allowed) device float[B*H*T]: receives each
  *                 row's denominator sum_j w + eps.
+ *   opts          NULL or the decay and rotary options (cattn_born_opts).
  *   stream        hipStream_t to enqueue on.
  */
 cattn_status cattn_born_fwd(int layout,
@@ -143,7 +184,8 @@ cattn_status cattn_born_fwd(int layout,
                             void *o_re, void *o_im,
                             int64_t B, int64_t H, int64_t T, int64_t d_h,
                             const cattn_strides *strides,
-                            int causal, float eps, float *row_den, void *stream);
+                            int causal, float eps, float *row_den,
+                            const cattn_born_opts *opts, void *stream);
 
 /*
  * Phase-coherent (PCT) attention forward (definition above).  Arguments as
@@ -208,6 +250,9 @@ cattn_status cattn_pct_gate_fwd(int layout,
  *   g_*        the incoming gradient G (same layout).
  *   row_den    Born: device float[B*H*T], the forward's row denominators
  *              (sum_j w + eps), required.
+ *   decay      Born: NULL or the forward's decay table (see "Per-head
+ *              decay"); every w[k,j] above, in dV and in D alike, then
+ *              carries the factor gamma_h^(k-j).
  *   dq_*, dk_*, dv_*  outputs (same layout), fully overwritten.
  *   db_rows    PCT: optional (NULL allowed) device float[B*H*T], receives
  *              sum_j ds[i,j] per query row; their sum is dL/d(bias).
@@ -227,7 +272,7 @@ cattn_status cattn_born_bwd(int layout,
                             void *dk_re, void *dk_im,
                             void *dv_re, void *dv_im,
                             int64_t B, int64_t H, int64_t T, int64_t d_h,
-                            int causal, void *stream);
+                            int causal, const float *decay, void *stream);
 
 cattn_status cattn_pct_bwd(int layout,
                            const void *q_re, const void *q_im,
@@ -291,19 +336,30 @@ cattn_status cattn_rotary(int layout,
  *     (k, v) to the state in place, then writes o and row_den[b*H + h] =
  *     q^H Z q + eps.  For bf16 the numerator is rounded once to bf16 before
  *     the division (a second rounding of o).
+ * Decay: each of these calls takes a decay table (NULL: none; see "Per-head
+ *     decay"), under which every token first scales the state by gamma_h and
+ *     then adds its own terms, so the state after token t holds
+ *     sum_{j <= t} gamma_h^(t-j) (...):
+ *     cattn_born_state  S <- gamma_h^T S + sum_t gamma_h^(T-1-t) (terms of t)
+ *                       (with accumulate = 0 the old contents count as 0);
+ *     cattn_born_merge  the incoming state counts gamma_h^(t+1) at token t:
+ *                       O <- (O l + g q^H M q) / (l + g q^H Z q), g = gamma_h^(t+1),
+ *                       which needs O and l from cattn_born_fwd with the same table;
+ *     cattn_born_step   S <- gamma_h S + (terms of the token), then the read-out.
  * Written buffers must not overlap any other buffer of the call.
  */
 cattn_status cattn_born_state(int layout,
                               const void *k_re, const void *k_im,
                               const void *v_re, const void *v_im,
                               int64_t B, int64_t H, int64_t T, int64_t d_h,
-                              float *S, int accumulate, void *stream);
+                              float *S, int accumulate, const float *decay, void *stream);
 
 cattn_status cattn_born_merge(int layout,
                               const void *q_re, const void *q_im,
                               const float *S,
                               void *o_re, void *o_im, float *row_den,
-                              int64_t B, int64_t H, int64_t T, int64_t d_h, void *stream);
+                              int64_t B, int64_t H, int64_t T, int64_t d_h,
+                              const float *decay, void *stream);
 
 cattn_status cattn_born_step(int layout,
                              const void *q_re, const void *q_im,
@@ -311,14 +367,16 @@ cattn_status cattn_born_step(int layout,
                              const void *v_re, const void *v_im,
                              void *o_re, void *o_im,
                              float *S, float *row_den,
-                             int64_t B, int64_t H, int64_t d_h, float eps, void *stream);
+                             int64_t B, int64_t H, int64_t d_h, float eps,
+                             const float *decay, void *stream);
 
 /* Static, NUL-terminated description of a status value (never NULL; an
  * unknown value gives "unknown status"). */
 const char *cattn_status_str(cattn_status status);
 
-/* ABI version of this header: 7 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state,
-   6 its packed real layout, 7 strided operands in the forward calls). */
+/* ABI version of this header: 8 (2 added the backward, 3 the PCT gates, 4 rotary, 5 the carried state,
+   6 its packed real layout, 7 strided operands in the forward calls, 8 per-head decay and rotary Q
+   at load). */
 int cattn_abi_version(void);
 
 #ifdef __cplusplus

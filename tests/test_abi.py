@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = cattn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.cattn_abi_version() == 7
+    assert L.cattn_abi_version() == 8
 
 
 def test_status_strings():
@@ -47,9 +47,9 @@ def strides(q=(0, 0, 0), k=(0, 0, 0), v=(0, 0, 0), o=(0, 0, 0)):
     return ctypes.byref(cattn.Strides(cattn.Stride(*q), cattn.Stride(*k), cattn.Stride(*v), cattn.Stride(*o)))
 
 
-def born(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=1, eps=0.0, row_den=None, st=None):
+def born(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=1, eps=0.0, row_den=None, st=None, opts=None):
     q = ptrs if ptrs is not None else ([P[0], None, P[1], None, P[2], None, P[3], None] if layout == 0 else P)
-    return cattn.lib().cattn_born_fwd(layout, *q, B, H, T, d, st, causal, eps, row_den, None)
+    return cattn.lib().cattn_born_fwd(layout, *q, B, H, T, d, st, causal, eps, row_den, opts, None)
 
 
 def pct(layout=0, ptrs=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0, st=None):
@@ -171,14 +171,14 @@ def test_python_binding_rejects_bad_tensors():
 Q = [0x100000 * (i + 20) for i in range(16)]
 
 
-def born_b(layout=0, ins=None, outs=None, row_den=Q[15], B=1, H=1, T=8, d=4, causal=1):
+def born_b(layout=0, ins=None, outs=None, row_den=Q[15], B=1, H=1, T=8, d=4, causal=1, decay=None):
     if ins is None:   # q, k, v, o, g as (re, im) pairs
         ins = [(Q[i], None) for i in range(5)] if layout == 0 else [(Q[i], Q[i + 5]) for i in range(5)]
     if outs is None:  # dq, dk, dv
         outs = [(Q[10 + i], None if layout == 0 else 0x100000 * (41 + i)) for i in range(3)]
     flat_in = [x for pair in ins for x in pair]
     flat_out = [x for pair in outs for x in pair]
-    return cattn.lib().cattn_born_bwd(layout, *flat_in, row_den, *flat_out, B, H, T, d, causal, None)
+    return cattn.lib().cattn_born_bwd(layout, *flat_in, row_den, *flat_out, B, H, T, d, causal, decay, None)
 
 
 def pct_b(layout=0, ins=None, outs=None, db_rows=None, B=1, H=1, T=8, d=4, causal=0, bias=0.0):
@@ -277,20 +277,73 @@ S = [0x1000000 * (i + 2) for i in range(10)]   # far apart: state buffers are la
 def test_linear_argument_errors():
     L = cattn.lib()
     # state build: d_h above 64 is unsupported for the carried state
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 65, S[2], 0, None) == 6
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, None, 0, None) == 1
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[2] + 8, 0, None) == 4
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[0] + 16, 0, None) == 5   # state over k
-    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 0, 4, None, 1, None) == 0        # empty
-    assert L.cattn_born_state(0, None, None, None, None, 1, 1, 0, 4, None, 0, None) == 1        # zeroing needs S
-    assert L.cattn_born_state(0, None, None, None, None, 0, 1, 0, 4, None, 0, None) == 0        # no heads
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 65, S[2], 0, None, None) == 6
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, None, 0, None, None) == 1
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[2] + 8, 0, None, None) == 4
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 8, 4, S[0] + 16, 0, None, None) == 5   # state over k
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 1, 0, 4, None, 1, None, None) == 0        # empty
+    assert L.cattn_born_state(0, None, None, None, None, 1, 1, 0, 4, None, 0, None, None) == 1        # zeroing needs S
+    assert L.cattn_born_state(0, None, None, None, None, 0, 1, 0, 4, None, 0, None, None) == 0        # no heads
     # merge: the written output and row_den must not overlap the state
-    assert L.cattn_born_merge(0, S[0], None, S[1], S[1], None, S[4], 1, 1, 8, 4, None) == 5
-    assert L.cattn_born_merge(0, S[0], None, S[1], S[3], None, None, 1, 1, 8, 4, None) == 1
+    assert L.cattn_born_merge(0, S[0], None, S[1], S[1], None, S[4], 1, 1, 8, 4, None, None) == 5
+    assert L.cattn_born_merge(0, S[0], None, S[1], S[3], None, None, 1, 1, 8, 4, None, None) == 1
     # step: eps checked first; o over q
     assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[3], None, S[4], S[6], 1, 1, 4,
-                             -1.0, None) == 8
+                             -1.0, None, None) == 8
     assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[0], None, S[4], S[6], 1, 1, 4,
-                             0.0, None) == 5
+                             0.0, None, None) == 5
     assert L.cattn_born_step(1, S[0], None, S[1], S[7], S[2], S[8], S[3], S[9], S[4], S[6], 1, 1, 4,
-                             0.0, None) == 1   # bf16 needs both planes of q
+                             0.0, None, None) == 1   # bf16 needs both planes of q
+
+
+def _floats(*v):
+    return (ctypes.c_float * len(v))(*v)
+
+
+def _opts(decay=None, base=0.0, pos0=0):
+    d = None if decay is None else ctypes.cast(decay, ctypes.POINTER(ctypes.c_float))
+    return ctypes.byref(cattn.BornOpts(d, base, pos0))
+
+
+def test_born_options_validation():
+    # every case is valid but for its options, so each must stop there, before any launch
+    H = 3
+    ok = _floats(0.5, 1.0, 0.99)
+    for bad in ((0.5, 0.0, 0.9), (0.5, -0.1, 0.9), (1.0, 1.5, 0.9), (float("nan"), 0.5, 0.5),
+                (float("inf"), 0.5, 0.5)):
+        assert born(H=H, opts=_opts(_floats(*bad))) == 8, bad
+    assert born(H=H, causal=0, opts=_opts(ok)) == 8                 # decay needs causal attention
+    assert born(H=257, opts=_opts(_floats(*([0.5] * 257)))) == 6      # more heads than a table holds
+    assert born(H=H, opts=_opts(base=-1.0)) == 8
+    assert born(H=H, opts=_opts(base=float("nan"))) == 8
+    assert born(H=H, opts=_opts(base=float("inf"))) == 8
+    assert born(H=H, opts=_opts(base=10000.0, pos0=-1)) == 8
+    assert born(H=H, opts=_opts(base=10000.0, pos0=(1 << 40) + 1)) == 8
+    assert born(B=0, H=H, opts=_opts(_floats(0.5, 2.0, 0.5))) == 8    # options are checked on empty calls too
+    assert born(B=0, H=H, opts=_opts(ok, base=10000.0)) == 0        # empty and valid: nothing to do
+    # the argument checks of the call itself come first
+    assert born(H=H, d=0, opts=_opts(_floats(0.5, 2.0, 0.5))) == 6
+
+
+def test_decay_validation_backward_and_state():
+    L = cattn.lib()
+    bad = _floats(0.5, 0.0)
+    assert born_b(H=2, decay=bad) == 8
+    assert born_b(H=2, causal=0, decay=_floats(0.5, 0.5)) == 8
+    assert born_b(H=300, decay=_floats(*([0.5] * 300))) == 6
+    # carried state: a bad table is refused before anything else is looked at
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 2, 8, 4, S[2], 0, bad, None) == 8
+    assert L.cattn_born_merge(0, S[0], None, S[1], S[3], None, S[4], 1, 2, 8, 4, bad, None) == 8
+    assert L.cattn_born_step(0, S[0], None, S[1], None, S[2], None, S[3], None, S[4], S[6], 1, 2, 4, 0.0, bad,
+                             None) == 8
+    assert L.cattn_born_state(0, S[0], None, S[1], None, 1, 257, 8, 4, S[2], 0, _floats(*([0.5] * 257)),
+                              None) == 6
+
+
+def test_binding_decay_table():
+    arr = cattn._decay([0.5, 0.25], 2)
+    assert list(arr) == [0.5, 0.25]
+    assert list(cattn._decay(0.75, 3)) == [0.75, 0.75, 0.75]
+    assert cattn._decay(None, 4) is None
+    with pytest.raises(ValueError):
+        cattn._decay([0.5], 2)

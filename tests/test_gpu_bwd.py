@@ -69,11 +69,16 @@ def run_oracle_bwd(w, inp, grad, bias=0.0, eps=0.0, heads=None):
     return oracle.pct_attention_bwd(q, k, v, g, causal=w.causal, bias=bias)
 
 
-def term_scales(op, q, k, v, g, causal, bias=0.0, eps=0.0):
+def term_scales(op, q, k, v, g, causal, bias=0.0, eps=0.0, decay=None):
     """Per-row magnitude (max modulus) of the terms each gradient row is formed from,
-    before they cancel: (dq, dk, dv) arrays of shape [..., T]."""
+    before they cancel: (dq, dk, dv) arrays of shape [..., T].  decay: per-head
+    gammas [H] of q's head axis (Born, causal)."""
     T, d = q.shape[-2], q.shape[-1]
     mask = np.tril(np.ones((T, T))) if causal else np.ones((T, T))
+    if decay is not None:
+        dist = np.arange(T)[:, None] - np.arange(T)[None, :]
+        gam = np.asarray(decay, dtype=np.float64)[:, None, None]
+        mask = np.where(dist >= 0, gam ** np.maximum(dist, 0), 0.0)     # [H, T, T]
     tr = lambda x: np.swapaxes(x, -1, -2)
     amax = lambda x: np.abs(x).max(axis=-1)
     E = (g.conj() @ tr(v)).real * mask
