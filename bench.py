@@ -44,6 +44,11 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # name -> {"source": kernel file, "sha256": its hash when the counters were
     # taken, "bytes": FETCH_SIZE + WRITE_SIZE per launch, scaled by the copy probe}
+    "born_causal_bf16_b8h16t4096d64_rotary": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_d64.hip",
+        "sha256": "7c6c753ec257cb2bcb7994a9cefdb6a4d9be0ae4b53adfd20d83b712767e6259",
+        "bytes": 930.9e6,   # read 796.7 MB + write 134.2 MB
+    },
 }
 
 
