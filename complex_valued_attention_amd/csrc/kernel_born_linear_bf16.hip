@@ -29,8 +29,13 @@
 // as the row operand through the transposing LDS read; the keys are staged as
 // transposed (Re, Im) pairs (KT[channel][token]), with the rotated pairs
 // (-Im, Re) of the workgroup's four feature rows for the features below the
-// diagonal.  Workgroup: 4 waves, wave w owns feature row a = 4 g + w (64
-// features, two column tiles).
+// diagonal.  Workgroup: feature rows 4 g .. 4 g + 3 of one head (256
+// features), 8 waves in two token groups of four: wave w of a group owns the
+// two rows 4 g + 2 (w / 2) + {0, 1} over the column tile w % 2 (32 features
+// each), so the key pairs of its columns are read once per token step for
+// both rows.  The even stages go to group 0 and the odd ones to group 1, so
+// two waves share each SIMD and hide each other's operand latency; at the end
+// group 1's partial sums are added to group 0's through LDS in a fixed order.
 //
 // Decay (per head gamma): the state build weighs token t of T by
 // gamma^(T-1-t) on the feature operand (a per-stage table of the 64 token
@@ -308,13 +313,20 @@ __device__ inline void loads_done_barrier() {
     __asm__ __volatile__("" ::: "memory");
 }
 
-template <bool DECAY>
-__global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p) {
-    __shared__ __align__(16) StateStage st[2];
+constexpr int SNT = 2 * NT;   // threads per state-build workgroup: two token groups
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+template <bool DECAY>
+__global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem p) {
+    // the two stage buffers, each [token group], as two LDS variables: every
+    // access names its buffer at compile time, so the reads of one buffer wait
+    // only for the loads into it, not for the next stage's loads into the other
+    __shared__ __align__(16) StateStage stA[2];
+    __shared__ __align__(16) StateStage stB[2];
+
+    const int lane = threadIdx.x & 63;
+    const int grp = threadIdx.x / NT;         // token group: even (0) or odd (1) stages
+    const int tid = threadIdx.x % NT;         // thread within the group
+    const int wave = tid >> 6;                // wave within the group
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int T = p.T;
@@ -325,7 +337,8 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
     const int lin = (nblk % 8 == 0) ? (x % 8) * (nblk / 8) + x / 8 : x;
     const int64_t bh = lin / GROUPS;
     const int a0 = (lin % GROUPS) * ROWS_PER_WG;
-    const int a = a0 + wave;                  // this wave's feature row
+    const int ftw = wave & 1;                 // this wave's column tile: features b = 32 ftw + l32
+    const int ar0 = a0 + 2 * (wave >> 1);     // and its feature rows ar0, ar0 + 1 (both groups alike)
     const int64_t base = bh * (int64_t)T * D;
     const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re) + base;
     const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im) + base;
@@ -402,32 +415,42 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
     // the Z tile's row operand: ones in row 128 (lane 0 of each half), zero elsewhere
     const uint32_t one2 = 0x3f803f80u;
     const bf16x8 zrow = l32 == 0 ? as_bf16x8(u32x4{one2, one2, one2, one2}) : as_bf16x8(u32x4{0, 0, 0, 0});
-    // column tile ft holds features (a, b = 32 ft + l32): on or above the diagonal the
-    // first operand is the pair of k_a (KT row a), below it the rotated pair (KR row)
-    int xoff[2], boff[2];
+    // row i of the wave holds features (a = ar0 + i, b = 32 ftw + l32): on or above the
+    // diagonal the first operand is the pair of k_a (KT row a), below it the rotated
+    // pair (KR row a - a0); the second is the pair of k_b (KT row b) for both rows
+    int xoff[2];
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-        const int b = 32 * ft + l32;
-        xoff[ft] = a <= b ? (int)offsetof(StateStage, KT) + a * KROW * 4 : (int)offsetof(StateStage, KR) + wave * KROW * 4;
-        boff[ft] = (int)offsetof(StateStage, KT) + b * KROW * 4;
+    for (int i = 0; i < 2; ++i) {
+        const int ai = ar0 + i, b = 32 * ftw + l32;
+        xoff[i] = ai <= b ? (int)offsetof(StateStage, KT) + ai * KROW * 4
+                          : (int)offsetof(StateStage, KR) + (ai - a0) * KROW * 4;
     }
+    const int boff = (int)offsetof(StateStage, KT) + (32 * ftw + l32) * KROW * 4;
 
+    // pair pr: stage 2 pr for group 0, 2 pr + 1 for group 1.  A stage past the
+    // end (group 1 in the last pair of an odd count) is staged harmlessly (its
+    // keys are zero, its value rows clamped to T - 1) and not multiplied.
     const int nst = (T + ST_TOK - 1) / ST_TOK;
-    if (nst > 0) {
-        issue_values(0, st[0]);
-        load_keys(0);
-        store_keys(st[0], 0);
+    const int npair = (nst + 1) / 2;
+    auto t0_of = [&](int pr) { return (2 * pr + grp) * ST_TOK; };
+    if (npair > 0) {
+        issue_values(t0_of(0), stA[grp]);
+        load_keys(t0_of(0));
+        store_keys(stA[grp], t0_of(0));
     }
     loads_done_barrier();
-    for (int s = 0; s < nst; ++s) {
-        StateStage &cur = st[s & 1];
+    // pair pr reads buffer pr % 2 and stages pair pr + 1 into the other
+    auto pair_step = [&](StateStage (&cur_buf)[2], StateStage (&nxt_buf)[2], int pr) {
+        StateStage &cur = cur_buf[grp];
         const char *cb = reinterpret_cast<const char *>(&cur);
-        if (s + 1 < nst) {
-            issue_values((s + 1) * ST_TOK, st[(s + 1) & 1]);
-            load_keys((s + 1) * ST_TOK);
+        if (pr + 1 < npair) {
+            issue_values(t0_of(pr + 1), nxt_buf[grp]);
+            load_keys(t0_of(pr + 1));
         }
+        const bool live = t0_of(pr) < T;   // wave-uniform
 #pragma unroll
         for (int ks = 0; ks < ST_TOK / 16; ++ks) {
+            if (!live) break;
             bf16x8 wa[NTILE];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -444,12 +467,12 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 fa = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 4 * h]);
                 fb = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 8 + 4 * h]);
             }
+            const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(cb + boff + tb);
+            const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(cb + boff + tb + 32);
 #pragma unroll
-            for (int ft = 0; ft < 2; ++ft) {
+            for (int ft = 0; ft < 2; ++ft) {   // ft: the wave's row ar0 + ft
                 const u32x4 x0 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb);
                 const u32x4 x1 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb + 32);
-                const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb);
-                const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(cb + boff[ft] + tb + 32);
                 uint32_t pk[4];
                 if (DECAY) {
                     pk[0] = pack_bf16x2(fa.x * dot2(x0[0], kb0[0]), fa.y * dot2(x0[1], kb0[1]));
@@ -467,12 +490,43 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
                 for (int ti = 0; ti < NTILE; ++ti) acc[ft][ti] = mfma(wa[ti], fk, acc[ft][ti]);
             }
         }
-        if (s + 1 < nst) store_keys(st[(s + 1) & 1], (s + 1) * ST_TOK);
+        if (pr + 1 < npair) store_keys(nxt_buf[grp], t0_of(pr + 1));
         loads_done_barrier();
+    };
+    for (int pr = 0; pr < npair; pr += 2) {
+        pair_step(stA, stB, pr);
+        if (pr + 1 < npair) pair_step(stB, stA, pr + 1);
     }
 
-    // write S[n][a * 64 + b]: lane (column b = 32 ft + l32, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4
-    // (an accumulated state first decays by gamma^T)
+    // group 1's partial sums to group 0 through LDS (the stage buffers are
+    // free: every read ended before the last barrier).  Rows n < 129 only:
+    // tiles 0-3 whole, and of tile 4 register 0 (row 128 = Z on half 0).
+    constexpr int PL = 2 * (4 * 16 + 1);   // floats per lane
+    static_assert((size_t)2 * PL * 64 * 4 <= sizeof(stA), "two waves' partials fit in one stage buffer");
+    float *part = reinterpret_cast<float *>(wave < 2 ? &stA[0] : &stB[0]) + (size_t)(wave & 1) * PL * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[((ft * 4 + ti) * 16 + r) * 64] = acc[ft][ti][r];
+            part[(2 * 64 + ft) * 64] = acc[ft][NTILE - 1][0];
+        }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ft][ti][r] += part[((ft * 4 + ti) * 16 + r) * 64];
+        acc[ft][NTILE - 1][0] += part[(2 * 64 + ft) * 64];
+    }
+
+    // write S[n][a * 64 + b], a = ar0 + ft, b = 32 ftw + l32: lane (l32, half h) holds
+    // rows n = 32 ti + 8 (r / 4) + 4 h + r % 4 (an accumulated state first decays by gamma^T)
     float *Sh = p.S + bh * (int64_t)NM * D * D;
     const float carry = DECAY ? decay_pow(lg2, T) : 1.f;
 #pragma unroll
@@ -483,7 +537,7 @@ __global__ __launch_bounds__(NT) void born_state_bf16_d64_kernel(LinearProblem p
             for (int r = 0; r < 16; ++r) {
                 const int n = 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (n >= NM) continue;
-                float *dst = Sh + ((int64_t)n * D + a) * D + 32 * ft + l32;
+                float *dst = Sh + ((int64_t)n * D + ar0 + ft) * D + 32 * ftw + l32;
                 *dst = p.accumulate ? carry * *dst + acc[ft][ti][r] : acc[ft][ti][r];
             }
 }
@@ -510,7 +564,7 @@ hipError_t launch_born_state_bf16_d64(const LinearProblem &p) {
     const int64_t blocks = (int64_t)p.BH * (D / ROWS_PER_WG);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     auto kern = p.decay.on ? born_state_bf16_d64_kernel<true> : born_state_bf16_d64_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SNT), 0, p.stream, p);
     return hipGetLastError();
 }
 
