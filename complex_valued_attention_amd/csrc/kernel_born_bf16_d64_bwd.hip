@@ -228,13 +228,10 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
 
         // Q' and G' of this lane's query as B operands; delta and 2/l
         u32x4 x[8];
-        bf16x8 qb[8], qneg[4], gb[8];
+        bf16x8 qb[8], gb[8];
         load_rows_b(plane(p.q_re), plane(p.q_im), q, T, h, x);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            qb[kk] = as_bf16x8(x[kk]);
-            if (kk < 4) qneg[kk] = as_bf16x8(x[kk] ^ 0x80008000u);
-        }
+        for (int kk = 0; kk < 8; ++kk) qb[kk] = as_bf16x8(x[kk]);
         load_rows_b(plane(p.g_re), plane(p.g_im), q, T, h, x);
         u32x4 ox[8];
         load_rows_b(plane(p.o_re), plane(p.o_im), q, T, h, ox);
@@ -260,12 +257,17 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
 
         auto key_block = [&](const char *st, int sb, bool masked, int lim) {
             f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
+            // the sign mask made opaque here, so that -Re Q is formed in the
+            // block rather than hoisted into 16 registers for the whole loop
+            uint32_t sgn = 0x80008000u;
+            __asm__ __volatile__("" : "+s"(sgn));
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int o = (kk >> 2) * REGION + sb * 32 * ROWB + off.koff[kk & 3];
                 const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(st + o);
                 sr = mfma(ak, qb[kk], sr);
-                si = mfma(ak, kk < 4 ? qb[kk + 4] : qneg[kk - 4], si);
+                // -Re Q formed as it is used (sign bits flipped), not held in 16 more registers
+                si = mfma(ak, kk < 4 ? qb[kk + 4] : as_bf16x8(__builtin_bit_cast(u32x4, qb[kk - 4]) ^ sgn), si);
                 const bf16x8 av = *reinterpret_cast<const bf16x8 *>(st + 2 * REGION + o);
                 e = mfma(av, gb[kk], e);
             }
