@@ -30,6 +30,14 @@
 //    block: S and E (queries x keys), w/l and P, then dV^T += G^T (w/l) and
 //    dK^T += Q^T P.
 // Causal work is balanced by mirrored pairs of tiles, as in the forward.
+//
+// Per-head decay (DECAY instances): every weight w and D2 on the causal
+// support carries gamma^(k - j) (query k, key j).  In the dQ kernel, on a
+// block with no mask, the factor splits into a part per lane and register
+// group (one exponential each) and a part per register within its group
+// (gamma^0..3, per kernel); the dK/dV kernel, at its register limit, and
+// masked blocks form it per weight, the distance clamped at 0 where the mask
+// zeroes the weight anyway.
 #include "cattn_internal.h"
 
 namespace cattn {
@@ -193,6 +201,7 @@ constexpr int QNW = 8;
 constexpr int QNT = 64 * QNW;
 constexpr int QBT = 32 * QNW;
 
+template <bool DECAY>
 __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
     __shared__ __align__(16) char lds[2 * QREG * REGION];
 
@@ -250,12 +259,17 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
             inv2 = l != 0.f ? 2.f / l : 0.f;   // a zero denominator: no gradient
         }
         const float dinv2 = dl * inv2;
+        // DECAY: gamma^(3 - b) for register b = r % 4 of a group
+        const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
+        float sig[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sig[b] = DECAY ? decay_pow(lg2, 3 - b) : 1.f;
 
         f32x16 acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
 
-        auto key_block = [&](const char *st, int sb, bool masked, int lim) {
+        auto key_block = [&](const char *st, int sb, bool masked, int lim, int kb0) {
             f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
             // the sign mask made opaque here, so that -Re Q is formed in the
             // block rather than hoisted into 16 registers for the whole loop
@@ -272,10 +286,19 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
                 e = mfma(av, gb[kk], e);
             }
             // P^T = D2 S^T; register r of lane half h is key 8 (r/4) + 4 h + r % 4
+            // DECAY, no mask: gamma^(q - key) = mu[r / 4] sigma[r % 4] (all <= 1)
+            float mu[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) mu[a] = DECAY && !masked ? decay_pow(lg2, q - kb0 - 8 * a - 4 * h - 3) : 1.f;
             uint32_t pr[8], pi[8];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float d0 = e[r] * inv2 - dinv2, d1 = e[r + 1] * inv2 - dinv2;
+                if (DECAY) {
+                    const int n0 = q - kb0 - (8 * (r >> 2) + 4 * h + (r & 3));
+                    d0 *= masked ? decay_pow(lg2, max(n0, 0)) : mu[r >> 2] * sig[r & 3];
+                    d1 *= masked ? decay_pow(lg2, max(n0 - 1, 0)) : mu[r >> 2] * sig[(r & 3) + 1];
+                }
                 if (masked) {
                     const int key0 = 8 * (r >> 2) + 4 * h + (r & 3);
                     d0 = key0 > lim ? 0.f : d0;
@@ -326,7 +349,7 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
             if (s + 1 < nstages) issue_stage(s + 1);
             const char *st = lds + (s & 1) * QREG * REGION;
 #pragma unroll
-            for (int sb = 0; sb < BS / 32; ++sb) key_block(st, sb, false, 31);
+            for (int sb = 0; sb < BS / 32; ++sb) key_block(st, sb, false, 31, s * BS + 32 * sb);
         }
         for (; s < nstages; ++s) {
             loads_done_barrier();
@@ -339,9 +362,9 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
                 const bool skip = kb0 >= T || (p.causal && kb0 > qt0);
                 const bool full = (!p.causal || kb0 + 32 <= qt0) && kb0 + 32 <= T;
                 if (full)
-                    key_block(st, sb, false, 31);
+                    key_block(st, sb, false, 31, kb0);
                 else if (!skip)
-                    key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0));
+                    key_block(st, sb, true, min(p.causal ? qt0 + l32 - kb0 : 31, T - 1 - kb0), kb0);
             }
         }
         if (q < T) store_rows(reinterpret_cast<uint16_t *>(p.dq_re) + head, reinterpret_cast<uint16_t *>(p.dq_im) + head,
@@ -352,6 +375,7 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
 // ---------------------------------------------------------------------------- dK, dV
 constexpr int KREG = 8;   // Q re, Q im, G re, G im (row-major), the same four (transposing)
 
+template <bool DECAY>
 __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p, int nkt, int nwork) {
     __shared__ __align__(16) char lds[2 * KREG * REGION];
     __shared__ __align__(16) float scal[2][2][BS];   // [buffer][1/l, delta/l][query of the stage]
@@ -431,6 +455,9 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         f32x16 dk[4], dv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) dk[c] = dv[c] = f32x16{};
+        // DECAY: the head's log2 gamma (this kernel is at its register limit: each
+        // factor is one exponential, formed as it is used)
+        const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
 
         // The work of one 32-query block sb, in steps that a full stage
         // interleaves across its two blocks.
@@ -445,11 +472,13 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         };
         // weights of register group g: register r of lane half h is query
         // 8 (r/4) + 4 h + r % 4 of the block
+        // DECAY: qb0 is the block's first query; the factor gamma^(query - key)
         auto weight_group = [&](const float *sc_inv, const float *sc_dinv, int sb, int g, bool masked, int lo,
                                 int hi, const f32x16 &sr, const f32x16 &si, const f32x16 &e, uint32_t (&aw)[8],
-                                uint32_t (&pr)[8], uint32_t (&pi)[8]) {
+                                uint32_t (&pr)[8], uint32_t (&pi)[8], int qb0) {
             const f32x4 iv = *reinterpret_cast<const f32x4 *>(sc_inv + 32 * sb + 8 * g + 4 * h);
             const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv + 32 * sb + 8 * g + 4 * h);
+            const int n0 = qb0 + 8 * g + 4 * h - key;   // distance of register c = 0
             float a[4], d2[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -457,6 +486,11 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
                 // w/l, and half of dL/ds (2 (e - delta)/l); dK is doubled on store
                 a[c] = iv[c] * (sr[r] * sr[r] + si[r] * si[r]);
                 d2[c] = e[r] * iv[c] - di[c];
+                if (DECAY) {   // distances are >= 0 where the mask keeps the weight
+                    const float f = decay_pow(lg2, max(n0 + c, 0));
+                    a[c] *= f;
+                    d2[c] *= f;
+                }
                 if (masked) {
                     const int qi = 8 * g + 4 * h + c;
                     const bool ok = qi >= lo && qi <= hi;
@@ -506,14 +540,15 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             dk[2 + ct] = mfma(qit, w.prb[m], dk[2 + ct]);
             dk[2 + ct] = mfma(qrt, w.pnb[m], dk[2 + ct]);
         };
-        auto query_block = [&](const char *st, const float *sc_inv, const float *sc_dinv, int sb, bool masked,
+        auto query_block = [&](const char *st, const float *sc_inv, const float *sc_dinv, int sb, int qb0, bool masked,
                                int lo, int hi) {
             f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) score_step(st, sb, kk, sr, si, e);
             uint32_t aw[8], pr[8], pi[8];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) weight_group(sc_inv, sc_dinv, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi);
+            for (int g = 0; g < 4; ++g)
+                weight_group(sc_inv, sc_dinv, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi, qb0);
             const GradOps w = grad_ops(aw, pr, pi);
 #pragma unroll
             for (int j = 0; j < 4; ++j) grad_step(st, sb, j, w);
@@ -521,7 +556,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         // both blocks of a stage with no mask: block 1's score products run
         // beside block 0's weight arithmetic, and block 0's gradient products
         // beside block 1's weight arithmetic
-        auto full_stage = [&](const char *st, const float *sc_inv, const float *sc_dinv) {
+        auto full_stage = [&](const char *st, const float *sc_inv, const float *sc_dinv, int qbase) {
             f32x16 sr0 = f32x16{}, si0 = f32x16{}, e0 = f32x16{};
             f32x16 sr1 = f32x16{}, si1 = f32x16{}, e1 = f32x16{};
 #pragma unroll
@@ -537,7 +572,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             for (int g = 0; g < 4; ++g) {
                 score_step(st, 1, 2 * g, sr1, si1, e1);
                 score_step(st, 1, 2 * g + 1, sr1, si1, e1);
-                weight_group(sc_inv, sc_dinv, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0);
+                weight_group(sc_inv, sc_dinv, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0, qbase);
             }
             const GradOps w0 = grad_ops(aw0, pr0, pi0);
 #pragma unroll
@@ -553,7 +588,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 grad_step(st, 0, j, w0);
-                weight_group(sc_inv, sc_dinv, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1);
+                weight_group(sc_inv, sc_dinv, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1, qbase + 32);
             }
             const GradOps w1 = grad_ops(aw1, pr1, pi1);
 #pragma unroll
@@ -596,7 +631,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             }
             const char *st = lds + (s & 1) * KREG * REGION;
             const float *si2 = scal[s & 1][0], *sdi = scal[s & 1][1];
-            if (all_full) full_stage(st, si2, sdi);
+            if (all_full) full_stage(st, si2, sdi, qs + s * BS);
 #pragma unroll
             for (int sb = 0; sb < BS / 32; ++sb) {
                 if (all_full) continue;
@@ -604,11 +639,11 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
                 const bool skip = qb0 >= T || kw0 >= T || (p.causal && qb0 + 31 < kw0);
                 const bool full = (!p.causal || qb0 >= kw0 + 31) && qb0 + 32 <= T && kw0 + 32 <= T;
                 if (full) {
-                    query_block(st, si2, sdi, sb, false, 0, 31);
+                    query_block(st, si2, sdi, sb, qb0, false, 0, 31);
                 } else if (!skip) {
                     const int lo = p.causal ? key - qb0 : 0;
                     const int hi = key < T ? T - 1 - qb0 : -1;
-                    query_block(st, si2, sdi, sb, true, lo, hi);
+                    query_block(st, si2, sdi, sb, qb0, true, lo, hi);
                 }
             }
             if (next) scal_store(qs + (s + 1) * BS, (s + 1) & 1);
@@ -638,7 +673,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 }  // namespace
 
 bool supports_born_bf16_d64_bwd(const BwdProblem &p) {
-    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D && !p.decay.on;
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == D;
 }
 
 hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {
@@ -646,7 +681,8 @@ hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {
     const int nwork = p.causal ? (nrb + 1) / 2 : nrb;
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_bf16_d64_bwd_dq_kernel, dim3((unsigned)blocks), dim3(QNT), 0, p.stream, p, nrb, nwork);
+    auto kern = p.decay.on ? born_bf16_d64_bwd_dq_kernel<true> : born_bf16_d64_bwd_dq_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(QNT), 0, p.stream, p, nrb, nwork);
     return hipGetLastError();
 }
 
@@ -655,7 +691,8 @@ hipError_t launch_born_bf16_d64_bwd_dkdv(const BwdProblem &p) {
     const int nwork = p.causal ? (nkt + 1) / 2 : nkt;
     const int64_t blocks = (int64_t)p.BH * nwork;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(born_bf16_d64_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nkt, nwork);
+    auto kern = p.decay.on ? born_bf16_d64_bwd_dkdv_kernel<true> : born_bf16_d64_bwd_dkdv_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, p.stream, p, nkt, nwork);
     return hipGetLastError();
 }
 

@@ -123,7 +123,9 @@ __device__ inline void store4(void *re, void *im, int64_t row, int f, f32x4 v) {
 }
 
 // ------------------------------------------------------------------------------ dQ (and db)
-template <int D, int OP, int LAY>
+// DECAY (Born): every weight and D2 carries gamma^(query - key), one
+// exponential per weight (the distance clamped at 0 where the mask zeroes it).
+template <int D, int OP, int LAY, bool DECAY>
 __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
     using C = BCfg<D>;
     extern __shared__ __align__(16) float fsm[];
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
                     const int key = 8 * g + 4 * h + e;
                     const bool keep = !((diag && key > l32) || k0 + key >= T);
                     if (born) {
-                        const float d2 = keep ? 2.f * (ev[r] - dl) * inv_l : 0.f;
+                        float d2 = keep ? 2.f * (ev[r] - dl) * inv_l : 0.f;
+                        if (DECAY) d2 *= decay_pow(p.decay.lg2[bh % p.H], max(qrow - (k0 + key), 0));
                         pr[r] = d2 * sr[r];
                         pi[r] = d2 * si[r];
                     } else {
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_f32_kernel(BwdProblem p, int nrb) {
 }
 
 // ------------------------------------------------------------------------------ dK, dV
-template <int D, int OP, int LAY>
+template <int D, int OP, int LAY, bool DECAY>
 __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb) {
     using C = BCfg<D>;
     extern __shared__ __align__(16) float fsm[];
@@ -469,8 +472,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
                     const bool keep = !((diag && qi < l32) || q0 + qi >= T);
                     if (born) {
                         const float w = sr[r] * sr[r] + si[r] * si[r];
-                        wl[r] = keep ? w * av[e] : 0.f;
-                        const float d2 = keep ? 2.f * (ev[r] - bv[e]) * av[e] : 0.f;
+                        // DECAY: gamma^(query - key) on the weight and on D2
+                        const float f = DECAY ? decay_pow(p.decay.lg2[bh % p.H], max(q0 + qi - (kt0 + l32), 0)) : 1.f;
+                        wl[r] = keep ? w * av[e] * f : 0.f;
+                        const float d2 = keep ? 2.f * (ev[r] - bv[e]) * av[e] * f : 0.f;
                         pr[r] = d2 * sr[r];
                         pi[r] = d2 * si[r];
                     } else {
@@ -527,15 +532,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(BwdProblem p, int nkb)
         }
 }
 
-template <int D, int OP, int LAY>
+template <int D, int OP, int LAY, bool DECAY = false>
 hipError_t launch_cfg(const BwdProblem &p) {
     using C = BCfg<D>;
     static std::atomic<uint64_t> dq_set{0}, kv_set{0};
     const int nblk = (p.T + BM - 1) / BM;
     const int64_t blocks = (int64_t)p.BH * nblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    auto kkv = bwd_dkdv_f32_kernel<D, OP, LAY>;
-    auto kdq = bwd_dq_f32_kernel<D, OP, LAY>;
+    auto kkv = bwd_dkdv_f32_kernel<D, OP, LAY, DECAY>;
+    auto kdq = bwd_dq_f32_kernel<D, OP, LAY, DECAY>;
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), C::LDS_BYTES_KV, kv_set);
     if (e != hipSuccess) return e;
     e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), C::LDS_BYTES, dq_set);
@@ -549,7 +554,9 @@ hipError_t launch_cfg(const BwdProblem &p) {
 
 template <int D, int LAY>
 hipError_t launch_op(const BwdProblem &p) {
-    return p.op == OP_BORN ? launch_cfg<D, OP_BORN, LAY>(p) : launch_cfg<D, OP_PCT, LAY>(p);
+    if (p.op == OP_BORN)
+        return p.decay.on ? launch_cfg<D, OP_BORN, LAY, true>(p) : launch_cfg<D, OP_BORN, LAY>(p);
+    return launch_cfg<D, OP_PCT, LAY>(p);
 }
 
 template <int D>
@@ -562,7 +569,7 @@ hipError_t launch_d(const BwdProblem &p) {
 bool supports_bwd_f32_mfma(const BwdProblem &p) {
     // complex64, or bf16 planes widened to fp32 on load (bf16 Born at width 64
     // has its own bf16 matrix-core pair, tried first)
-    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64) && !p.decay.on;
+    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64);
 }
 
 hipError_t launch_bwd_f32_mfma(const BwdProblem &p) {

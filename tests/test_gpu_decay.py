@@ -254,6 +254,55 @@ def test_decay_backward(layout, B, H, T, d):
     compare(w, got, ref, f"decay bwd {layout} d{d}", terms)
 
 
+@pytest.mark.parametrize("layout,d", [("bf16", 64), ("c64", 64), ("c64", 16), ("bf16", 32), ("c64", 17)])
+def test_decay_of_one_backward_is_plain(layout, d):
+    # every factor is exp2(0) = 1 exactly: the decayed instances give the plain gradients' bits
+    from complex_valued_attention_amd.check import grad_to_device
+    c = _cattn()
+    B, H, T = 1, 2, 300
+    w = gen.Workload("dbwd1", "born", True, B, H, T, d, layout, seed=97, qk_unit=True)
+    inp = gen.make_inputs(w)
+    grad = gen.make_grad(w)
+    q, k, v = to_device(inp)
+    g = grad_to_device(grad)
+    den = torch.empty(B * H * T, dtype=torch.float32, device="cuda")
+    o = c.born_fwd(q, k, v, causal=True, row_den=den)
+    a = c.born_bwd(q, k, v, o, g, den, causal=True, decay=[1.0] * H)
+    b = c.born_bwd(q, k, v, o, g, den, causal=True)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        xa, ya = from_device(x), from_device(y)
+        say(f"decay 1 bwd {layout} d{d} {name}: max |diff| {np.abs(xa - ya).max():.3e}")
+        assert np.array_equal(xa, ya), name
+
+
+def test_decay_backward_full_size_heads():
+    # the B8 H16 T4096 bf16 shape on the matrix-core pair, two whole heads against the oracle
+    import oracle
+    from complex_valued_attention_amd.check import grad_to_device
+    from test_gpu_bwd import compare, term_scales
+    c = _cattn()
+    w = FULL["c3"]
+    gam = gen.decay_gammas(w.H)
+    say("case decay bwd full", w)
+    inp = gen.make_inputs(w)
+    grad = gen.make_grad(w)
+    q, k, v = to_device(inp)
+    den = torch.empty(w.B * w.H * w.T, dtype=torch.float32, device="cuda")
+    o = c.born_fwd(q, k, v, causal=True, row_den=den, decay=gam)
+    dq, dk, dv = c.born_bwd(q, k, v, o, grad_to_device(grad), den, causal=True, decay=gam)
+    torch.cuda.synchronize()
+    got = [from_device(x) for x in (dq, dk, dv)]
+    g32 = f32(gam)
+    for b, h in [(0, 0), (7, 15)]:
+        ref = oracle.born_attention_bwd(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], grad.g64[b, h], causal=True,
+                                        decay=g32[h])
+        terms = term_scales("born", inp.q64[b, h][None], inp.k64[b, h][None], inp.v64[b, h][None],
+                            grad.g64[b, h][None], True, decay=g32[h:h + 1])
+        compare(w, tuple(x[b, h] for x in got) + (None,), tuple(ref) + (None,), f"decay bwd full head {b},{h}",
+                tuple(t[0] for t in terms))
+
+
 # ----------------------------------------------------------------------------- rotary Q at load
 
 ROT_CASES = [
