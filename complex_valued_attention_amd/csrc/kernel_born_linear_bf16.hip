@@ -527,19 +527,37 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
 
     // write S[n][a * 64 + b], a = ar0 + ft, b = 32 ftw + l32: lane (l32, half h) holds
     // rows n = 32 ti + 8 (r / 4) + 4 h + r % 4 (an accumulated state first decays by gamma^T)
+    // Tiles 0-3 hold only valid rows (n < 128), so their accesses carry no
+    // condition and the old values are loaded eight at a time; of tile 4 only
+    // register 0 of half 0 is a row (n = 128, Z).
     float *Sh = p.S + bh * (int64_t)NM * D * D;
     const float carry = DECAY ? decay_pow(lg2, T) : 1.f;
+    const bool acc_mode = p.accumulate;   // uniform
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+    for (int ft = 0; ft < 2; ++ft) {
+        float *col = Sh + (int64_t)(ar0 + ft) * D + 32 * ftw + l32;   // row n at col + n D^2
 #pragma unroll
-        for (int ti = 0; ti < NTILE; ++ti)
+        for (int ti = 0; ti < NTILE - 1; ++ti) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (n >= NM) continue;
-                float *dst = Sh + ((int64_t)n * D + ar0 + ft) * D + 32 * ftw + l32;
-                *dst = p.accumulate ? carry * *dst + acc[ft][ti][r] : acc[ft][ti][r];
+            for (int r0 = 0; r0 < 16; r0 += 8) {
+                float old[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int n = 32 * ti + 8 * ((r0 + r) >> 2) + 4 * h + ((r0 + r) & 3);
+                    old[r] = acc_mode ? col[(int64_t)n * D * D] : 0.f;
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int n = 32 * ti + 8 * ((r0 + r) >> 2) + 4 * h + ((r0 + r) & 3);
+                    col[(int64_t)n * D * D] = acc_mode ? carry * old[r] + acc[ft][ti][r0 + r] : acc[ft][ti][r0 + r];
+                }
             }
+        }
+        if (h == 0) {
+            float *z = col + (int64_t)(NM - 1) * D * D;
+            *z = acc_mode ? carry * *z + acc[ft][NTILE - 1][0] : acc[ft][NTILE - 1][0];
+        }
+    }
 }
 
 }  // namespace
