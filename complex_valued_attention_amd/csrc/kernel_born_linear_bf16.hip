@@ -22,20 +22,24 @@
 // the other's matrix products), 32 tokens per wave, one head.
 //
 // State build: S[n][f] (+)= sum_j W[j][n] phi_f(k_j) with W[j] = (Re V[j],
-// Im V[j], 1), a real product [129 x T] x [T x 4096] per head.  MFMA rows are
-// the state matrices (the Z tile takes a constant operand: ones in row 128),
-// columns are features, the reduction runs over tokens.  Per 64-token stage
-// the value planes are copied token-major into LDS (LDS-direct loads) and read
-// as the row operand through the transposing LDS read; the keys are staged as
-// transposed (Re, Im) pairs (KT[channel][token]), with the rotated pairs
-// (-Im, Re) of the workgroup's four feature rows for the features below the
-// diagonal.  Workgroup: feature rows 4 g .. 4 g + 3 of one head (256
-// features), 8 waves in two token groups of four: wave w of a group owns the
-// two rows 4 g + 2 (w / 2) + {0, 1} over the column tile w % 2 (32 features
-// each), so the key pairs of its columns are read once per token step for
-// both rows.  The even stages go to group 0 and the odd ones to group 1, so
-// two waves share each SIMD and hide each other's operand latency; at the end
-// group 1's partial sums are added to group 0's through LDS in a fixed order.
+// Im V[j], 1), a real product [129 x T] x [T x 4096] per head.  The value
+// rows (Re V, Im V: four tiles of 32) run on matrix cores, MFMA rows the state
+// matrices, columns the features, the reduction over tokens; the Z row (the
+// plain sum of the features over tokens) is summed per lane from the fp32
+// features.  Per 64-token stage the key and value planes are copied
+// token-major into LDS (LDS-direct loads, no registers) and read through the
+// transposing LDS read: the values as the row operand, the keys so that lane
+// l32 receives channel b of its eight tokens, whose (Re, Im) pairs two byte
+// permutes form.  The pairs of the workgroup's four feature rows, and their
+// rotations (-Im, Re) for the features below the diagonal, are staged
+// [row][token] through one wave's registers.  Workgroup: feature rows
+// 4 g .. 4 g + 3 of one head (256 features), 8 waves in two token groups of
+// four: wave w of a group owns the two rows 4 g + 2 (w / 2) + {0, 1} over the
+// column tile w % 2 (32 features each), so the key pairs of its columns are
+// formed once per token step for both rows.  The even stages go to group 0
+// and the odd ones to group 1, so two waves share each SIMD and hide each
+// other's operand latency; at the end each group finishes half the state
+// rows, adding the other group's partial sums through LDS in a fixed order.
 //
 // Decay (per head gamma): the state build weighs token t of T by
 // gamma^(T-1-t) on the feature operand (a per-stage table of the 64 token
@@ -292,13 +296,18 @@ typedef __bf16 bf16x4v __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct StateStage {
-    uint32_t KT[D][KROW];                // (Re k, Im k) pairs, [channel][token]
-    uint32_t KR[ROWS_PER_WG][KROW];      // (-Im k, Re k) of this workgroup's feature rows
-    char V[2][VREGION];                  // value planes, token-major, 16-byte chunks swizzled by token
+    char K[2][VREGION];                  // key planes, token-major, 16-byte chunks swizzled by token
+    char V[2][VREGION];                  // value planes, the same layout
+    uint32_t KA[ROWS_PER_WG][KROW];      // (Re k, Im k) of this workgroup's feature rows, [row][token]
+    uint32_t KR[ROWS_PER_WG][KROW];      // (-Im k, Re k) of the same rows
     float F[ST_TOK];                     // decay: gamma^(T-1-t) of the stage's tokens
 };
 
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
+
+// (Re, Im) bf16 pairs from two words of one plane each: the low halves, the high halves
+__device__ inline uint32_t pair_lo(uint32_t re, uint32_t im) { return __builtin_amdgcn_perm(im, re, 0x05040100u); }
+__device__ inline uint32_t pair_hi(uint32_t re, uint32_t im) { return __builtin_amdgcn_perm(im, re, 0x07060302u); }
 
 __device__ inline u32x2 ds_read_tr(const char *p) {
     const bf16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4v *)(p));
@@ -342,39 +351,31 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
     const int64_t base = bh * (int64_t)T * D;
     const uint16_t *kre = reinterpret_cast<const uint16_t *>(p.k_re) + base;
     const uint16_t *kim = reinterpret_cast<const uint16_t *>(p.k_im) + base;
-    const uint16_t *vpl[2] = {reinterpret_cast<const uint16_t *>(p.v_re) + base,
+    const uint16_t *vpl[4] = {kre, kim, reinterpret_cast<const uint16_t *>(p.v_re) + base,
                               reinterpret_cast<const uint16_t *>(p.v_im) + base};
 
-    // keys through registers (interleaved to pairs, transposed); thread -> (token, 8 channels), twice
-    u32x4 kr_reg[2], ki_reg[2];
-    auto load_keys = [&](int t0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = tid + i * NT;
-            const int r = g / (D / 8), c8 = (g % (D / 8)) * 8;
-            kr_reg[i] = ki_reg[i] = u32x4{0, 0, 0, 0};
-            if (t0 + r < T) {
-                kr_reg[i] = *reinterpret_cast<const u32x4 *>(kre + (int64_t)(t0 + r) * D + c8);
-                ki_reg[i] = *reinterpret_cast<const u32x4 *>(kim + (int64_t)(t0 + r) * D + c8);
-            }
+    // the workgroup's four feature rows through registers: lane t of the
+    // group's first wave holds channels a0 .. a0 + 3 of token t of a stage
+    // (zero past T, which makes every feature of such a token zero)
+    u32x2 rr_reg, ri_reg;
+    auto load_rows = [&](int t0) {
+        rr_reg = ri_reg = u32x2{0u, 0u};
+        if (tid < ST_TOK && t0 + tid < T) {
+            rr_reg = *reinterpret_cast<const u32x2 *>(kre + (int64_t)(t0 + tid) * D + a0);
+            ri_reg = *reinterpret_cast<const u32x2 *>(kim + (int64_t)(t0 + tid) * D + a0);
         }
     };
     const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
-    auto store_keys = [&](StateStage &S_, int t0) {
-        if (DECAY && tid < ST_TOK) S_.F[tid] = t0 + tid < T ? decay_pow(lg2, T - 1 - (t0 + tid)) : 0.f;
+    auto store_rows = [&](StateStage &S_, int t0) {
+        if (tid < ST_TOK) {
+            if (DECAY) S_.F[tid] = t0 + tid < T ? decay_pow(lg2, T - 1 - (t0 + tid)) : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = tid + i * NT;
-            const int r = g / (D / 8), c8 = (g % (D / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t p0 = (kr_reg[i][e] & 0xffffu) | (ki_reg[i][e] << 16);
-                const uint32_t p1 = (kr_reg[i][e] >> 16) | (ki_reg[i][e] & 0xffff0000u);
-                S_.KT[c8 + 2 * e][r] = p0;
-                S_.KT[c8 + 2 * e + 1][r] = p1;
-                const int c0 = c8 + 2 * e - a0;
-                if (c0 >= 0 && c0 < ROWS_PER_WG) S_.KR[c0][r] = rot_pair(p0);
-                if (c0 + 1 >= 0 && c0 + 1 < ROWS_PER_WG) S_.KR[c0 + 1][r] = rot_pair(p1);
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t p0 = pair_lo(rr_reg[i], ri_reg[i]), p1 = pair_hi(rr_reg[i], ri_reg[i]);
+                S_.KA[2 * i][tid] = p0;
+                S_.KA[2 * i + 1][tid] = p1;
+                S_.KR[2 * i][tid] = rot_pair(p0);
+                S_.KR[2 * i + 1][tid] = rot_pair(p1);
             }
         }
     };
@@ -384,11 +385,12 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
     const int lcv = sslot ^ swz_v(srow);
     auto issue_values = [&](int t0, StateStage &S_) {
 #pragma unroll
-        for (int i = 0; i < 2 * VRPT; ++i) {
+        for (int i = 0; i < 4 * VRPT; ++i) {
             const int pl = i / VRPT, e = i % VRPT;
             const int row = min(t0 + srow + (NT / 8) * e, T - 1);
+            char *dst = pl < 2 ? S_.K[pl] : S_.V[pl - 2];
             __builtin_amdgcn_global_load_lds((GLB_AS void *)(vpl[pl] + (int64_t)row * D + 8 * lcv),
-                                             (LDS_AS void *)(S_.V[pl] + e * (NT * 16) + wave * 1024), 16, 0, 0);
+                                             (LDS_AS void *)(dst + e * (NT * 16) + wave * 1024), 16, 0, 0);
         }
     };
     // V^T operand through the transposing read (k-step of 16 tokens): lane 16 G + 4 r + c4
@@ -404,28 +406,27 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
         }
     }
 
-    f32x16 acc[2][NTILE];
+    // value rows (tiles 0-3: Re V, Im V) on matrix cores; the Z row (the plain
+    // sum of the features over tokens) as per-lane sums of the fp32 features
+    f32x16 acc[2][NTILE - 1];
+    float zs[2] = {0.f, 0.f};
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-        for (int ti = 0; ti < NTILE; ++ti)
+        for (int ti = 0; ti < NTILE - 1; ++ti)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[ft][ti][r] = 0.f;
-
-    // the Z tile's row operand: ones in row 128 (lane 0 of each half), zero elsewhere
-    const uint32_t one2 = 0x3f803f80u;
-    const bf16x8 zrow = l32 == 0 ? as_bf16x8(u32x4{one2, one2, one2, one2}) : as_bf16x8(u32x4{0, 0, 0, 0});
     // row i of the wave holds features (a = ar0 + i, b = 32 ftw + l32): on or above the
-    // diagonal the first operand is the pair of k_a (KT row a), below it the rotated
-    // pair (KR row a - a0); the second is the pair of k_b (KT row b) for both rows
+    // diagonal the first operand is the pair of k_a (KA row a - a0), below it the rotated
+    // pair (KR row a - a0); the second is the pair of k_b, formed from the two key planes
+    // (read like the value operand: lane l32 gets channel b for its eight tokens)
     int xoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int ai = ar0 + i, b = 32 * ftw + l32;
-        xoff[i] = ai <= b ? (int)offsetof(StateStage, KT) + ai * KROW * 4
+        xoff[i] = ai <= b ? (int)offsetof(StateStage, KA) + (ai - a0) * KROW * 4
                           : (int)offsetof(StateStage, KR) + (ai - a0) * KROW * 4;
     }
-    const int boff = (int)offsetof(StateStage, KT) + (32 * ftw + l32) * KROW * 4;
 
     // pair pr: stage 2 pr for group 0, 2 pr + 1 for group 1.  A stage past the
     // end (group 1 in the last pair of an odd count) is staged harmlessly (its
@@ -435,8 +436,8 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
     auto t0_of = [&](int pr) { return (2 * pr + grp) * ST_TOK; };
     if (npair > 0) {
         issue_values(t0_of(0), stA[grp]);
-        load_keys(t0_of(0));
-        store_keys(stA[grp], t0_of(0));
+        load_rows(t0_of(0));
+        store_rows(stA[grp], t0_of(0));
     }
     loads_done_barrier();
     // pair pr reads buffer pr % 2 and stages pair pr + 1 into the other
@@ -445,13 +446,13 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
         const char *cb = reinterpret_cast<const char *>(&cur);
         if (pr + 1 < npair) {
             issue_values(t0_of(pr + 1), nxt_buf[grp]);
-            load_keys(t0_of(pr + 1));
+            load_rows(t0_of(pr + 1));
         }
         const bool live = t0_of(pr) < T;   // wave-uniform
 #pragma unroll
         for (int ks = 0; ks < ST_TOK / 16; ++ks) {
             if (!live) break;
-            bf16x8 wa[NTILE];
+            bf16x8 wa[NTILE - 1];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const char *vb = cur.V[c >> 1] + 16 * ks * VROWB + voff[c & 1];
@@ -459,7 +460,6 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
                 const u32x2 hi = ds_read_tr(vb + 8 * VROWB);
                 wa[c] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
-            wa[NTILE - 1] = zrow;
             const int tb = (16 * ks + 4 * h) * 4;   // byte offset of this lane's first token in a key row
             // decay: the factors of the lane's tokens 16 ks + 4 h + e and 16 ks + 8 + 4 h + e
             float4 fa = make_float4(1.f, 1.f, 1.f, 1.f), fb = fa;
@@ -467,30 +467,36 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
                 fa = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 4 * h]);
                 fb = *reinterpret_cast<const float4 *>(&cur.F[16 * ks + 8 + 4 * h]);
             }
-            const u32x4 kb0 = *reinterpret_cast<const u32x4 *>(cb + boff + tb);
-            const u32x4 kb1 = *reinterpret_cast<const u32x4 *>(cb + boff + tb + 32);
+            u32x4 kb0, kb1;
+            {
+                const char *kb = cur.K[0] + 16 * ks * VROWB + voff[ftw];
+                const u32x2 rlo = ds_read_tr(kb), rhi = ds_read_tr(kb + 8 * VROWB);
+                const u32x2 ilo = ds_read_tr(kb + VREGION), ihi = ds_read_tr(kb + VREGION + 8 * VROWB);
+                kb0 = u32x4{pair_lo(rlo[0], ilo[0]), pair_hi(rlo[0], ilo[0]), pair_lo(rlo[1], ilo[1]), pair_hi(rlo[1], ilo[1])};
+                kb1 = u32x4{pair_lo(rhi[0], ihi[0]), pair_hi(rhi[0], ihi[0]), pair_lo(rhi[1], ihi[1]), pair_hi(rhi[1], ihi[1])};
+            }
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {   // ft: the wave's row ar0 + ft
                 const u32x4 x0 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb);
                 const u32x4 x1 = *reinterpret_cast<const u32x4 *>(cb + xoff[ft] + tb + 32);
-                uint32_t pk[4];
-                if (DECAY) {
-                    pk[0] = pack_bf16x2(fa.x * dot2(x0[0], kb0[0]), fa.y * dot2(x0[1], kb0[1]));
-                    pk[1] = pack_bf16x2(fa.z * dot2(x0[2], kb0[2]), fa.w * dot2(x0[3], kb0[3]));
-                    pk[2] = pack_bf16x2(fb.x * dot2(x1[0], kb1[0]), fb.y * dot2(x1[1], kb1[1]));
-                    pk[3] = pack_bf16x2(fb.z * dot2(x1[2], kb1[2]), fb.w * dot2(x1[3], kb1[3]));
-                } else {
-                    pk[0] = pack_bf16x2(dot2(x0[0], kb0[0]), dot2(x0[1], kb0[1]));
-                    pk[1] = pack_bf16x2(dot2(x0[2], kb0[2]), dot2(x0[3], kb0[3]));
-                    pk[2] = pack_bf16x2(dot2(x1[0], kb1[0]), dot2(x1[1], kb1[1]));
-                    pk[3] = pack_bf16x2(dot2(x1[2], kb1[2]), dot2(x1[3], kb1[3]));
-                }
-                const bf16x8 fk = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+                float f[8];
 #pragma unroll
-                for (int ti = 0; ti < NTILE; ++ti) acc[ft][ti] = mfma(wa[ti], fk, acc[ft][ti]);
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = dot2(x0[e], kb0[e]);
+                    f[4 + e] = dot2(x1[e], kb1[e]);
+                }
+                if (DECAY) {
+                    f[0] *= fa.x, f[1] *= fa.y, f[2] *= fa.z, f[3] *= fa.w;
+                    f[4] *= fb.x, f[5] *= fb.y, f[6] *= fb.z, f[7] *= fb.w;
+                }
+                zs[ft] += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+                const bf16x8 fk = as_bf16x8(u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                  pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
+#pragma unroll
+                for (int ti = 0; ti < NTILE - 1; ++ti) acc[ft][ti] = mfma(wa[ti], fk, acc[ft][ti]);
             }
         }
-        if (pr + 1 < npair) store_keys(nxt_buf[grp], t0_of(pr + 1));
+        if (pr + 1 < npair) store_rows(nxt_buf[grp], t0_of(pr + 1));
         loads_done_barrier();
     };
     for (int pr = 0; pr < npair; pr += 2) {
@@ -498,65 +504,92 @@ __global__ __launch_bounds__(SNT) void born_state_bf16_d64_kernel(LinearProblem 
         if (pr + 1 < npair) pair_step(stB, stA, pr + 1);
     }
 
-    // group 1's partial sums to group 0 through LDS (the stage buffers are
-    // free: every read ended before the last barrier).  Rows n < 129 only:
-    // tiles 0-3 whole, and of tile 4 register 0 (row 128 = Z on half 0).
-    constexpr int PL = 2 * (4 * 16 + 1);   // floats per lane
-    static_assert((size_t)2 * PL * 64 * 4 <= sizeof(stA), "two waves' partials fit in one stage buffer");
-    float *part = reinterpret_cast<float *>(wave < 2 ? &stA[0] : &stB[0]) + (size_t)(wave & 1) * PL * 64 + lane;
-    if (grp == 1) {
+    // Epilogue, split over the two token groups: group 0 finishes the value
+    // tiles 0-1 (rows n < 64) and Z, group 1 the tiles 2-3 (64 <= n < 128).
+    // Each sends the other's tiles of its partial sums through LDS (the stage
+    // buffers are free: every read ended before the last barrier), and in
+    // accumulate mode the old state of its own rows is in flight meanwhile.
+    // Lane (l32, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4 of
+    // S[n][a * 64 + b], a = ar0 + ft, b = 32 ftw + l32; an accumulated state
+    // first decays by gamma^T.
+    constexpr int PX = 2 * 2 * 16 + 2;   // floats per lane sent: two tiles of both rows, and Z
+    static_assert((size_t)NW * PX * 64 * 4 <= sizeof(stA), "a group's partials fit in one stage buffer pair");
+    float *xsend = reinterpret_cast<float *>(grp == 0 ? &stA[0] : &stB[0]) + (size_t)wave * PX * 64 + lane;
+    const float *xrecv = reinterpret_cast<const float *>(grp == 0 ? &stB[0] : &stA[0]) + (size_t)wave * PX * 64 + lane;
+    // the two halves of a wave summed different tokens of the same feature
 #pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
+    for (int ft = 0; ft < 2; ++ft) zs[ft] += __shfl_xor(zs[ft], 32);
+    auto send = [&](auto SEND) {
+        constexpr int t0 = decltype(SEND)::value;
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
+        for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) part[((ft * 4 + ti) * 16 + r) * 64] = acc[ft][ti][r];
-            part[(2 * 64 + ft) * 64] = acc[ft][NTILE - 1][0];
-        }
-    }
-    __syncthreads();
-    if (grp == 1) return;
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
+                for (int r = 0; r < 16; ++r) xsend[((ft * 2 + i) * 16 + r) * 64] = acc[ft][t0 + i][r];
+    };
+    if (grp == 0) {
+        send(std::integral_constant<int, 2>{});
+    } else {
+        send(std::integral_constant<int, 0>{});
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[ft][ti][r] += part[((ft * 4 + ti) * 16 + r) * 64];
-        acc[ft][NTILE - 1][0] += part[(2 * 64 + ft) * 64];
+        for (int ft = 0; ft < 2; ++ft) xsend[(64 + ft) * 64] = zs[ft];
     }
 
-    // write S[n][a * 64 + b], a = ar0 + ft, b = 32 ftw + l32: lane (l32, half h) holds
-    // rows n = 32 ti + 8 (r / 4) + 4 h + r % 4 (an accumulated state first decays by gamma^T)
-    // Tiles 0-3 hold only valid rows (n < 128), so their accesses carry no
-    // condition and the old values are loaded eight at a time; of tile 4 only
-    // register 0 of half 0 is a row (n = 128, Z).
     float *Sh = p.S + bh * (int64_t)NM * D * D;
-    const float carry = DECAY ? decay_pow(lg2, T) : 1.f;
-    const bool acc_mode = p.accumulate;   // uniform
+    float *col[2];
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-        float *col = Sh + (int64_t)(ar0 + ft) * D + 32 * ftw + l32;   // row n at col + n D^2
+    for (int ft = 0; ft < 2; ++ft) col[ft] = Sh + (int64_t)(ar0 + ft) * D + 32 * ftw + l32;   // row n at col + n D^2
+    const int keep = 2 * grp;                 // first kept tile
+    const bool acc_mode = p.accumulate;       // uniform
+    const bool zlane = grp == 0 && h == 0;    // lanes that write Z (row 128)
+    float old[2][2][16], oldz[2] = {0.f, 0.f};
+    if (acc_mode) {
 #pragma unroll
-        for (int ti = 0; ti < NTILE - 1; ++ti) {
+        for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-            for (int r0 = 0; r0 < 16; r0 += 8) {
-                float old[8];
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int n = 32 * ti + 8 * ((r0 + r) >> 2) + 4 * h + ((r0 + r) & 3);
-                    old[r] = acc_mode ? col[(int64_t)n * D * D] : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int n = 32 * (keep + i) + 8 * (r >> 2) + 4 * h + (r & 3);
+                    old[ft][i][r] = col[ft][(int64_t)n * D * D];
                 }
+        if (zlane) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int n = 32 * ti + 8 * ((r0 + r) >> 2) + 4 * h + ((r0 + r) & 3);
-                    col[(int64_t)n * D * D] = acc_mode ? carry * old[r] + acc[ft][ti][r0 + r] : acc[ft][ti][r0 + r];
+            for (int ft = 0; ft < 2; ++ft) oldz[ft] = col[ft][(int64_t)(NM - 1) * D * D];
+        }
+    } else {
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) old[ft][i][r] = 0.f;
+    }
+    __syncthreads();
+    const float carry = !acc_mode ? 0.f : DECAY ? decay_pow(lg2, T) : 1.f;
+    auto finish = [&](auto KEEP) {
+        constexpr int t0 = decltype(KEEP)::value;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = 32 * (t0 + i) + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float v = acc[ft][t0 + i][r] + xrecv[((ft * 2 + i) * 16 + r) * 64];
+                    col[ft][(int64_t)n * D * D] = fmaf(carry, old[ft][i][r], v);
                 }
-            }
+    };
+    if (grp == 0) {
+        finish(std::integral_constant<int, 0>{});
+        if (zlane) {
+#pragma unroll
+            for (int ft = 0; ft < 2; ++ft)
+                col[ft][(int64_t)(NM - 1) * D * D] = fmaf(carry, oldz[ft], zs[ft] + xrecv[(64 + ft) * 64]);
         }
-        if (h == 0) {
-            float *z = col + (int64_t)(NM - 1) * D * D;
-            *z = acc_mode ? carry * *z + acc[ft][NTILE - 1][0] : acc[ft][NTILE - 1][0];
-        }
+    } else {
+        finish(std::integral_constant<int, 2>{});
     }
 }
 
