@@ -16,8 +16,9 @@
 // one plane per 8 KiB region, staged straight from global memory into LDS,
 // A operands of row-major tiles read as 16-byte chunks, and the transposing
 // LDS read (ds_read_b64_tr_b16) for tiles used with their rows as the
-// contraction index.  A tile needed both ways is staged twice, once in each
-// swizzle, so every LDS read stays free of bank conflicts.  Products are
+// contraction index.  A tile needed both ways is staged once, in a swizzle
+// that keeps both kinds of read free of bank conflicts (swz_b; the dQ
+// kernel still stages K twice, in the forward's two swizzles).  Products are
 // formed with the streamed rows along the MFMA's k-dimension's partner, so
 // each lane's 16 accumulator values are directly the bf16 B operand of the
 // next product (no shuffles).
@@ -26,7 +27,9 @@
 //    wave's Q' and G' in registers) and streams K and V.  Per 32-key block:
 //    S^T and E^T (keys x queries), P^T, then dQ^T += K^T P^T.
 //  * dK/dV kernel: a workgroup owns 128 keys (K' and V' in registers) and
-//    streams Q and G with the per-query 1/l and delta/l.  Per 32-query
+//    streams Q and G with the per-query 1/l and delta/l (formed once per
+//    query by a small kernel before it, see born_bf16_d64_bwd_scal_kernel,
+//    and copied into LDS with each stage).  Per 32-query
 //    block: S and E (queries x keys), w/l and P, then dV^T += G^T (w/l) and
 //    dK^T += Q^T P.
 // Causal work is balanced by mirrored pairs of tiles, as in the forward.
@@ -65,6 +68,16 @@ constexpr int REGION = BS * ROWB;       // 8 KiB
 
 __device__ inline int swz_k(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 __device__ inline int swz_v(int row) { return (row & 3) << 1; }
+// One swizzle for a tile read both ways, free of bank conflicts for the
+// row-major operand reads (16 lanes on 16 rows, one chunk) and for the
+// transposing reads (rows 4 q .. 4 q + 3, four chunks): the even rows of
+// 16 take eight distinct slots, and so do the odd ones, and rows 4 q and
+// 4 q + 2 (likewise 4 q + 1 and 4 q + 3) differ in bit 2 of the slot.
+__device__ inline int swz_b(int row) {
+    const int i = (row >> 1) & 7;
+    return (((i & 1) << 2) | (i >> 1)) ^ ((row & 1) << 1);
+}
+enum Swizzle { SWZ_K, SWZ_V, SWZ_B };
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -107,7 +120,7 @@ __device__ inline void loads_done_barrier() {
 // slot c ^ swz(r).  Rows past T repeat row T - 1 (they are masked later).
 // NTH threads of the workgroup share the copy.
 template <int NTH>
-__device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, bool vswz, int tid,
+__device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, Swizzle sw, int tid,
                                     int wave) {
     constexpr int C = REGION / 16 / NTH;   // 16-byte chunks per thread
     static_assert(C * 16 * NTH == REGION, "staging split");
@@ -119,7 +132,7 @@ __device__ inline void stage_region(uint32_t region, const uint16_t *plane, int 
 #pragma unroll
     for (int e = 0; e < C; ++e) {
         const int row = (tid >> 3) + (NTH / 8) * e;
-        const int lc = slot ^ (vswz ? swz_v(row) : swz_k(row));
+        const int lc = slot ^ (sw == SWZ_B ? swz_b(row) : sw == SWZ_V ? swz_v(row) : swz_k(row));
         const int g = min(row, T - 1 - r0);   // row within the stage; < 64, so the offset is < 8 KiB
         const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NTH * 16 + wave * 1024));
         dma16(dst, rsrc, (uint32_t)(g * ROWB + 16 * lc));
@@ -143,6 +156,7 @@ __device__ inline void load_rows_b(const uint16_t *re, const uint16_t *im, int r
 struct Offsets {
     int koff[4];
     int voff[2];
+    int voffh[2];   // the second transposing read (8 rows on); swz_b tiles only
 };
 
 __device__ inline Offsets lane_offsets(int lane) {
@@ -159,10 +173,35 @@ __device__ inline Offsets lane_offsets(int lane) {
     return o;
 }
 
+// The same offsets for tiles staged once in the shared swizzle swz_b, whose
+// slot also depends on bit 3 of the row: the second transposing read of an
+// operand (rows 8 on) has offsets of its own.
+__device__ inline Offsets lane_offsets_b(int lane) {
+    Offsets o;
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.koff[j] = l32 * ROWB + (((2 * j + h) ^ swz_b(l32)) << 4);
+    const int G = lane >> 4, r = (lane >> 2) & 3, c4 = lane & 3;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+        const int lc = 4 * cc + 2 * (G & 1) + (c4 >> 1);
+        o.voff[cc] = (4 * h + r) * ROWB + ((lc ^ swz_b(4 * h + r)) << 4) + ((c4 & 1) << 3);
+        o.voffh[cc] = (4 * h + r + 8) * ROWB + ((lc ^ swz_b(4 * h + r + 8)) << 4) + ((c4 & 1) << 3);
+    }
+    return o;
+}
+
 // 32 channels x 16 rows A operand through two transposing reads.
 __device__ inline bf16x8 tr_operand(const char *p) {
     const u32x2 lo = ds_read_tr(p);
     const u32x2 hi = ds_read_tr(p + 8 * ROWB);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// The same for a swz_b tile: rows 0-7 and 8-15 of the step at their own offsets.
+__device__ inline bf16x8 tr_operand_b(const char *base, int lo_off, int hi_off) {
+    const u32x2 lo = ds_read_tr(base + lo_off);
+    const u32x2 hi = ds_read_tr(base + hi_off);
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
@@ -225,7 +264,7 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
         const uint32_t base = lds0 + (uint32_t)((s & 1) * QREG * REGION);
 #pragma unroll
         for (int r = 0; r < QREG; ++r)
-            stage_region<QNT>(base + r * REGION, stage_planes[r], s * BS, T, r >= 4, tid, wave);
+            stage_region<QNT>(base + r * REGION, stage_planes[r], s * BS, T, r >= 4 ? SWZ_V : SWZ_K, tid, wave);
     };
 
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
@@ -373,12 +412,45 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
 }
 
 // ---------------------------------------------------------------------------- dK, dV
-constexpr int KREG = 8;   // Q re, Q im, G re, G im (row-major), the same four (transposing)
+constexpr int KREG = 4;   // Q re, Q im, G re, G im, each staged once (swizzle swz_b)
+
+// Per-query scalars of the key-side kernel, (1 / l, delta / l) as a float
+// pair per row, formed once before it (four threads per query, the
+// channels split as 4 x 16) rather than in every workgroup of keys.  They
+// are written into the dq_re buffer, which the query-side kernel, run after
+// the key-side one, then overwrites.
+__global__ __launch_bounds__(256) void born_bf16_d64_bwd_scal_kernel(BwdProblem p, int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    const int sp = threadIdx.x & 3;
+    const uint16_t *src[4] = {reinterpret_cast<const uint16_t *>(p.g_re), reinterpret_cast<const uint16_t *>(p.g_im),
+                              reinterpret_cast<const uint16_t *>(p.o_re), reinterpret_cast<const uint16_t *>(p.o_im)};
+    u32x4 sx[8];   // G re, G im, O re, O im: two 16-byte chunks each
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < rows) v = *reinterpret_cast<const u32x4 *>(src[i >> 1] + row * D + 16 * sp + 8 * (i & 1));
+        sx[i] = v;
+    }
+    float dl = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dl += bf_lo(sx[i][e]) * bf_lo(sx[4 + i][e]) + bf_hi(sx[i][e]) * bf_hi(sx[4 + i][e]) +
+                  bf_lo(sx[2 + i][e]) * bf_lo(sx[6 + i][e]) + bf_hi(sx[2 + i][e]) * bf_hi(sx[6 + i][e]);
+    dl += __shfl_xor(dl, 1);
+    dl += __shfl_xor(dl, 2);
+    if (sp == 0 && row < rows) {
+        const float l = p.row_den[row];
+        const float inv = l != 0.f ? 1.f / l : 0.f;
+        reinterpret_cast<f32x2 *>(p.dq_re)[row] = f32x2{inv, dl * inv};
+    }
+}
 
 template <bool DECAY>
 __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p, int nkt, int nwork) {
     __shared__ __align__(16) char lds[2 * KREG * REGION];
-    __shared__ __align__(16) float scal[2][2][BS];   // [buffer][1/l, delta/l][query of the stage]
+    __shared__ __align__(16) float scal[2][2 * BS];   // [buffer][(1/l, delta/l) of each query of the stage]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -391,44 +463,21 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 
     const int64_t head = (int64_t)bh * T * D;
     auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + head; };
-    const uint16_t *stage_planes[KREG] = {plane(p.q_re), plane(p.q_im), plane(p.g_re), plane(p.g_im),
-                                          plane(p.q_re), plane(p.q_im), plane(p.g_re), plane(p.g_im)};
-    const uint16_t *ore = plane(p.o_re), *oim = plane(p.o_im), *gre = plane(p.g_re), *gim = plane(p.g_im);
+    const uint16_t *stage_planes[KREG] = {plane(p.q_re), plane(p.q_im), plane(p.g_re), plane(p.g_im)};
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char *)lds;
-    const Offsets off = lane_offsets(lane);
+    const Offsets off = lane_offsets_b(lane);
 
-    // per-query scalars of a stage: thread -> query tid / 4, channels 16 (tid % 4) .. + 16
-    const int sq = tid >> 2, sp = tid & 3;
-    u32x4 sx[8];   // G re, G im, O re, O im: two 16-byte chunks each
-    auto scal_load = [&](int q0) {
-        const int q = q0 + sq;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t *src = (i >> 1) == 0 ? gre : (i >> 1) == 1 ? gim : (i >> 1) == 2 ? ore : oim;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (q < T) v = *reinterpret_cast<const u32x4 *>(src + (int64_t)q * D + 16 * sp + 8 * (i & 1));
-            sx[i] = v;
-        }
-    };
-    auto scal_store = [&](int q0, int buf) {
-        float dl = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dl += bf_lo(sx[i][e]) * bf_lo(sx[4 + i][e]) + bf_hi(sx[i][e]) * bf_hi(sx[4 + i][e]) +
-                      bf_lo(sx[2 + i][e]) * bf_lo(sx[6 + i][e]) + bf_hi(sx[2 + i][e]) * bf_hi(sx[6 + i][e]);
-        dl += __shfl_xor(dl, 1);
-        dl += __shfl_xor(dl, 2);
-        if (sp == 0) {
-            const int q = q0 + sq;
-            float inv = 0.f;
-            if (q < T) {
-                const float l = p.row_den[(int64_t)bh * T + q];
-                inv = l != 0.f ? 1.f / l : 0.f;
-            }
-            scal[buf][0][sq] = inv;
-            scal[buf][1][sq] = dl * inv;
+    // the stage's per-query scalars (64 float pairs, 512 bytes) from the pairs
+    // written before this kernel, by waves 0 and 1 (64 lanes x 4 bytes each);
+    // pairs past T read as zero
+    const char *scal_src = reinterpret_cast<const char *>(p.dq_re) + (int64_t)bh * T * 8;
+    auto scal_issue = [&](int q0, int buf) {
+        if (wave < 2) {
+            const int64_t left = (int64_t)(T - q0) * 8;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(scal_src + (int64_t)q0 * 8), 0, (int)(left < 512 ? left : 512), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(&scal[buf][0] + 64 * wave), 4,
+                                                     (uint32_t)(256 * wave + 4 * lane), 0, 0, 0);
         }
     };
 
@@ -473,11 +522,14 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         // weights of register group g: register r of lane half h is query
         // 8 (r/4) + 4 h + r % 4 of the block
         // DECAY: qb0 is the block's first query; the factor gamma^(query - key)
-        auto weight_group = [&](const float *sc_inv, const float *sc_dinv, int sb, int g, bool masked, int lo,
+        auto weight_group = [&](const float *sc, int sb, int g, bool masked, int lo,
                                 int hi, const f32x16 &sr, const f32x16 &si, const f32x16 &e, uint32_t (&aw)[8],
                                 uint32_t (&pr)[8], uint32_t (&pi)[8], int qb0) {
-            const f32x4 iv = *reinterpret_cast<const f32x4 *>(sc_inv + 32 * sb + 8 * g + 4 * h);
-            const f32x4 di = *reinterpret_cast<const f32x4 *>(sc_dinv + 32 * sb + 8 * g + 4 * h);
+            // (1/l, delta/l) of queries 32 sb + 8 g + 4 h + c, c = 0 .. 3
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sc + 2 * (32 * sb + 8 * g + 4 * h));
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sc + 2 * (32 * sb + 8 * g + 4 * h) + 4);
+            const f32x4 iv = {x0[0], x0[2], x1[0], x1[2]};
+            const f32x4 di = {x0[1], x0[3], x1[1], x1[3]};
             const int n0 = qb0 + 8 * g + 4 * h - key;   // distance of register c = 0
             float a[4], d2[4];
 #pragma unroll
@@ -528,19 +580,20 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         // dV^T += G'^T (w/l);  dK^T: Re += Q_r P_r + Q_i P_i,  Im += Q_i P_r - Q_r P_i
         auto grad_step = [&](const char *st, int sb, int j, const GradOps &w) {
             const int m = j >> 1, ct = j & 1;
-            const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
-            const bf16x8 grt = tr_operand(st + 6 * REGION + o);
-            const bf16x8 git = tr_operand(st + 7 * REGION + o);
+            const char *b = st + (32 * sb + 16 * m) * ROWB;
+            const int lo = off.voff[ct], hi = off.voffh[ct];
+            const bf16x8 grt = tr_operand_b(b + 2 * REGION, lo, hi);
+            const bf16x8 git = tr_operand_b(b + 3 * REGION, lo, hi);
             dv[ct] = mfma(grt, w.ab[m], dv[ct]);
             dv[2 + ct] = mfma(git, w.ab[m], dv[2 + ct]);
-            const bf16x8 qrt = tr_operand(st + 4 * REGION + o);
-            const bf16x8 qit = tr_operand(st + 5 * REGION + o);
+            const bf16x8 qrt = tr_operand_b(b, lo, hi);
+            const bf16x8 qit = tr_operand_b(b + REGION, lo, hi);
             dk[ct] = mfma(qrt, w.prb[m], dk[ct]);
             dk[ct] = mfma(qit, w.pib[m], dk[ct]);
             dk[2 + ct] = mfma(qit, w.prb[m], dk[2 + ct]);
             dk[2 + ct] = mfma(qrt, w.pnb[m], dk[2 + ct]);
         };
-        auto query_block = [&](const char *st, const float *sc_inv, const float *sc_dinv, int sb, int qb0, bool masked,
+        auto query_block = [&](const char *st, const float *sc, int sb, int qb0, bool masked,
                                int lo, int hi) {
             f32x16 sr = f32x16{}, si = f32x16{}, e = f32x16{};
 #pragma unroll
@@ -548,7 +601,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             uint32_t aw[8], pr[8], pi[8];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                weight_group(sc_inv, sc_dinv, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi, qb0);
+                weight_group(sc, sb, g, masked, lo, hi, sr, si, e, aw, pr, pi, qb0);
             const GradOps w = grad_ops(aw, pr, pi);
 #pragma unroll
             for (int j = 0; j < 4; ++j) grad_step(st, sb, j, w);
@@ -556,7 +609,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
         // both blocks of a stage with no mask: block 1's score products run
         // beside block 0's weight arithmetic, and block 0's gradient products
         // beside block 1's weight arithmetic
-        auto full_stage = [&](const char *st, const float *sc_inv, const float *sc_dinv, int qbase) {
+        auto full_stage = [&](const char *st, const float *sc, int qbase) {
             f32x16 sr0 = f32x16{}, si0 = f32x16{}, e0 = f32x16{};
             f32x16 sr1 = f32x16{}, si1 = f32x16{}, e1 = f32x16{};
 #pragma unroll
@@ -572,7 +625,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             for (int g = 0; g < 4; ++g) {
                 score_step(st, 1, 2 * g, sr1, si1, e1);
                 score_step(st, 1, 2 * g + 1, sr1, si1, e1);
-                weight_group(sc_inv, sc_dinv, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0, qbase);
+                weight_group(sc, 0, g, false, 0, 31, sr0, si0, e0, aw0, pr0, pi0, qbase);
             }
             const GradOps w0 = grad_ops(aw0, pr0, pi0);
 #pragma unroll
@@ -588,7 +641,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 grad_step(st, 0, j, w0);
-                weight_group(sc_inv, sc_dinv, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1, qbase + 32);
+                weight_group(sc, 1, j, false, 0, 31, sr1, si1, e1, aw1, pr1, pi1, qbase + 32);
             }
             const GradOps w1 = grad_ops(aw1, pr1, pi1);
 #pragma unroll
@@ -611,14 +664,13 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             const uint32_t base = lds0 + (uint32_t)((s & 1) * KREG * REGION);
 #pragma unroll
             for (int r = 0; r < KREG; ++r)
-                stage_region<NT>(base + r * REGION, stage_planes[r], qs + s * BS, T, r >= 4, tid, wave);
+                stage_region<NT>(base + r * REGION, stage_planes[r], qs + s * BS, T, SWZ_B, tid, wave);
+            scal_issue(qs + s * BS, s & 1);
         };
 
         loads_done_barrier();   // the previous key tile is done with both buffers
         if (nstages > 0) {
             issue_stage(0);
-            scal_load(qs);
-            scal_store(qs, 0);
         }
         // One stage: wait for it, issue the next one, run its two query blocks.
         // ALL_FULL drops the mask and skip branches (see below).
@@ -627,11 +679,10 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             const bool next = s + 1 < nstages;
             if (next) {
                 issue_stage(s + 1);
-                scal_load(qs + (s + 1) * BS);
             }
             const char *st = lds + (s & 1) * KREG * REGION;
-            const float *si2 = scal[s & 1][0], *sdi = scal[s & 1][1];
-            if (all_full) full_stage(st, si2, sdi, qs + s * BS);
+            const float *sc = scal[s & 1];
+            if (all_full) full_stage(st, sc, qs + s * BS);
 #pragma unroll
             for (int sb = 0; sb < BS / 32; ++sb) {
                 if (all_full) continue;
@@ -639,14 +690,13 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
                 const bool skip = qb0 >= T || kw0 >= T || (p.causal && qb0 + 31 < kw0);
                 const bool full = (!p.causal || qb0 >= kw0 + 31) && qb0 + 32 <= T && kw0 + 32 <= T;
                 if (full) {
-                    query_block(st, si2, sdi, sb, qb0, false, 0, 31);
+                    query_block(st, sc, sb, qb0, false, 0, 31);
                 } else if (!skip) {
                     const int lo = p.causal ? key - qb0 : 0;
                     const int hi = key < T ? T - 1 - qb0 : -1;
-                    query_block(st, si2, sdi, sb, qb0, true, lo, hi);
+                    query_block(st, sc, sb, qb0, true, lo, hi);
                 }
             }
-            if (next) scal_store(qs + (s + 1) * BS, (s + 1) & 1);
         };
         // Stages [s_lo, s_hi) hold only queries inside T that see every key of
         // the tile (causal: at least BT - 1 past its first key), so they run in
@@ -687,6 +737,12 @@ hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p) {
 }
 
 hipError_t launch_born_bf16_d64_bwd_dkdv(const BwdProblem &p) {
+    const int64_t rows = (int64_t)p.BH * p.T;
+    if (rows > 0) {
+        if ((rows + 63) / 64 > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(born_bf16_d64_bwd_scal_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, p.stream, p,
+                           rows);
+    }
     const int nkt = (p.T + BT - 1) / BT;
     const int nwork = p.causal ? (nkt + 1) / 2 : nkt;
     const int64_t blocks = (int64_t)p.BH * nwork;

@@ -258,8 +258,11 @@ cattn_status cattn_pct_gate_fwd(int layout,
  *              sum_j ds[i,j] per query row; their sum is dL/d(bias).
  * The outputs must not overlap any input or each other.  The arithmetic is
  * fp32 for both layouts (bf16 inputs are widened, outputs rounded to bf16).
- * Each call enqueues two kernels (key-side and query-side gradients); it
- * allocates nothing, uses no atomics and is deterministic.
+ * Each call enqueues two kernels (key-side and query-side gradients), and on
+ * the bf16 Born path at d_h = 64 a third before them that writes per-query
+ * scalars into the dq_re buffer for the key-side kernel (the query-side
+ * kernel then overwrites it); it allocates nothing, uses no atomics and is
+ * deterministic.
  */
 cattn_status cattn_born_bwd(int layout,
                             const void *q_re, const void *q_im,

@@ -49,8 +49,9 @@ def test_bf16_backward_lds_direct_loads_use_sgpr_base(tmp_path):
     lds_loads = [l.strip() for l in asm.splitlines() if re.search(r"\bload_lds_dword|\blds$", l.strip())]
     assert lds_loads, "no LDS-direct loads found"
     for l in lds_loads:
-        # buffer_load_dwordx4 <voffset>, s[..], <soffset> offen lds: one 32-bit VGPR offset, SGPR base
-        assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], \S+ offen lds$", l), l
+        # buffer_load_dword[x4] <voffset>, s[..], <soffset> offen lds: one 32-bit VGPR offset, SGPR
+        # base (x4: the 16-byte stage chunks; dword: the per-query scalar pairs of a stage)
+        assert re.match(r"buffer_load_dword(x4)? v\d+, s\[\d+:\d+\], \S+ offen lds$", l), l
 
 
 def test_bf16_backward_stage_offsets_stay_in_one_stage():
