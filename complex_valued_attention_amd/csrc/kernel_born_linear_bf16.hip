@@ -88,7 +88,9 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem p, int ntile_t) {
-    __shared__ __align__(16) uint16_t Sb[2][NM][SROW];   // staged state rows (bf16), double buffered
+    // staged state rows (bf16), double buffered; rows NM .. 32 NTILE - 1 stay zero, so
+    // the Z tile (row 128 and 31 zero rows) is read like the others
+    __shared__ __align__(16) uint16_t Sb[2][32 * NTILE][SROW];
     __shared__ uint32_t Qs[TOK][QROW];                   // (Re, Im) bf16 pairs of the tile's tokens
 
     const int tid = threadIdx.x;
@@ -109,6 +111,10 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
     const uint16_t *qre = reinterpret_cast<const uint16_t *>(p.q_re);
     const uint16_t *qim = reinterpret_cast<const uint16_t *>(p.q_im);
 
+    for (int i = tid; i < 2 * (32 * NTILE - NM) * (SROW / 2); i += MNT) {
+        const int b = i / ((32 * NTILE - NM) * (SROW / 2)), j = i % ((32 * NTILE - NM) * (SROW / 2));
+        reinterpret_cast<uint32_t *>(&Sb[b][NM][0])[j] = 0u;
+    }
     // ---- stage the tile's queries as (Re, Im) pairs; rows past T are zero
     for (int i = tid; i < TOK * (D / 8); i += MNT) {
         const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
@@ -183,10 +189,12 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[s][ti][r] = 0.f;
 
-    const u32x4 zero4 = {0, 0, 0, 0};
     // feature row a: products from Sb[a % 2]; rows a + 2 load into the set that held
     // row a, rows a + 1 (loaded an iteration ago) go to the other buffer
-    auto feature_row = [&](int a, float4 (&ld)[SLOADS], const float4 (&sv)[SLOADS]) {
+    // feature row a of the 16-row block MB (a = 16 MB + 0 .. 15): steps m < MB lie
+    // wholly below the diagonal, steps m > MB wholly above it, step MB holds it
+    auto feature_row = [&](auto MB, int a, float4 (&ld)[SLOADS], const float4 (&sv)[SLOADS]) {
+        constexpr int mb = decltype(MB)::value;
         const int buf = a & 1;
         if (a + 2 < D) load_rows(a + 2, ld);
         uint32_t qa[TPW], qr[TPW];
@@ -200,21 +208,19 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
             // state operand: rows 32 ti + l32, features 16 m + 8 h .. + 7 of row a
             bf16x8 sa[NTILE];
 #pragma unroll
-            for (int ti = 0; ti < NTILE - 1; ++ti)
+            for (int ti = 0; ti < NTILE; ++ti)
                 sa[ti] = *reinterpret_cast<const bf16x8 *>(&Sb[buf][32 * ti + l32][16 * m + 8 * h]);
-            sa[NTILE - 1] = l32 == 0 ? *reinterpret_cast<const bf16x8 *>(&Sb[buf][2 * D][16 * m + 8 * h])
-                                     : as_bf16x8(zero4);
             // steps wholly above (a < 16 m) or below (a > 16 m + 15) the diagonal take one
             // operand for all their features; in the step holding the diagonal (at position
             // rd = a - 16 m) the lane's feature 8 h + e lies above it when 8 h + e > rd, and
             // the diagonal feature itself takes half the upper value (q_b is doubled)
             const int rd = a - 16 * m;
-            const bool mixed = rd >= 0 && rd <= 15;
+            const bool mixed = m == mb;
 #pragma unroll
             for (int s = 0; s < TPW; ++s) {
                 float f[8];
                 if (!mixed) {
-                    const uint32_t xs = rd < 0 ? qa[s] : qr[s];
+                    const uint32_t xs = m > mb ? qa[s] : qr[s];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) f[e] = dot2(xs, qb[s][8 * m + e]);
                 } else {
@@ -237,10 +243,17 @@ __global__ __launch_bounds__(MNT) void born_merge_bf16_d64_kernel(LinearProblem 
         if (a + 1 < D) store_rows(buf ^ 1, sv);
         __syncthreads();
     };
-    for (int a = 0; a < D; a += 2) {
-        feature_row(a, sreg0, sreg1);
-        feature_row(a + 1, sreg1, sreg0);
-    }
+    auto block16 = [&](auto MB) {
+        constexpr int mb = decltype(MB)::value;
+        for (int a = 16 * mb; a < 16 * mb + 16; a += 2) {
+            feature_row(MB, a, sreg0, sreg1);
+            feature_row(MB, a + 1, sreg1, sreg0);
+        }
+    };
+    block16(std::integral_constant<int, 0>{});
+    block16(std::integral_constant<int, 1>{});
+    block16(std::integral_constant<int, 2>{});
+    block16(std::integral_constant<int, 3>{});
 
     // ---- epilogue: lane (token, half h) holds rows n = 32 ti + 8 (r / 4) + 4 h + r % 4
     uint16_t *ore = reinterpret_cast<uint16_t *>(p.o_re);
