@@ -329,9 +329,13 @@ def main_step(args, w):
 
 def main_linear(args, w):
     """A whole causal Born sequence in chunks of C tokens with a carried state:
-    per chunk the quadratic kernel over the chunk, the merge of the incoming
-    state, and the state update; beside it the quadratic kernel over the whole
-    sequence on the same inputs."""
+    the quadratic kernel within each chunk, then per chunk the merge of the
+    incoming state and the state update; beside it the quadratic kernel over
+    the whole sequence on the same inputs.  The within-chunk products do not
+    depend on the state, so when C divides T they run as one launch over all
+    chunks (a strided view of the sequence as [chunks, B*H, C, d_h], the
+    outputs chunk-major), which fills the chip where one chunk of few heads
+    would not; otherwise one launch per chunk."""
     import oracle
     import torch
     from complex_valued_attention_amd import cattn, inputs as gen
@@ -346,18 +350,42 @@ def main_linear(args, w):
     B, H, T, d, C = w.B, w.H, w.T, w.d_h, args.chunk
     nc = (T + C - 1) // C
     chunks = [tuple(_chunk(x, i * C, min(T, (i + 1) * C)) for x in (q, k, v)) for i in range(nc)]
-    outs = [cattn._like(c[0]) for c in chunks]
-    dens = [torch.empty(B * H * min(C, T - i * C), dtype=torch.float32, device="cuda") for i in range(nc)]
+    batched = T % C == 0 and nc > 1
+    if batched:
+        # chunk-major views: operand element (c, b*H + h, t, :) is row c*C + t of head (b, h)
+        def view(x):
+            if isinstance(x, tuple):
+                return tuple(view(p) for p in x)
+            return x.as_strided((nc, B * H, C, d), (C * d, T * d, d, 1))
+        qv, kv, vv = view(q), view(k), view(v)
+        fresh = lambda x: torch.empty((nc, B * H, C, d), dtype=x.dtype, device=x.device)
+        out_all = tuple(fresh(p) for p in qv) if isinstance(qv, tuple) else fresh(qv)
+        den_all = torch.empty(nc * B * H * C, dtype=torch.float32, device="cuda")
+        pick = lambda x, i: tuple(p[i].view(B, H, C, d) for p in x) if isinstance(x, tuple) else x[i].view(B, H, C, d)
+        outs = [pick(out_all, i) for i in range(nc)]
+        dens = [den_all[i * B * H * C:(i + 1) * B * H * C] for i in range(nc)]
+    else:
+        outs = [cattn._like(c[0]) for c in chunks]
+        dens = [torch.empty(B * H * min(C, T - i * C), dtype=torch.float32, device="cuda") for i in range(nc)]
     S = cattn.born_state_buffer(B, H, d)
     stream = torch.cuda.current_stream()
     kinds = ("fwd", "merge", "state")
 
     def chunked(evs=None):
+        if batched:
+            marks = []
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+            cattn.born_fwd(qv, kv, vv, causal=True, out=out_all, row_den=den_all)
+            if evs is not None:
+                marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+                evs.append(marks + [marks[-1], marks[-1]])
         for i, (qc, kc, vc) in enumerate(chunks):
             marks = []
             if evs is not None:
                 marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-            cattn.born_fwd(qc, kc, vc, causal=True, out=outs[i], row_den=dens[i])
+            if not batched:
+                cattn.born_fwd(qc, kc, vc, causal=True, out=outs[i], row_den=dens[i])
             if evs is not None:
                 marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
             if i:
@@ -438,7 +466,8 @@ def main_linear(args, w):
            "dtype": "bf16" if w.layout == "bf16" else "f32",
            "data": "synthetic (seeded complex Gaussian, unit-norm rotary Q/K)" if w.rotary else "synthetic",
            "config": {"workload": w.name, "pass": "linear", "B": B, "H": H, "T": T, "d_h": d, "layout": w.layout,
-                      "chunk": C, "chunks": nc},
+                      "chunk": C, "chunks": nc, "within_chunk": "one launch over all chunks" if batched
+                      else "one launch per chunk"},
            "quadratic_ms": ms_quad, "speedup_vs_quadratic": ms_quad / ms,
            "parts_ms": part,
            "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
