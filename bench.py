@@ -49,6 +49,17 @@ MEASURED_TRAFFIC = {
         "sha256": "7c6c753ec257cb2bcb7994a9cefdb6a4d9be0ae4b53adfd20d83b712767e6259",
         "bytes": 930.9e6,   # read 796.7 MB + write 134.2 MB
     },
+    # the carried-state kernels of --pass linear at chunk 4096 (mean per launch over a pass)
+    "linear-state:born_causal_bf16_b1h16t32768d64_rotary:4096": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
+        "sha256": "edb94da4d42529beee88a404769fb38cbc9b91943c03cc8dbe8a342660201698",
+        "bytes": 96.6e6,    # read 62.8 MB + write 33.8 MB
+    },
+    "linear-merge:born_causal_bf16_b1h16t32768d64_rotary:4096": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
+        "sha256": "edb94da4d42529beee88a404769fb38cbc9b91943c03cc8dbe8a342660201698",
+        "bytes": 85.4e6,    # read 67.9 MB + write 17.5 MB
+    },
 }
 
 
@@ -472,7 +483,7 @@ def main_linear(args, w):
            "parts_ms": part,
            "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                         "frac": achieved / peak,
-                        "traffic": measured_traffic(f"linear:{w.name}:{C}") if dom == "state" else None,
+                        "traffic": measured_traffic(f"linear-{dom}:{w.name}:{C}"),
                         "kernel": kname, "kernel_ms_mean": dom_ms,
                         "flops_per_launch": dom_flops},
            "gpu_vs_quadratic_rowwise_rel_err": err_quad,
