@@ -89,7 +89,7 @@ def kernel_name(w) -> str:
     """The HIP kernel the library dispatches for this workload."""
     if w.op == "born" and w.layout == "bf16":
         return "born_bf16_d64_kernel" if w.d_h == 64 else "born_bf16_mfma_kernel"
-    if w.d_h in (16, 32, 64):   # complex64, and PCT on bf16 planes
+    if w.d_h in (16, 32, 64, 128):   # complex64, and PCT on bf16 planes
         return "attn_f32_mfma16_kernel"
     return "generic_fwd_kernel"
 

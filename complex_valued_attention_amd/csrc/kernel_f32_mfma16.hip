@@ -64,7 +64,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 8;          // waves per workgroup: two row blocks of four tiles
 constexpr int NT = 64 * NW;    // threads
-constexpr int NST = 256;       // threads that stage K and V (the first four waves)
+constexpr int NST = 256;       // threads that stage K and V (the first four waves; all eight at d = 128)
 constexpr int TQ = 16;         // queries per wave tile
 constexpr int BM = TQ * 4;     // queries per row block
 constexpr int BN = 32;         // keys per LDS stage (two 16-key blocks)
@@ -78,8 +78,13 @@ struct Cfg16 {
     static constexpr int ROW = KD + 4;      // padded LDS row (floats) of K' and V'
     static constexpr int STAGE = 2 * BN * ROW + BN;   // K', V', per-key inverse norms
     static constexpr int LDS_BYTES = 2 * STAGE * 4;
-    static constexpr int LPK = NST / BN;              // staging lanes per key (8)
+    static constexpr int NSTG = D >= 128 ? 2 * NST : NST;   // staging threads
+    static constexpr int LPK = NSTG / BN;             // staging lanes per key (8; 16 at d = 128)
     static constexpr int CPT = (KD / 4) / LPK;        // float4 chunks per staging lane
+    // d = 128: the (Im, -Re) query operand is formed as it is used rather than
+    // held (64 more registers), and a lane's K' slice is read in pieces of 16
+    static constexpr bool QIM = D < 128;
+    static constexpr int KP = D < 128 ? KQ : 16;      // K' floats per LDS read batch
 };
 
 // n floats from LDS into registers with the widest reads that fit
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
     const int qt0 = m0 + TQ * (wave & 3);   // first query of this wave's tile
     const int qrow = qt0 + j16;
     const bool live = rb >= 0 && qt0 < T;
-    const bool stager = tid < NST;           // wave-uniform
+    const bool stager = tid < C::NSTG;       // wave-uniform
     // d = 64: value rows i with ((i >> 2) ^ (i >> 3)) odd take their slice's
     // halves swapped; as A operand row i = j16, as output row i = 4 g + r
     const int vsw = C::CPL == 8 ? 4 * (((j16 >> 2) ^ (j16 >> 3)) & 1) : 0;
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
 
     // query operands q', q''' over this lane group's quarter of the row, and
     // PCT's sqrt(d_h) / |q| (0 for a zero row)
-    float qre[C::KQ], qim[C::KQ];
+    float qre[C::KQ], qim[C::QIM ? C::KQ : 1];
     float rq = 0.f;
     auto load_q = [&](int qt, bool ok) {
         const int qr = qt + j16;
@@ -276,10 +281,12 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             qre[4 * i + 2] = x[i][2];
             qre[4 * i + 3] = x[i][3];
             // (Im, -Re) per complex element; a quarter starts on an element boundary
-            qim[4 * i] = x[i][1];
-            qim[4 * i + 1] = -x[i][0];
-            qim[4 * i + 2] = x[i][3];
-            qim[4 * i + 3] = -x[i][2];
+            if constexpr (C::QIM) {
+                qim[4 * i] = x[i][1];
+                qim[4 * i + 1] = -x[i][0];
+                qim[4 * i + 2] = x[i][3];
+                qim[4 * i + 3] = -x[i][2];
+            }
         }
         if (OP != OP_BORN) {
             float ss = 0.f;
@@ -401,13 +408,28 @@ __global__ __launch_bounds__(NT) void attn_f32_mfma16_kernel(Problem p, int nrb,
             const bool diag = p.causal && kb0 == qt_cur;
 
             // S^T for 16 keys x 16 queries
-            float ka[C::KQ];
-            lds_row<C::KQ>(ks + (16 * sb + j16) * C::ROW + g * C::KQ, ka);
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
+            // d = 128: the sign flip of -Re q made opaque here, so that it is
+            // applied per product and not hoisted into 32 more registers
+            uint32_t sgn = 0x80000000u;
+            if constexpr (!C::QIM) __asm__ __volatile__("" : "+v"(sgn));
 #pragma unroll
-            for (int s2 = 0; s2 < C::KQ; ++s2) {
-                sr = mfma16(ka[s2], qre[s2], sr);
-                if (OP == OP_BORN) si = mfma16(ka[s2], qim[s2], si);
+            for (int p0 = 0; p0 < C::KQ; p0 += C::KP) {
+                float ka[C::KP];
+                lds_row<C::KP>(ks + (16 * sb + j16) * C::ROW + g * C::KQ + p0, ka);
+#pragma unroll
+                for (int s3 = 0; s3 < C::KP; ++s3) {
+                    const int s2 = p0 + s3;
+                    sr = mfma16(ka[s3], qre[s2], sr);
+                    if (OP == OP_BORN) {
+                        float qi;
+                        if constexpr (C::QIM)
+                            qi = qim[s2];
+                        else   // (Im, -Re): element s2 + 1 (even s2), or minus element s2 - 1 (odd)
+                            qi = (s2 & 1) ? __uint_as_float(__float_as_uint(qre[s2 - 1]) ^ sgn) : qre[s2 + 1];
+                        si = mfma16(ka[s3], qi, si);
+                    }
+                }
             }
 
             // weights: register r is key 4 g + r of the block
@@ -531,9 +553,10 @@ hipError_t launch_d16(const Problem &p) {
 }  // namespace
 
 // complex64 (every operator) and bf16 planes (the PCT cells: bf16 Born has
-// its own bf16 matrix-core kernels) at widths 16, 32, 64
+// its own bf16 matrix-core kernels) at widths 16, 32, 64 and 128
 bool supports_f32_mfma16(const Problem &p) {
-    return (p.d == 16 || p.d == 32 || p.d == 64) && (p.layout == LAYOUT_C64 || p.op != OP_BORN) && p.aligned16;
+    return (p.d == 16 || p.d == 32 || p.d == 64 || p.d == 128) && (p.layout == LAYOUT_C64 || p.op != OP_BORN) &&
+           p.aligned16;
 }
 
 hipError_t launch_f32_mfma16(const Problem &p) {
@@ -541,6 +564,7 @@ hipError_t launch_f32_mfma16(const Problem &p) {
         case 16: return launch_d16<16>(p);
         case 32: return launch_d16<32>(p);
         case 64: return launch_d16<64>(p);
+        case 128: return launch_d16<128>(p);
         default: return hipErrorNotSupported;
     }
 }

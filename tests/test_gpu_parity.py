@@ -136,9 +136,10 @@ def test_parity_edge_shapes(op, layout, causal, B, H, T, d):
 # width
 # bf16 planes take the same kernel for the PCT cells (widened to fp32 on load)
 PAIRS = [(op, causal, T, d, "c64") for op in ("born", "pct") for T in (64, 65, 191, 256, 449, 513)
-         for d in (16, 32, 64) for causal in (True,)] + \
-        [(op, False, T, d, "c64") for op in ("born", "pct") for T in (65, 191, 513) for d in (16, 64)] + \
-        [("pct", causal, T, d, "bf16") for causal in (True, False) for T in (65, 191, 513) for d in (16, 32, 64)]
+         for d in (16, 32, 64, 128) for causal in (True,)] + \
+        [(op, False, T, d, "c64") for op in ("born", "pct") for T in (65, 191, 513) for d in (16, 64, 128)] + \
+        [("pct", causal, T, d, "bf16") for causal in (True, False) for T in (65, 191, 513)
+         for d in (16, 32, 64, 128)]
 
 
 @pytest.mark.parametrize("op,causal,T,d,layout", PAIRS)
