@@ -16,9 +16,9 @@
 // one plane per 8 KiB region, staged straight from global memory into LDS,
 // A operands of row-major tiles read as 16-byte chunks, and the transposing
 // LDS read (ds_read_b64_tr_b16) for tiles used with their rows as the
-// contraction index.  A tile needed both ways is staged once, in a swizzle
-// that keeps both kinds of read free of bank conflicts (swz_b; the dQ
-// kernel still stages K twice, in the forward's two swizzles).  Products are
+// contraction index.  Every tile is staged once, in a swizzle that keeps
+// both kinds of read free of bank conflicts (swz_b), whether a kernel reads
+// it one way (V in the dQ kernel) or both (K; Q and G).  Products are
 // formed with the streamed rows along the MFMA's k-dimension's partner, so
 // each lane's 16 accumulator values are directly the bf16 B operand of the
 // next product (no shuffles).
@@ -66,8 +66,6 @@ constexpr int BS = 64;                  // streamed rows per LDS stage
 constexpr int ROWB = 2 * D;             // bytes per row of one plane
 constexpr int REGION = BS * ROWB;       // 8 KiB
 
-__device__ inline int swz_k(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
-__device__ inline int swz_v(int row) { return (row & 3) << 1; }
 // One swizzle for a tile read both ways, free of bank conflicts for the
 // row-major operand reads (16 lanes on 16 rows, one chunk) and for the
 // transposing reads (rows 4 q .. 4 q + 3, four chunks): the even rows of
@@ -77,7 +75,6 @@ __device__ inline int swz_b(int row) {
     const int i = (row >> 1) & 7;
     return (((i & 1) << 2) | (i >> 1)) ^ ((row & 1) << 1);
 }
-enum Swizzle { SWZ_K, SWZ_V, SWZ_B };
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -117,11 +114,10 @@ __device__ inline void loads_done_barrier() {
 }
 
 // Rows r0 .. r0 + 63 of one plane into one LDS region, chunk c of row r at
-// slot c ^ swz(r).  Rows past T repeat row T - 1 (they are masked later).
+// slot c ^ swz_b(r).  Rows past T repeat row T - 1 (they are masked later).
 // NTH threads of the workgroup share the copy.
 template <int NTH>
-__device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, Swizzle sw, int tid,
-                                    int wave) {
+__device__ inline void stage_region(uint32_t region, const uint16_t *plane, int r0, int T, int tid, int wave) {
     constexpr int C = REGION / 16 / NTH;   // 16-byte chunks per thread
     static_assert(C * 16 * NTH == REGION, "staging split");
     // the stage's first row as the uniform base (64-bit arithmetic, any T);
@@ -132,7 +128,7 @@ __device__ inline void stage_region(uint32_t region, const uint16_t *plane, int 
 #pragma unroll
     for (int e = 0; e < C; ++e) {
         const int row = (tid >> 3) + (NTH / 8) * e;
-        const int lc = slot ^ (sw == SWZ_B ? swz_b(row) : sw == SWZ_V ? swz_v(row) : swz_k(row));
+        const int lc = slot ^ swz_b(row);
         const int g = min(row, T - 1 - r0);   // row within the stage; < 64, so the offset is < 8 KiB
         const uint32_t dst = __builtin_amdgcn_readfirstlane(region + (uint32_t)(e * NTH * 16 + wave * 1024));
         dma16(dst, rsrc, (uint32_t)(g * ROWB + 16 * lc));
@@ -150,32 +146,17 @@ __device__ inline void load_rows_b(const uint16_t *re, const uint16_t *im, int r
     }
 }
 
-// Per-lane LDS offsets (the forward's): the A operand of k-step kk of a
-// row-major tile (row l32, logical chunk 2 (kk % 4) + h), and the
-// transposing read of a tile whose rows are the contraction index.
+// Per-lane LDS offsets in a swz_b tile: the A operand of k-step kk of a
+// row-major tile (row l32, logical chunk 2 (kk % 4) + h), and the two
+// transposing reads of a tile whose rows are the contraction index (rows
+// 0-7 and 8-15 of a 16-row step: the slot depends on bit 3 of the row, so
+// the second read has offsets of its own).
 struct Offsets {
     int koff[4];
     int voff[2];
-    int voffh[2];   // the second transposing read (8 rows on); swz_b tiles only
+    int voffh[2];
 };
 
-__device__ inline Offsets lane_offsets(int lane) {
-    Offsets o;
-    const int l32 = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o.koff[j] = l32 * ROWB + (((2 * j + h) ^ swz_k(l32)) << 4);
-    const int G = lane >> 4, r = (lane >> 2) & 3, c4 = lane & 3;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-        const int lc = 4 * cc + 2 * (G & 1) + (c4 >> 1);
-        o.voff[cc] = (4 * h + r) * ROWB + ((lc ^ (r << 1)) << 4) + ((c4 & 1) << 3);
-    }
-    return o;
-}
-
-// The same offsets for tiles staged once in the shared swizzle swz_b, whose
-// slot also depends on bit 3 of the row: the second transposing read of an
-// operand (rows 8 on) has offsets of its own.
 __device__ inline Offsets lane_offsets_b(int lane) {
     Offsets o;
     const int l32 = lane & 31, h = lane >> 5;
@@ -191,14 +172,8 @@ __device__ inline Offsets lane_offsets_b(int lane) {
     return o;
 }
 
-// 32 channels x 16 rows A operand through two transposing reads.
-__device__ inline bf16x8 tr_operand(const char *p) {
-    const u32x2 lo = ds_read_tr(p);
-    const u32x2 hi = ds_read_tr(p + 8 * ROWB);
-    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-// The same for a swz_b tile: rows 0-7 and 8-15 of the step at their own offsets.
+// 32 channels x 16 rows A operand through two transposing reads, rows 0-7
+// and 8-15 of the step at their own offsets.
 __device__ inline bf16x8 tr_operand_b(const char *base, int lo_off, int hi_off) {
     const u32x2 lo = ds_read_tr(base + lo_off);
     const u32x2 hi = ds_read_tr(base + hi_off);
@@ -233,7 +208,7 @@ __device__ inline void work_item(const BwdProblem &p, int nwork, int &bh, int &i
 }
 
 // ---------------------------------------------------------------------------- dQ
-constexpr int QREG = 6;   // K re, K im, V re, V im (row-major swizzle), K re, K im (transposing swizzle)
+constexpr int QREG = 4;   // K re, K im, V re, V im, each staged once (swizzle swz_b)
 // The dQ kernel runs 8 waves (two per SIMD) over 256 queries: every staged
 // K/V stage feeds twice the queries, and one wave's waits are filled by the other.
 constexpr int QNW = 8;
@@ -255,16 +230,15 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
 
     const int64_t head = (int64_t)bh * T * D;
     auto plane = [&](const void *x) { return reinterpret_cast<const uint16_t *>(x) + head; };
-    const uint16_t *stage_planes[QREG] = {plane(p.k_re), plane(p.k_im), plane(p.v_re),
-                                          plane(p.v_im), plane(p.k_re), plane(p.k_im)};
+    const uint16_t *stage_planes[QREG] = {plane(p.k_re), plane(p.k_im), plane(p.v_re), plane(p.v_im)};
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char *)lds;
-    const Offsets off = lane_offsets(lane);
+    const Offsets off = lane_offsets_b(lane);
 
     auto issue_stage = [&](int s) {
         const uint32_t base = lds0 + (uint32_t)((s & 1) * QREG * REGION);
 #pragma unroll
         for (int r = 0; r < QREG; ++r)
-            stage_region<QNT>(base + r * REGION, stage_planes[r], s * BS, T, r >= 4 ? SWZ_V : SWZ_K, tid, wave);
+            stage_region<QNT>(base + r * REGION, stage_planes[r], s * BS, T, tid, wave);
     };
 
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
@@ -360,9 +334,9 @@ __global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p,
             for (int m = 0; m < 2; ++m) {
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const int o = (32 * sb + 16 * m) * ROWB + off.voff[ct];
-                    const bf16x8 krt = tr_operand(st + 4 * REGION + o);
-                    const bf16x8 kit = tr_operand(st + 5 * REGION + o);
+                    const char *b = st + (32 * sb + 16 * m) * ROWB;
+                    const bf16x8 krt = tr_operand_b(b, off.voff[ct], off.voffh[ct]);
+                    const bf16x8 kit = tr_operand_b(b + REGION, off.voff[ct], off.voffh[ct]);
                     acc[ct] = mfma(krt, prb[m], acc[ct]);
                     acc[ct] = mfma(kit, pnb[m], acc[ct]);
                     acc[2 + ct] = mfma(kit, prb[m], acc[2 + ct]);
@@ -664,7 +638,7 @@ __global__ __launch_bounds__(NT) void born_bf16_d64_bwd_dkdv_kernel(BwdProblem p
             const uint32_t base = lds0 + (uint32_t)((s & 1) * KREG * REGION);
 #pragma unroll
             for (int r = 0; r < KREG; ++r)
-                stage_region<NT>(base + r * REGION, stage_planes[r], qs + s * BS, T, SWZ_B, tid, wave);
+                stage_region<NT>(base + r * REGION, stage_planes[r], qs + s * BS, T, tid, wave);
             scal_issue(qs + s * BS, s & 1);
         };
 

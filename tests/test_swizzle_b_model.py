@@ -1,5 +1,5 @@
-"""CPU model of the one-copy tile swizzle of the bf16 backward's key-side
-kernel (swz_b in kernel_born_bf16_d64_bwd.hip).
+"""CPU model of the one-copy tile swizzle of the bf16 backward kernels
+(swz_b in kernel_born_bf16_d64_bwd.hip).
 
 A 64-row stage of one bf16 plane is 64 rows of 128 bytes, eight 16-byte
 chunks each; the LDS-direct copy puts logical chunk c of row r at slot
@@ -17,8 +17,8 @@ bit of the row the swizzle depends on fails), and that under 64 banks
 (8 and 16 lanes) no read touches a bank at two addresses in one step.  A
 swizzle that is a function of the low two row bits only (the value tiles'
 swizzle) fails the row-major reads, and the key tiles' swizzle fails the
-transposing reads; that is why the kernels that keep both kinds of tile
-stage them twice, and this one once.
+transposing reads (the forward's two swizzles, which a tile read both ways
+would need twice over).
 """
 import pytest
 
