@@ -145,11 +145,13 @@ def main_bwd(args, w):
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] bwd {w.name}: {ms:.4f} ms/step (median {np.median(per):.4f} ms), {tflops:.2f} TFLOP/s")
     # which kernels the library dispatches: bf16 matrix cores for Born at d_h = 64, fp32 matrix
-    # cores for complex64 at d_h 16/32/64, else fp32 vector code
+    # cores (32 x 32 tiles) for complex64 and bf16 planes at d_h 16/32/64, the 16 x 16 fp32
+    # kernels at 128, else fp32 vector code
     mfma = w.op == "born" and w.layout == "bf16" and w.d_h == 64
-    mfma32 = w.layout == "c64" and w.d_h in (16, 32, 64)
+    mfma32 = not mfma and w.d_h in (16, 32, 64, 128)
     peak = PEAK_TFLOPS["bf16"] if mfma else PEAK_TFLOPS["c64"]
     kern = ("born_bf16_d64_bwd_dkdv_kernel + born_bf16_d64_bwd_dq_kernel" if mfma
+            else "bwd16_dkdv_kernel + bwd16_dq_kernel" if w.d_h == 128
             else "bwd_dkdv_f32_kernel + bwd_dq_f32_kernel" if mfma32
             else "bwd_dkdv_kernel + bwd_dq_kernel")
     rec = {
@@ -673,6 +675,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="default run: skip timing the other four workloads beside the headline")
+    ap.add_argument("--d-h", type=int, default=0,
+                    help="--pass fwd/bwd: the named workload at this head width instead (not a headline number)")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "rotary", "step", "linear"], default="fwd")
     ap.add_argument("--chunk", type=int, default=4096, help="--pass linear: tokens per chunk")
     ap.add_argument("--gate", choices=["sigmoid", "softmax", "screen"], default="sigmoid",
@@ -690,6 +694,9 @@ def main():
     from complex_valued_attention_amd import inputs as gen
     name = args.workload or gen.BENCH_WORKLOAD
     w = gen.WORKLOADS[name]
+    if args.d_h:   # the named workload's shape and recipe at another head width
+        name = f"{name}@d{args.d_h}"
+        w = dataclasses.replace(w, d_h=args.d_h, name=name)
 
     if args.which == "bwd":
         main_bwd(args, w)
@@ -752,9 +759,9 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, got, gate=args.gate)
         log(f"[bench] cpu baseline {rec['cpu_baseline']}")
-    if args.workload is None and not args.no_configs and w.op == "born":
+    if args.workload is None and not args.d_h and not args.no_configs and w.op == "born":
         rec["options"] = option_records(w, inp, kernel_ms, args.steps, args.warmup)
-    if args.workload is None and not args.no_configs:
+    if args.workload is None and not args.d_h and not args.no_configs:
         # every workload of the metric's config list, timed in this run (the
         # headline's own entry repeats the numbers above)
         configs = {}

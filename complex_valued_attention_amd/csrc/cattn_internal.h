@@ -124,6 +124,8 @@ hipError_t launch_bwd_generic_dkdv(const BwdProblem &p);   // key-side gradients
 hipError_t launch_bwd_generic_dq(const BwdProblem &p);     // query-side gradients only
 
 bool supports_born_bf16_d64_bwd(const BwdProblem &p);
+bool supports_bwd_f32_mfma16(const BwdProblem &p);        // width 128, 16 x 16 fp32 tiles
+hipError_t launch_bwd_f32_mfma16(const BwdProblem &p);    // all its kernels
 bool supports_bwd_f32_mfma(const BwdProblem &p);          // complex64, widths 16/32/64
 hipError_t launch_bwd_f32_mfma(const BwdProblem &p);      // both kernels
 hipError_t launch_born_bf16_d64_bwd_dq(const BwdProblem &p);

@@ -1,0 +1,655 @@
+// Backward of Born and phase-coherent attention at head width 128 on
+// interleaved complex64 (or bf16 planes, widened to the same fp32 rows on load
+// and rounded back on store) with gfx950 fp32 matrix cores in their 16 x 16
+// form (v_mfma_f32_16x16x4_f32), fp32 throughout.
+//
+// Gradients are dL/d(conj z) for a real loss L given G = dL/d(conj O)
+// ("CNet ...", section 3, the Wirtinger accumulation rule (2)).  Born ("CNet
+// ...", section 11.2), with S = Q K^H, w = |S|^2, l the forward's row
+// denominators, delta = Re(G^H O) per query and D = (Re(G V^H) - delta) / l:
+//     dV = (w / l)^T G,   dQ = (2 D o S) K,   dK = (2 D o S)^H Q.
+// PCT ("Complex-valued Phase-Coherent Transformers", section 1 and Appendix
+// D.2), with s = sqrt(d_h) Re<qh, kh>, w = sigmoid(s + b), ds = Re(G V^H) w (1 - w):
+//     dV = w^T G,  dq = P_q(sqrt(d_h) sum_j ds kh_j) / ||q||,  dk = P_k(sqrt(d_h) sum_i ds qh_i) / ||k||,
+// P_x removing the component along the unit vector x; the bias gradient per
+// query row is sum_j ds.
+//
+// Why the 16 x 16 form at this width.  A complex row of 128 channels is a real
+// row x' = (Re x0, Im x0, ...) of 256 floats.  A wave that owns rows as a
+// register operand holds (rows x 256) / 64 floats per lane: 128 per operand
+// for 32 rows, and each kernel holds two (Q', G' or K', V') beside the
+// gradient accumulators of the same size -- more than a lane has.  With
+// 16-row tiles it is 64 floats per operand and 64 per accumulator.
+//
+// Products (lane l: j16 = l % 16, lane group g = l / 16; an A operand row and
+// a B operand column are j16, the contraction index of a step is g; a result
+// lane holds rows 4 g + r of column j16).
+//  * Scores: the contraction runs over the real row in any order both
+//    operands share; lane group g takes the contiguous quarter
+//    [64 g, 64 g + 64) of the row, so a lane reads its slice of a streamed row
+//    with 16-byte LDS reads.  Re <q, k> = k' . q' and Im <q, k> = k'' . q'
+//    with k'' = (-Im k0, Re k0, ...) (equally q''' . k' with
+//    q''' = (Im q0, -Re q0, ...)): the swapped, sign-flipped partner is formed
+//    from the streamed operand as it is read, and the owned operand is used as
+//    it stands.
+//  * Gradients: over a 16-row block in 4 steps of 4 rows; step t takes row
+//    4 g + t from lane group g, which is its own result register r = t, so the
+//    weights need no shuffle.  Channel tile c, row i stands for real channel
+//    16 i + 4 ((c / 4 + i / 4) mod 4) + c mod 4: the streamed operand a lane
+//    needs for one row is 16 contiguous floats (four 16-byte reads, taken in
+//    an order rotated by i / 4 so that the 16 lanes of a read cover every LDS
+//    bank once), and the gradient a lane ends with is the 64 contiguous
+//    channels of its quarter.  The imaginary part of a complex product uses
+//    the partner channel (c ^ 1, the same rotation) with the sign on the weight.
+//
+// Three kernels:
+//  * Born only: per query, 1 / l and delta, written as float pairs into the
+//    dq buffer (it holds B H T 8 bytes many times over, and nothing reads it
+//    until the dq kernel overwrites it);
+//  * dkdv: a wave owns 16 keys (K', V' in registers) and streams 16-query
+//    stages of Q', G' (with the pairs, or 1 / ||q||) through LDS: lane = key,
+//    registers = queries; dV'^T += G'^T W, dK'^T += Q'^T P;
+//  * dq: a wave owns 16 queries (Q', G' in registers) and streams 16-key stages
+//    of K', V' through LDS: lane = query, registers = keys; dQ'^T += K'^T P^T.
+// Every wave runs every stage of its workgroup with no branch around the
+// products: the causal mask, applied per weight, zeroes the blocks above a
+// wave's diagonal.  (A branch there made the compiler copy the loop-carried
+// gradient accumulators between register files at every stage; the few
+// wasted blocks cost less.)
+// Nothing is written twice: no atomics, deterministic results.
+#include "cattn_internal.h"
+
+namespace cattn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int KD = 2 * D;          // real width of a row (floats)
+constexpr int KQ = KD / 4;         // contraction floats per lane group
+constexpr int NC = KD / 16;        // 16-channel tiles of a gradient row
+constexpr int ROW = KD + 4;        // padded LDS row (floats): a 16-lane read of 16 rows covers every bank once
+constexpr int NW = 4;              // waves per workgroup, one per SIMD
+constexpr int NT = 64 * NW;
+constexpr int TR = 16;             // rows owned per wave
+constexpr int BM = TR * NW;        // rows owned per workgroup
+constexpr int BN = 16;             // streamed rows per LDS stage
+constexpr int LPK = NT / BN;       // staging lanes per row
+constexpr int CPT = KD / 4 / LPK;  // 16-byte chunks per staging lane and operand
+constexpr int STAGE = 2 * BN * ROW + 2 * BN;   // two operands and two per-row scalars (floats)
+constexpr int LDS_BYTES = 2 * STAGE * 4;
+constexpr int KP = 16;             // contraction floats per LDS read batch of the score products
+static_assert(CPT * LPK * 4 == KD, "staging split");
+
+__device__ inline f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// hardware reciprocal (1 ulp), not the IEEE division sequence
+__device__ inline float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Floats f .. f + 3 (complex elements f / 2, f / 2 + 1) of dense row `row`;
+// LAYOUT_BF16 reads the two planes and widens.
+template <int LAY>
+__device__ inline f32x4 load4(const void *re, const void *im, int64_t row, int f) {
+    if constexpr (LAY == LAYOUT_C64) {
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(re) + row * KD + f);
+    } else {
+        const int64_t el = row * D + f / 2;
+        const uint32_t r2 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(re) + el);
+        const uint32_t i2 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(im) + el);
+        return f32x4{bf_lo(r2), bf_lo(i2), bf_hi(r2), bf_hi(i2)};
+    }
+}
+
+// LAYOUT_BF16 rounds to bf16 (nearest even) and writes the two planes.
+template <int LAY>
+__device__ inline void store4(void *re, void *im, int64_t row, int f, f32x4 v) {
+    if constexpr (LAY == LAYOUT_C64) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(re) + row * KD + f) = v;
+    } else {
+        const int64_t el = row * D + f / 2;
+        const f32x2 r = {v[0], v[2]}, i = {v[1], v[3]};
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(re) + el) =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(im) + el) =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(i, bf16x2));
+    }
+}
+
+// n floats from LDS with 16-byte reads
+template <int N>
+__device__ inline void lds_row(const float *p, float (&out)[N]) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(p + 4 * i);
+        out[4 * i] = x[0];
+        out[4 * i + 1] = x[1];
+        out[4 * i + 2] = x[2];
+        out[4 * i + 3] = x[3];
+    }
+}
+
+// The 16 floats 16 j16 .. 16 j16 + 15 of a streamed LDS row as the gradient
+// products' operand: out[4 p + e] is float 4 ((p + j16 / 4) mod 4) + e of the run.
+__device__ inline void lds_run16(const float *rowp, int j16, float (&out)[16]) {
+    const float *run = rowp + 16 * j16;
+    const int rho = j16 >> 2;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(run + 4 * ((p + rho) & 3));
+        out[4 * p] = x[0];
+        out[4 * p + 1] = x[1];
+        out[4 * p + 2] = x[2];
+        out[4 * p + 3] = x[3];
+    }
+}
+
+// The owned operand's float at gradient tile c, register r of lane group g:
+// x[16 r + 4 ((c / 4 + g) mod 4) + c mod 4], selected with compile-time
+// indices (c and r unrolled) so that the array stays in registers.
+__device__ inline float own_of(const float (&x)[KQ], int g, int c, int r) {
+    const int m = ((c >> 2) + g) & 3;
+    const float v0 = x[16 * r + (c & 3)], v1 = x[16 * r + 4 + (c & 3)];
+    const float v2 = x[16 * r + 8 + (c & 3)], v3 = x[16 * r + 12 + (c & 3)];
+    return m == 0 ? v0 : m == 1 ? v1 : m == 2 ? v2 : v3;
+}
+
+// Workgroup -> (head, owned block).  The blocks of a head go to one XCD when
+// BH % 8 == 0 (workgroups are dealt to the 8 XCDs in turn).  `heavy_last`:
+// the query side, whose last blocks see the most keys under the causal mask,
+// takes them first; the key side takes its first blocks first.
+__device__ inline void map_block(int BH, int nblk, bool heavy_last, int &bh, int &blk) {
+    const int L = blockIdx.x;
+    int j;
+    if ((BH & 7) == 0) {
+        const int x = L & 7;
+        j = L >> 3;
+        bh = x + 8 * (j / nblk);
+    } else {
+        bh = L / nblk;
+        j = L;
+    }
+    blk = heavy_last ? nblk - 1 - (j % nblk) : j % nblk;
+}
+
+// Streamed rows: thread t stages row t / LPK, chunks t % LPK + LPK i of each
+// operand (the 16 lanes of one LDS write cover a row: every bank once).
+struct Stager {
+    int row, sc;
+    __device__ Stager(int tid) : row(tid / LPK), sc(tid % LPK) {}
+    __device__ int chunk(int i) const { return sc + LPK * i; }
+};
+
+// ------------------------------------------------------------------------------ per-query scalars (Born)
+// 16 lanes per query row: 1 / l (0 for a zero denominator: O = 0, no gradient)
+// and delta = Re(G^H O), as a float pair at index row of the dq buffer.
+template <int LAY>
+__global__ __launch_bounds__(256) void bwd16_scal_kernel(BwdProblem p, int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int sp = threadIdx.x & 15;
+    float dl = 0.f;
+    if (row < rows) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 gg = load4<LAY>(p.g_re, p.g_im, row, 16 * sp + 4 * i);
+            const f32x4 o = load4<LAY>(p.o_re, p.o_im, row, 16 * sp + 4 * i);
+            dl += gg[0] * o[0] + gg[1] * o[1] + gg[2] * o[2] + gg[3] * o[3];
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dl += __shfl_xor(dl, o);
+    if (sp == 0 && row < rows) {
+        const float l = p.row_den[row];
+        reinterpret_cast<f32x2 *>(p.dq_re)[row] = f32x2{l != 0.f ? 1.f / l : 0.f, dl};
+    }
+}
+
+// ------------------------------------------------------------------------------ dK, dV
+// DECAY (Born): every weight and D2 carries gamma^(query - key), one
+// exponential per weight (the distance clamped at 0 where the mask zeroes it).
+template <int OP, int LAY, bool DECAY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
+    extern __shared__ __align__(16) float fsm[];
+    constexpr bool born = OP == OP_BORN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j16 = lane & 15;
+    const int g = lane >> 4;
+    const int T = p.T;
+
+    int bh, kblk;
+    map_block(p.BH, nkb, false, bh, kblk);
+    const int kb0 = kblk * BM;
+    const int64_t hrow = (int64_t)bh * T;   // this head's first row
+    const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
+
+    // K', V' of this wave's 16 keys over the lane group's quarter of the row
+    const int kt0 = kb0 + TR * wave;
+    const int krow = kt0 + j16;
+    float kre[KQ], vre[KQ];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, v = x;
+        if (krow < T) {
+            x = load4<LAY>(p.k_re, p.k_im, hrow + krow, g * KQ + 4 * i);
+            v = load4<LAY>(p.v_re, p.v_im, hrow + krow, g * KQ + 4 * i);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kre[4 * i + e] = x[e];
+            vre[4 * i + e] = v[e];
+            ss += x[e] * x[e];
+        }
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rk = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;   // PCT: 1 / ||k||
+    const float sqd = sqrtf((float)D);
+
+    f32x4 dk[NC], dv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dk[c] = dv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // query stages: with the causal mask only queries >= this workgroup's first key
+    const int qstart = p.causal ? kb0 : 0;
+    const int nst = qstart < T ? (T - qstart + BN - 1) / BN : 0;
+    const Stager stg(tid);
+    f32x4 qreg[CPT], greg[CPT];
+    f32x2 tab = {0.f, 0.f};
+    auto load_stage = [&](int q0) {
+        const int qr = q0 + stg.row;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+            if (qr < T) {
+                a = load4<LAY>(p.q_re, p.q_im, hrow + qr, 4 * stg.chunk(i));
+                b = load4<LAY>(p.g_re, p.g_im, hrow + qr, 4 * stg.chunk(i));
+            }
+            qreg[i] = a;
+            greg[i] = b;
+        }
+        if (born) {
+            tab = f32x2{0.f, 0.f};
+            if (stg.sc == 0 && qr < T) tab = reinterpret_cast<const f32x2 *>(p.dq_re)[hrow + qr];
+        }
+    };
+    // per query: Born (1 / l, delta); PCT (1 / ||q||, unused)
+    auto store_stage = [&](int buf) {
+        float *qs = fsm + buf * STAGE;
+        float *gs = qs + BN * ROW;
+        float *sa = gs + BN * ROW;
+        float *sb = sa + BN;
+        float x2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            *reinterpret_cast<f32x4 *>(qs + stg.row * ROW + 4 * stg.chunk(i)) = qreg[i];
+            *reinterpret_cast<f32x4 *>(gs + stg.row * ROW + 4 * stg.chunk(i)) = greg[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x2 += qreg[i][e] * qreg[i][e];
+        }
+        if (!born) {
+#pragma unroll
+            for (int o = 1; o < LPK; o <<= 1) x2 += __shfl_xor(x2, o);
+        }
+        if (stg.sc == 0) {
+            if (born) {
+                sa[stg.row] = tab[0];
+                sb[stg.row] = tab[1];
+            } else {
+                sa[stg.row] = x2 > 0.f ? 1.f / sqrtf(x2) : 0.f;
+                sb[stg.row] = 0.f;
+            }
+        }
+    };
+    if (nst > 0) {
+        load_stage(qstart);
+        store_stage(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < nst; ++st) {
+        const int qb0 = qstart + st * BN;
+        const int buf = st & 1;
+        if (st + 1 < nst) load_stage(qb0 + BN);
+        {   // every wave, every stage: the mask zeroes queries before a lane's key
+            const float *qs = fsm + buf * STAGE;
+            const float *gs = qs + BN * ROW;
+            const float *sa = gs + BN * ROW;
+            const float *sb = sa + BN;
+            // S, E for 16 queries x 16 keys: lane = key j16, registers = queries 4 g + r
+            f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
+#pragma unroll
+            for (int p0 = 0; p0 < KQ; p0 += KP) {
+                float qa[KP], ga[KP];
+                lds_row<KP>(qs + j16 * ROW + g * KQ + p0, qa);
+                lds_row<KP>(gs + j16 * ROW + g * KQ + p0, ga);
+#pragma unroll
+                for (int s = 0; s < KP; ++s) {
+                    sr = mfma16(qa[s], kre[p0 + s], sr);
+                    ev = mfma16(ga[s], vre[p0 + s], ev);
+                    // Im <q, k> = sum_n q'''[n] k'[n] with q''' = (Im q0, -Re q0, ...): the sign
+                    // and the swap on the streamed operand (a quarter starts on an even index)
+                    if (born) si = mfma16((s & 1) ? -qa[s - 1] : qa[s + 1], kre[p0 + s], si);
+                }
+            }
+            const f32x4 av = *reinterpret_cast<const f32x4 *>(sa + 4 * g);
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + 4 * g);
+            float wl[4], pr[4], pi[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qi = 4 * g + r;
+                const bool keep = (!p.causal || qb0 + qi >= krow) && qb0 + qi < T;
+                if (born) {
+                    const float w = sr[r] * sr[r] + si[r] * si[r];
+                    const float f = DECAY ? decay_pow(lg2, max(qb0 + qi - krow, 0)) : 1.f;
+                    wl[r] = keep ? w * av[r] * f : 0.f;
+                    const float d2 = keep ? 2.f * (ev[r] - bv[r]) * av[r] * f : 0.f;
+                    pr[r] = d2 * sr[r];
+                    pi[r] = d2 * si[r];
+                } else {
+                    const float w = sigmoid(sr[r] * sqd * av[r] * rk + p.bias);
+                    wl[r] = keep ? w : 0.f;
+                    const float ds = keep ? ev[r] * w * (1.f - w) : 0.f;
+                    pr[r] = sqd * ds * av[r];   // sqrt(d) ds qh on the raw query row
+                    pi[r] = 0.f;
+                }
+            }
+            // dV'^T += G'^T W, dK'^T += Q'^T Re P - Q''^T Im P; step t takes query 4 g + t
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float ga2[16], qa2[16];
+                lds_run16(gs + (4 * g + t) * ROW, j16, ga2);
+                lds_run16(qs + (4 * g + t) * ROW, j16, qa2);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    dv[c] = mfma16(ga2[c], wl[t], dv[c]);
+                    dk[c] = mfma16(qa2[c], pr[t], dk[c]);
+                }
+                if (born) {
+                    // -q''[n]: q'[n + 1] on even n, -q'[n - 1] on odd n
+                    const float npi = -pi[t];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) dk[c] = mfma16(qa2[c ^ 1], (c & 1) ? npi : pi[t], dk[c]);
+                }
+            }
+        }
+        if (st + 1 < nst) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // lane (key j16, group g), tile c, register r: channel 64 g + 16 r +
+    // 4 ((c / 4 + g) mod 4) + c mod 4, the float own_of(kre, c, r)
+    if (!born) {
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dot += dk[c][r] * own_of(kre, g, c, r);
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        dot *= rk * rk;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dk[c][r] = (dk[c][r] - dot * own_of(kre, g, c, r)) * rk;
+    }
+    if (krow >= T) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int f = g * KQ + 16 * r + 4 * ((q + g) & 3);
+            store4<LAY>(p.dk_re, p.dk_im, hrow + krow, f,
+                        f32x4{dk[4 * q][r], dk[4 * q + 1][r], dk[4 * q + 2][r], dk[4 * q + 3][r]});
+            store4<LAY>(p.dv_re, p.dv_im, hrow + krow, f,
+                        f32x4{dv[4 * q][r], dv[4 * q + 1][r], dv[4 * q + 2][r], dv[4 * q + 3][r]});
+        }
+}
+
+// ------------------------------------------------------------------------------ dQ (and db)
+template <int OP, int LAY, bool DECAY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd16_dq_kernel(BwdProblem p, int nrb) {
+    extern __shared__ __align__(16) float fsm[];
+    constexpr bool born = OP == OP_BORN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j16 = lane & 15;
+    const int g = lane >> 4;
+    const int T = p.T;
+
+    int bh, rb;
+    map_block(p.BH, nrb, true, bh, rb);
+    const int m0 = rb * BM;
+    const int64_t hrow = (int64_t)bh * T;
+    const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
+
+    // Q', G' of this wave's 16 queries over the lane group's quarter of the row
+    const int qt0 = m0 + TR * wave;
+    const int qrow = qt0 + j16;
+    float qre[KQ], gre[KQ];
+    float dl = 0.f, ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, gg = x, o = x;
+        if (qrow < T) {
+            x = load4<LAY>(p.q_re, p.q_im, hrow + qrow, g * KQ + 4 * i);
+            gg = load4<LAY>(p.g_re, p.g_im, hrow + qrow, g * KQ + 4 * i);
+            if (born) o = load4<LAY>(p.o_re, p.o_im, hrow + qrow, g * KQ + 4 * i);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qre[4 * i + e] = x[e];
+            gre[4 * i + e] = gg[e];
+            dl += gg[e] * o[e];   // Re(G^H O), this quarter's components
+            ss += x[e] * x[e];
+        }
+    }
+    dl += __shfl_xor(dl, 16);
+    dl += __shfl_xor(dl, 32);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    float inv_l = 0.f;   // Born: 1 / l (0 for a zero denominator: O = 0, no gradient)
+    if (born && qrow < T) {
+        const float l = p.row_den[hrow + qrow];
+        inv_l = l != 0.f ? 1.f / l : 0.f;
+    }
+    const float iq = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;   // PCT: 1 / ||q|| (0 for a zero row)
+    const float rq = sqrtf((float)D) * iq;
+
+    f32x4 dq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dsum = 0.f;
+
+    const int kend = p.causal ? min(T, m0 + BM) : T;
+    const int nst = (kend + BN - 1) / BN;
+    const Stager stg(tid);
+    f32x4 kreg[CPT], vreg[CPT];
+    auto load_stage = [&](int k0) {
+        const int kr = k0 + stg.row;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+            if (kr < T) {
+                a = load4<LAY>(p.k_re, p.k_im, hrow + kr, 4 * stg.chunk(i));
+                b = load4<LAY>(p.v_re, p.v_im, hrow + kr, 4 * stg.chunk(i));
+            }
+            kreg[i] = a;
+            vreg[i] = b;
+        }
+    };
+    auto store_stage = [&](int buf) {
+        float *ks = fsm + buf * STAGE;
+        float *vs = ks + BN * ROW;
+        float *rks = vs + BN * ROW;
+        float s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            *reinterpret_cast<f32x4 *>(ks + stg.row * ROW + 4 * stg.chunk(i)) = kreg[i];
+            *reinterpret_cast<f32x4 *>(vs + stg.row * ROW + 4 * stg.chunk(i)) = vreg[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s2 += kreg[i][e] * kreg[i][e];
+        }
+        if (!born) {
+#pragma unroll
+            for (int o = 1; o < LPK; o <<= 1) s2 += __shfl_xor(s2, o);
+            if (stg.sc == 0) rks[stg.row] = s2 > 0.f ? 1.f / sqrtf(s2) : 0.f;
+        }
+    };
+    if (nst > 0) {
+        load_stage(0);
+        store_stage(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < nst; ++st) {
+        const int kb0 = st * BN;
+        const int buf = st & 1;
+        if (st + 1 < nst) load_stage(kb0 + BN);
+        {   // every wave, every stage: the mask zeroes keys past a lane's query
+            const float *ks = fsm + buf * STAGE;
+            const float *vs = ks + BN * ROW;
+            const float *rks = vs + BN * ROW;
+            // S^T, E^T for 16 keys x 16 queries: lane = query j16, registers = keys 4 g + r
+            f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
+#pragma unroll
+            for (int p0 = 0; p0 < KQ; p0 += KP) {
+                float ka[KP], va[KP];
+                lds_row<KP>(ks + j16 * ROW + g * KQ + p0, ka);
+                lds_row<KP>(vs + j16 * ROW + g * KQ + p0, va);
+#pragma unroll
+                for (int s = 0; s < KP; ++s) {
+                    sr = mfma16(ka[s], qre[p0 + s], sr);
+                    ev = mfma16(va[s], gre[p0 + s], ev);
+                    // Im <q, k> = sum_n k''[n] q'[n] with k'' = (-Im k0, Re k0, ...): the sign and
+                    // the swap on the streamed operand
+                    if (born) si = mfma16((s & 1) ? ka[s - 1] : -ka[s + 1], qre[p0 + s], si);
+                }
+            }
+            f32x4 rkv = {0.f, 0.f, 0.f, 0.f};
+            if (!born) rkv = *reinterpret_cast<const f32x4 *>(rks + 4 * g);
+            float pr[4], pi[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 4 * g + r;
+                const bool keep = (!p.causal || kb0 + key <= qrow) && kb0 + key < T;
+                if (born) {
+                    float d2 = keep ? 2.f * (ev[r] - dl) * inv_l : 0.f;
+                    if (DECAY) d2 *= decay_pow(lg2, max(qrow - (kb0 + key), 0));
+                    pr[r] = d2 * sr[r];
+                    pi[r] = d2 * si[r];
+                } else {
+                    const float w = sigmoid(sr[r] * rq * rkv[r] + p.bias);
+                    const float ds = keep ? ev[r] * w * (1.f - w) : 0.f;
+                    dsum += ds;
+                    pr[r] = ds * rkv[r];   // ds kh on the raw key row
+                    pi[r] = 0.f;
+                }
+            }
+            // dQ'^T += K'^T Re P^T + K''^T Im P^T; step t takes key 4 g + t
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float a[16];
+                lds_run16(ks + (4 * g + t) * ROW, j16, a);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) dq[c] = mfma16(a[c], pr[t], dq[c]);
+                if (born) {
+                    // k''[n]: -k'[n + 1] on even n, k'[n - 1] on odd n
+                    const float npi = -pi[t];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) dq[c] = mfma16(a[c ^ 1], (c & 1) ? pi[t] : npi, dq[c]);
+                }
+            }
+        }
+        if (st + 1 < nst) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // lane (query j16, group g), tile c, register r: channel 64 g + 16 r +
+    // 4 ((c / 4 + g) mod 4) + c mod 4, the float own_of(qre, c, r)
+    if (!born) {
+        const float sq = sqrtf((float)D);
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dq[c][r] *= sq;
+                dot += dq[c][r] * own_of(qre, g, c, r);
+            }
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        dot *= iq * iq;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dq[c][r] = (dq[c][r] - dot * own_of(qre, g, c, r)) * iq;
+        float db = dsum + __shfl_xor(dsum, 16);
+        db += __shfl_xor(db, 32);
+        if (p.db_rows && g == 0 && qrow < T) p.db_rows[hrow + qrow] = db;
+    }
+    if (qrow >= T) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            store4<LAY>(p.dq_re, p.dq_im, hrow + qrow, g * KQ + 16 * r + 4 * ((q + g) & 3),
+                        f32x4{dq[4 * q][r], dq[4 * q + 1][r], dq[4 * q + 2][r], dq[4 * q + 3][r]});
+}
+
+template <int OP, int LAY, bool DECAY = false>
+hipError_t launch_cfg(const BwdProblem &p) {
+    static std::atomic<uint64_t> dq_set{0}, kv_set{0};
+    const int nblk = (p.T + BM - 1) / BM;
+    const int64_t blocks = (int64_t)p.BH * nblk;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    auto kkv = bwd16_dkdv_kernel<OP, LAY, DECAY>;
+    auto kdq = bwd16_dq_kernel<OP, LAY, DECAY>;
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), LDS_BYTES, kv_set);
+    if (e != hipSuccess) return e;
+    e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), LDS_BYTES, dq_set);
+    if (e != hipSuccess) return e;
+    if (OP == OP_BORN) {
+        const int64_t rows = (int64_t)p.BH * p.T;
+        const int64_t sblocks = (rows + 15) / 16;
+        if (sblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd16_scal_kernel<LAY>, dim3((unsigned)sblocks), dim3(256), 0, p.stream, p, rows);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, p.stream, p, nblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kdq, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, p.stream, p, nblk);
+    return hipGetLastError();
+}
+
+template <int LAY>
+hipError_t launch_op(const BwdProblem &p) {
+    if (p.op == OP_BORN)
+        return p.decay.on ? launch_cfg<OP_BORN, LAY, true>(p) : launch_cfg<OP_BORN, LAY>(p);
+    return launch_cfg<OP_PCT, LAY>(p);
+}
+
+}  // namespace
+
+bool supports_bwd_f32_mfma16(const BwdProblem &p) {
+    return (p.op == OP_BORN || p.op == OP_PCT) && p.d == D;
+}
+
+hipError_t launch_bwd_f32_mfma16(const BwdProblem &p) {
+    return p.layout == LAYOUT_C64 ? launch_op<LAYOUT_C64>(p) : launch_op<LAYOUT_BF16>(p);
+}
+
+}  // namespace cattn

@@ -187,6 +187,18 @@ CASES = [
     ("pct", "bf16", True, 2, 1, 130, 16, False),
     ("born", "bf16", True, 1, 8, 200, 32, True),
     ("born", "bf16", False, 1, 3, 150, 32, False),
+    # width 128 on the 16 x 16 fp32 matrix-core kernels: several 64-row blocks,
+    # ragged tails, T below one 16-row tile, 8 heads, bf16 planes widened
+    ("born", "c64", False, 1, 2, 200, 128, False),
+    ("born", "c64", True, 1, 8, 260, 128, True),
+    ("born", "c64", True, 2, 1, 16, 128, False),
+    ("born", "c64", True, 1, 1, 9, 128, True),
+    ("born", "bf16", False, 1, 1, 77, 128, False),
+    ("born", "bf16", True, 2, 4, 192, 128, True),
+    ("pct", "c64", True, 2, 4, 130, 128, False),
+    ("pct", "c64", False, 1, 1, 1, 128, False),
+    ("pct", "bf16", True, 1, 2, 150, 128, False),
+    ("pct", "bf16", False, 1, 3, 64, 128, False),
 ]
 
 
@@ -223,6 +235,33 @@ FULL = [
 ]
 
 
+# Width 128 at the B4 H8 T1024 shape (the complex64 rotary workload's shape)
+# on the 16 x 16 fp32 matrix-core kernels, and bf16 planes at B2 H8 T2048.
+FULL128 = [
+    (gen.Workload("bwd128_c64", "born", True, 4, 8, 1024, 128, "c64", seed=24, qk_unit=True, rotary=True),
+     [(0, 0), (3, 7)]),
+    (gen.Workload("bwd128_pct", "pct", False, 4, 8, 1024, 128, "c64", seed=25), [(1, 3)]),
+    (gen.Workload("bwd128_bf16", "born", True, 2, 8, 2048, 128, "bf16", seed=26, qk_unit=True, rotary=True),
+     [(1, 7)]),
+]
+
+
+@pytest.mark.parametrize("w,heads", FULL128, ids=[f[0].name for f in FULL128])
+def test_bwd_width128_sampled_heads(w, heads):
+    say("case bwd 128", w)
+    inp = gen.make_inputs(w)
+    grad = gen.make_grad(w)
+    bias = -math.log(w.T) if w.op == "pct" else 0.0
+    got = run_hip_bwd(w, inp, grad, bias=bias)
+    for x in got[:3]:
+        assert np.isfinite(x).all()
+    ref = run_oracle_bwd(w, inp, grad, bias=bias, heads=heads)
+    sel = lambda x: np.stack([x[b, h] for b, h in heads])
+    db = None if got[3] is None else sel(got[3].reshape(w.B, w.H, w.T))
+    terms = term_scales(w.op, sel(inp.q64), sel(inp.k64), sel(inp.v64), sel(grad.g64), w.causal, bias=bias)
+    compare(w, tuple(sel(x) for x in got[:3]) + (db,), ref, f"bwd 128 {w.name} heads {heads}", terms)
+
+
 @pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
 def test_bwd_full_size_sampled_heads(name, heads):
     w = gen.WORKLOADS[name]
@@ -239,9 +278,9 @@ def test_bwd_full_size_sampled_heads(name, heads):
     compare(w, tuple(sel(x) for x in got[:3]) + (db,), ref, f"bwd full {name} heads {heads}", terms)
 
 
-@pytest.mark.parametrize("op", ["born", "pct"])
-def test_bwd_bitwise_deterministic(op):
-    w = gen.Workload("det", op, True, 1, 2, 333, 64, "c64", seed=23, qk_unit=True)
+@pytest.mark.parametrize("op,d", [("born", 64), ("pct", 64), ("born", 128), ("pct", 128)])
+def test_bwd_bitwise_deterministic(op, d):
+    w = gen.Workload("det", op, True, 1, 2, 333, d, "c64", seed=23, qk_unit=True)
     inp = gen.make_inputs(w)
     grad = gen.make_grad(w)
     a = run_hip_bwd(w, inp, grad)

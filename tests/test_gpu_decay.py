@@ -229,6 +229,8 @@ BWD_CASES = [
     ("c64", 1, 2, 200, 16),
     ("c64", 1, 1, 150, 17),
     ("bf16", 1, 2, 257, 32),
+    ("c64", 1, 2, 200, 128),
+    ("bf16", 1, 8, 130, 128),
 ]
 
 
@@ -254,7 +256,8 @@ def test_decay_backward(layout, B, H, T, d):
     compare(w, got, ref, f"decay bwd {layout} d{d}", terms)
 
 
-@pytest.mark.parametrize("layout,d", [("bf16", 64), ("c64", 64), ("c64", 16), ("bf16", 32), ("c64", 17)])
+@pytest.mark.parametrize("layout,d", [("bf16", 64), ("c64", 64), ("c64", 16), ("bf16", 32), ("c64", 17), ("c64", 128),
+                                      ("bf16", 128)])
 def test_decay_of_one_backward_is_plain(layout, d):
     # every factor is exp2(0) = 1 exactly: the decayed instances give the plain gradients' bits
     from complex_valued_attention_amd.check import grad_to_device

@@ -153,10 +153,12 @@ def test_born_zero_query_rows(layout, causal, d, eps):
 
 
 BWD_CASES = [
-    # (op, layout, causal, d) -- the bf16 width-64 pair, the fp32 matrix-core pair, the vector pair
+    # (op, layout, causal, d) -- the bf16 width-64 pair, the fp32 matrix-core pairs, the vector pair
     ("born", "bf16", True, 64), ("born", "bf16", False, 64), ("born", "c64", True, 64),
     ("born", "bf16", True, 32), ("born", "c64", True, 17),
     ("pct", "c64", True, 64), ("pct", "bf16", False, 64), ("pct", "c64", False, 16), ("pct", "c64", True, 17),
+    # width 128: the 16 x 16 fp32 matrix-core kernels
+    ("born", "c64", True, 128), ("born", "bf16", False, 128), ("pct", "c64", True, 128), ("pct", "bf16", False, 128),
 ]
 
 
