@@ -46,11 +46,13 @@
 //  * Born only: per query, 1 / l and delta, written as float pairs into the
 //    dq buffer (it holds B H T 8 bytes many times over, and nothing reads it
 //    until the dq kernel overwrites it);
-//  * dkdv: a wave owns 16 keys (K', V' in registers) and streams 16-query
-//    stages of Q', G' (with the pairs, or 1 / ||q||) through LDS: lane = key,
-//    registers = queries; dV'^T += G'^T W, dK'^T += Q'^T P;
-//  * dq: a wave owns 16 queries (Q', G' in registers) and streams 16-key stages
-//    of K', V' through LDS: lane = query, registers = keys; dQ'^T += K'^T P^T.
+//  * dkdv: a wave owns 16 keys (K', V' in registers) and streams 32-query
+//    stages of Q', G' (with the pairs, or 1 / ||q||) through LDS, two 16-query
+//    blocks each: lane = key, registers = queries; dV'^T += G'^T W,
+//    dK'^T += Q'^T P;
+//  * dq: a wave owns 16 queries (Q', G' in registers) and streams 32-key stages
+//    of K', V' through LDS, two 16-key blocks each: lane = query, registers =
+//    keys; dQ'^T += K'^T P^T.
 // Every wave runs every stage of its workgroup with no branch around the
 // products: the causal mask, applied per weight, zeroes the blocks above a
 // wave's diagonal.  (A branch there made the compiler copy the loop-carried
@@ -75,7 +77,7 @@ constexpr int NW = 4;              // waves per workgroup, one per SIMD
 constexpr int NT = 64 * NW;
 constexpr int TR = 16;             // rows owned per wave
 constexpr int BM = TR * NW;        // rows owned per workgroup
-constexpr int BN = 16;             // streamed rows per LDS stage
+constexpr int BN = 32;             // streamed rows per LDS stage (two 16-row blocks)
 constexpr int LPK = NT / BN;       // staging lanes per row
 constexpr int CPT = KD / 4 / LPK;  // 16-byte chunks per staging lane and operand
 constexpr int STAGE = 2 * BN * ROW + 2 * BN;   // two operands and two per-row scalars (floats)
@@ -317,14 +319,16 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
-        const int qb0 = qstart + st * BN;
+        const int qb0s = qstart + st * BN;
         const int buf = st & 1;
-        if (st + 1 < nst) load_stage(qb0 + BN);
-        {   // every wave, every stage: the mask zeroes queries before a lane's key
-            const float *qs = fsm + buf * STAGE;
-            const float *gs = qs + BN * ROW;
-            const float *sa = gs + BN * ROW;
+        if (st + 1 < nst) load_stage(qb0s + BN);
+#pragma unroll
+        for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes queries before a lane's key
+            const float *qs = fsm + buf * STAGE + 16 * sbk * ROW;
+            const float *gs = fsm + buf * STAGE + BN * ROW + 16 * sbk * ROW;
+            const float *sa = fsm + buf * STAGE + 2 * BN * ROW + 16 * sbk;
             const float *sb = sa + BN;
+            const int qb0 = qb0s + 16 * sbk;
             // S, E for 16 queries x 16 keys: lane = key j16, registers = queries 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll
@@ -514,13 +518,15 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
-        const int kb0 = st * BN;
+        const int kb0s = st * BN;
         const int buf = st & 1;
-        if (st + 1 < nst) load_stage(kb0 + BN);
-        {   // every wave, every stage: the mask zeroes keys past a lane's query
-            const float *ks = fsm + buf * STAGE;
-            const float *vs = ks + BN * ROW;
-            const float *rks = vs + BN * ROW;
+        if (st + 1 < nst) load_stage(kb0s + BN);
+#pragma unroll
+        for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes keys past a lane's query
+            const float *ks = fsm + buf * STAGE + 16 * sbk * ROW;
+            const float *vs = fsm + buf * STAGE + BN * ROW + 16 * sbk * ROW;
+            const float *rks = fsm + buf * STAGE + 2 * BN * ROW + 16 * sbk;
+            const int kb0 = kb0s + 16 * sbk;
             // S^T, E^T for 16 keys x 16 queries: lane = query j16, registers = keys 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll

@@ -259,10 +259,10 @@ cattn_status cattn_pct_gate_fwd(int layout,
  * The outputs must not overlap any input or each other.  The arithmetic is
  * fp32 for both layouts (bf16 inputs are widened, outputs rounded to bf16).
  * Each call enqueues two kernels (key-side and query-side gradients), and on
- * the bf16 Born path at d_h = 64 a third before them that writes per-query
- * scalars into the dq_re buffer for the key-side kernel (the query-side
- * kernel then overwrites it); it allocates nothing, uses no atomics and is
- * deterministic.
+ * the bf16 Born path at d_h = 64 and the Born path at d_h = 128 (either
+ * layout) a third before them that writes per-query scalars into the dq_re
+ * buffer for the key-side kernel (the query-side kernel then overwrites it);
+ * it allocates nothing, uses no atomics and is deterministic.
  */
 cattn_status cattn_born_bwd(int layout,
                             const void *q_re, const void *q_im,
