@@ -145,13 +145,13 @@ def main_bwd(args, w):
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] bwd {w.name}: {ms:.4f} ms/step (median {np.median(per):.4f} ms), {tflops:.2f} TFLOP/s")
     # which kernels the library dispatches: bf16 matrix cores for Born at d_h = 64, fp32 matrix
-    # cores (32 x 32 tiles) for complex64 and bf16 planes at d_h 16/32/64, the 16 x 16 fp32
-    # kernels at 128, else fp32 vector code
+    # cores for complex64 and bf16 planes otherwise (16 x 16 tiles at d_h 32/64/128, 32 x 32 at
+    # 16), else fp32 vector code
     mfma = w.op == "born" and w.layout == "bf16" and w.d_h == 64
     mfma32 = not mfma and w.d_h in (16, 32, 64, 128)
     peak = PEAK_TFLOPS["bf16"] if mfma else PEAK_TFLOPS["c64"]
     kern = ("born_bf16_d64_bwd_dkdv_kernel + born_bf16_d64_bwd_dq_kernel" if mfma
-            else "bwd16_dkdv_kernel + bwd16_dq_kernel" if w.d_h == 128
+            else "bwd16_dkdv_kernel + bwd16_dq_kernel" if w.d_h in (32, 64, 128)
             else "bwd_dkdv_f32_kernel + bwd_dq_f32_kernel" if mfma32
             else "bwd_dkdv_kernel + bwd_dq_kernel")
     rec = {

@@ -270,10 +270,10 @@ cattn_status run_bwd(const cattn::BwdProblem &p) {
     if (cattn::supports_born_bf16_d64_bwd(p)) {
         e = cattn::launch_born_bf16_d64_bwd_dkdv(p);
         if (e == hipSuccess) e = cattn::launch_born_bf16_d64_bwd_dq(p);
-    } else if (cattn::supports_bwd_f32_mfma(p)) {
-        e = cattn::launch_bwd_f32_mfma(p);
     } else if (cattn::supports_bwd_f32_mfma16(p)) {
         e = cattn::launch_bwd_f32_mfma16(p);
+    } else if (cattn::supports_bwd_f32_mfma(p)) {
+        e = cattn::launch_bwd_f32_mfma(p);
     } else {
         e = cattn::launch_bwd_generic(p);
     }

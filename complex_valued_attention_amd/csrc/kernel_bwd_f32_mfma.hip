@@ -1,7 +1,7 @@
 // Backward of Born and phase-coherent attention on interleaved complex64 (or
 // bf16 planes, widened to the same fp32 rows on load and rounded back on
 // store) with gfx950 fp32 matrix cores (v_mfma_f32_32x32x2_f32), fp32
-// throughout; head widths 16, 32 and 64.
+// throughout; head width 16 (the wider heads run on the 16 x 16 kernels).
 //
 // Gradients are dL/d(conj z) for a real loss L given G = dL/d(conj O)
 // ("CNet ...", section 3, the Wirtinger accumulation rule (2)).  Born ("CNet
@@ -567,18 +567,14 @@ hipError_t launch_d(const BwdProblem &p) {
 }  // namespace
 
 bool supports_bwd_f32_mfma(const BwdProblem &p) {
-    // complex64, or bf16 planes widened to fp32 on load (bf16 Born at width 64
-    // has its own bf16 matrix-core pair, tried first)
-    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 16 || p.d == 32 || p.d == 64);
+    // complex64, or bf16 planes widened to fp32 on load, at width 16 (the
+    // widths 32, 64 and 128 run on the 16 x 16 kernels, and bf16 Born at 64 on
+    // its own bf16 pair)
+    return (p.op == OP_BORN || p.op == OP_PCT) && p.d == 16;
 }
 
 hipError_t launch_bwd_f32_mfma(const BwdProblem &p) {
-    switch (p.d) {
-        case 16: return launch_d<16>(p);
-        case 32: return launch_d<32>(p);
-        case 64: return launch_d<64>(p);
-        default: return hipErrorNotSupported;
-    }
+    return p.d == 16 ? launch_d<16>(p) : hipErrorNotSupported;
 }
 
 }  // namespace cattn

@@ -1,7 +1,7 @@
-// Backward of Born and phase-coherent attention at head width 128 on
-// interleaved complex64 (or bf16 planes, widened to the same fp32 rows on load
-// and rounded back on store) with gfx950 fp32 matrix cores in their 16 x 16
-// form (v_mfma_f32_16x16x4_f32), fp32 throughout.
+// Backward of Born and phase-coherent attention at head widths 32, 64 and 128
+// on interleaved complex64 (or bf16 planes, widened to the same fp32 rows on
+// load and rounded back on store) with gfx950 fp32 matrix cores in their
+// 16 x 16 form (v_mfma_f32_16x16x4_f32), fp32 throughout.
 //
 // Gradients are dL/d(conj z) for a real loss L given G = dL/d(conj O)
 // ("CNet ...", section 3, the Wirtinger accumulation rule (2)).  Born ("CNet
@@ -14,19 +14,20 @@
 // P_x removing the component along the unit vector x; the bias gradient per
 // query row is sum_j ds.
 //
-// Why the 16 x 16 form at this width.  A complex row of 128 channels is a real
-// row x' = (Re x0, Im x0, ...) of 256 floats.  A wave that owns rows as a
-// register operand holds (rows x 256) / 64 floats per lane: 128 per operand
-// for 32 rows, and each kernel holds two (Q', G' or K', V') beside the
-// gradient accumulators of the same size -- more than a lane has.  With
-// 16-row tiles it is 64 floats per operand and 64 per accumulator.
+// Why the 16 x 16 form.  A complex row of d channels is a real row
+// x' = (Re x0, Im x0, ...) of KD = 2 d floats.  A wave that owns rows as a
+// register operand holds (rows x KD) / 64 floats per lane, and each kernel
+// holds two such operands (Q', G' or K', V') beside gradient accumulators of
+// the same size.  With 32-row tiles that is 128 floats per operand at d = 128,
+// more than a lane has, and at d = 64 it allows one wave per SIMD; with 16-row
+// tiles it is KD / 4 floats: one wave per SIMD at 128, two at 64 and 32.
 //
 // Products (lane l: j16 = l % 16, lane group g = l / 16; an A operand row and
 // a B operand column are j16, the contraction index of a step is g; a result
 // lane holds rows 4 g + r of column j16).
 //  * Scores: the contraction runs over the real row in any order both
 //    operands share; lane group g takes the contiguous quarter
-//    [64 g, 64 g + 64) of the row, so a lane reads its slice of a streamed row
+//    [KQ g, KQ g + KQ), KQ = KD / 4, of the row, so a lane reads its slice of a streamed row
 //    with 16-byte LDS reads.  Re <q, k> = k' . q' and Im <q, k> = k'' . q'
 //    with k'' = (-Im k0, Re k0, ...) (equally q''' . k' with
 //    q''' = (Im q0, -Re q0, ...)): the swapped, sign-flipped partner is formed
@@ -34,12 +35,12 @@
 //    it stands.
 //  * Gradients: over a 16-row block in 4 steps of 4 rows; step t takes row
 //    4 g + t from lane group g, which is its own result register r = t, so the
-//    weights need no shuffle.  Channel tile c, row i stands for real channel
-//    16 i + 4 ((c / 4 + i / 4) mod 4) + c mod 4: the streamed operand a lane
-//    needs for one row is 16 contiguous floats (four 16-byte reads, taken in
-//    an order rotated by i / 4 so that the 16 lanes of a read cover every LDS
-//    bank once), and the gradient a lane ends with is the 64 contiguous
-//    channels of its quarter.  The imaginary part of a complex product uses
+//    weights need no shuffle.  With NC = KD / 16 tiles, channel tile c, row i
+//    stands for real channel NC i + 4 ((c / 4 + rho(i)) mod (NC / 4)) + c mod 4,
+//    rho(i) = i / (64 / NC): the streamed operand a lane needs for one row is
+//    NC contiguous floats (NC / 4 16-byte reads, taken in an order rotated by
+//    rho(i) so that the 16 lanes of a read cover every LDS bank once), and the
+//    gradient a lane ends with is the KQ contiguous channels of its quarter.  The imaginary part of a complex product uses
 //    the partner channel (c ^ 1, the same rotation) with the sign on the weight.
 //
 // Three kernels:
@@ -68,22 +69,31 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int D = 128;
-constexpr int KD = 2 * D;          // real width of a row (floats)
-constexpr int KQ = KD / 4;         // contraction floats per lane group
-constexpr int NC = KD / 16;        // 16-channel tiles of a gradient row
-constexpr int ROW = KD + 4;        // padded LDS row (floats): a 16-lane read of 16 rows covers every bank once
 constexpr int NW = 4;              // waves per workgroup, one per SIMD
 constexpr int NT = 64 * NW;
 constexpr int TR = 16;             // rows owned per wave
 constexpr int BM = TR * NW;        // rows owned per workgroup
 constexpr int BN = 32;             // streamed rows per LDS stage (two 16-row blocks)
 constexpr int LPK = NT / BN;       // staging lanes per row
-constexpr int CPT = KD / 4 / LPK;  // 16-byte chunks per staging lane and operand
-constexpr int STAGE = 2 * BN * ROW + 2 * BN;   // two operands and two per-row scalars (floats)
-constexpr int LDS_BYTES = 2 * STAGE * 4;
-constexpr int KP = 16;             // contraction floats per LDS read batch of the score products
-static_assert(CPT * LPK * 4 == KD, "staging split");
+
+template <int D>
+struct B16 {
+    static constexpr int KD = 2 * D;          // real width of a row (floats)
+    static constexpr int KQ = KD / 4;         // contraction floats per lane group
+    static constexpr int NC = KD / 16;        // 16-row tiles of a gradient; also the floats of a lane's run
+    static constexpr int NCK = NC / 4;        // 16-byte reads per run
+    static constexpr int RDIV = 16 / NCK;     // a run's reads are rotated by (row / RDIV) mod NCK
+    static constexpr int ROW = KD + 4;        // padded LDS row (floats): a 16-lane read of 16 rows covers every bank once
+    static constexpr int NCH = KD / 4;        // 16-byte chunks per row
+    static constexpr int CPT = NCH / LPK;     // chunks per staging lane and operand
+    static constexpr int STAGE = 2 * BN * ROW + 2 * BN;   // two operands and two per-row scalars (floats)
+    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    static constexpr int KP = KQ < 16 ? KQ : 16;          // contraction floats per LDS read batch of the scores
+    // waves per SIMD: at width 128 the owned operands and accumulators need
+    // about 450 registers (dK/dV); at 64 half that, and two waves fit
+    static constexpr int WPE = D >= 128 ? 1 : 2;
+    static_assert(CPT * LPK == NCH && NCK >= 1 && NC % 4 == 0, "width");
+};
 
 __device__ inline f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -97,10 +107,10 @@ __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff000
 
 // Floats f .. f + 3 (complex elements f / 2, f / 2 + 1) of dense row `row`;
 // LAYOUT_BF16 reads the two planes and widens.
-template <int LAY>
+template <int D, int LAY>
 __device__ inline f32x4 load4(const void *re, const void *im, int64_t row, int f) {
     if constexpr (LAY == LAYOUT_C64) {
-        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(re) + row * KD + f);
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(re) + row * (2 * D) + f);
     } else {
         const int64_t el = row * D + f / 2;
         const uint32_t r2 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(re) + el);
@@ -110,10 +120,10 @@ __device__ inline f32x4 load4(const void *re, const void *im, int64_t row, int f
 }
 
 // LAYOUT_BF16 rounds to bf16 (nearest even) and writes the two planes.
-template <int LAY>
+template <int D, int LAY>
 __device__ inline void store4(void *re, void *im, int64_t row, int f, f32x4 v) {
     if constexpr (LAY == LAYOUT_C64) {
-        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(re) + row * KD + f) = v;
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(re) + row * (2 * D) + f) = v;
     } else {
         const int64_t el = row * D + f / 2;
         const f32x2 r = {v[0], v[2]}, i = {v[1], v[3]};
@@ -137,14 +147,16 @@ __device__ inline void lds_row(const float *p, float (&out)[N]) {
     }
 }
 
-// The 16 floats 16 j16 .. 16 j16 + 15 of a streamed LDS row as the gradient
-// products' operand: out[4 p + e] is float 4 ((p + j16 / 4) mod 4) + e of the run.
-__device__ inline void lds_run16(const float *rowp, int j16, float (&out)[16]) {
-    const float *run = rowp + 16 * j16;
-    const int rho = j16 >> 2;
+// The run of NC floats NC j16 .. NC j16 + NC - 1 of a streamed LDS row as the
+// gradient products' operand: out[4 p + e] is float 4 ((p + rho) mod NCK) + e
+// of the run, rho = (j16 / RDIV) mod NCK.
+template <class C>
+__device__ inline void lds_run(const float *rowp, int j16, float (&out)[C::NC]) {
+    const float *run = rowp + C::NC * j16;
+    const int rho = (j16 / C::RDIV) % C::NCK;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(run + 4 * ((p + rho) & 3));
+    for (int p = 0; p < C::NCK; ++p) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(run + 4 * ((p + rho) % C::NCK));
         out[4 * p] = x[0];
         out[4 * p + 1] = x[1];
         out[4 * p + 2] = x[2];
@@ -152,14 +164,20 @@ __device__ inline void lds_run16(const float *rowp, int j16, float (&out)[16]) {
     }
 }
 
-// The owned operand's float at gradient tile c, register r of lane group g:
-// x[16 r + 4 ((c / 4 + g) mod 4) + c mod 4], selected with compile-time
-// indices (c and r unrolled) so that the array stays in registers.
-__device__ inline float own_of(const float (&x)[KQ], int g, int c, int r) {
-    const int m = ((c >> 2) + g) & 3;
-    const float v0 = x[16 * r + (c & 3)], v1 = x[16 * r + 4 + (c & 3)];
-    const float v2 = x[16 * r + 8 + (c & 3)], v3 = x[16 * r + 12 + (c & 3)];
-    return m == 0 ? v0 : m == 1 ? v1 : m == 2 ? v2 : v3;
+// Gradient tile c, register r of lane group g is row i = 4 g + r, real channel
+// NC i + 4 ((c / 4 + rho(i)) mod NCK) + c mod 4 with rho(i) = (i / RDIV) mod NCK:
+// in the lane's quarter of the row, float own_idx = NC r + 4 m + c mod 4.
+template <class C>
+__device__ inline int run_rot(int g, int r) { return ((4 * g + r) / C::RDIV) % C::NCK; }
+// The owned operand's float at gradient tile c, register r, selected with
+// compile-time indices (c and r unrolled) so that the array stays in registers.
+template <class C>
+__device__ inline float own_of(const float (&x)[C::KQ], int g, int c, int r) {
+    const int m = ((c >> 2) + run_rot<C>(g, r)) % C::NCK;
+    float v = x[C::NC * r + (c & 3)];
+#pragma unroll
+    for (int j = 1; j < C::NCK; ++j) v = m == j ? x[C::NC * r + 4 * j + (c & 3)] : v;
+    return v;
 }
 
 // Workgroup -> (head, owned block).  The blocks of a head go to one XCD when
@@ -181,26 +199,29 @@ __device__ inline void map_block(int BH, int nblk, bool heavy_last, int &bh, int
 }
 
 // Streamed rows: thread t stages row t / LPK, chunks t % LPK + LPK i of each
-// operand (the 16 lanes of one LDS write cover a row: every bank once).
+// operand, rotated by 7 chunks on odd rows: the 16 lanes of one LDS write,
+// two rows, then cover every bank once.
+template <int NCH>
 struct Stager {
-    int row, sc;
-    __device__ Stager(int tid) : row(tid / LPK), sc(tid % LPK) {}
-    __device__ int chunk(int i) const { return sc + LPK * i; }
+    int row, sc, rot;
+    __device__ Stager(int tid) : row(tid / LPK), sc(tid % LPK), rot(7 * ((tid / LPK) & 1)) {}
+    __device__ int chunk(int i) const { return (sc + LPK * i + rot) % NCH; }
 };
 
 // ------------------------------------------------------------------------------ per-query scalars (Born)
 // 16 lanes per query row: 1 / l (0 for a zero denominator: O = 0, no gradient)
 // and delta = Re(G^H O), as a float pair at index row of the dq buffer.
-template <int LAY>
+template <int D, int LAY>
 __global__ __launch_bounds__(256) void bwd16_scal_kernel(BwdProblem p, int64_t rows) {
+    using C = B16<D>;
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int sp = threadIdx.x & 15;
     float dl = 0.f;
     if (row < rows) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 gg = load4<LAY>(p.g_re, p.g_im, row, 16 * sp + 4 * i);
-            const f32x4 o = load4<LAY>(p.o_re, p.o_im, row, 16 * sp + 4 * i);
+        for (int i = 0; i < C::NCK; ++i) {
+            const f32x4 gg = load4<D, LAY>(p.g_re, p.g_im, row, C::NC * sp + 4 * i);
+            const f32x4 o = load4<D, LAY>(p.o_re, p.o_im, row, C::NC * sp + 4 * i);
             dl += gg[0] * o[0] + gg[1] * o[1] + gg[2] * o[2] + gg[3] * o[3];
         }
     }
@@ -215,9 +236,10 @@ __global__ __launch_bounds__(256) void bwd16_scal_kernel(BwdProblem p, int64_t r
 // ------------------------------------------------------------------------------ dK, dV
 // DECAY (Born): every weight and D2 carries gamma^(query - key), one
 // exponential per weight (the distance clamped at 0 where the mask zeroes it).
-template <int OP, int LAY, bool DECAY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int OP, int LAY, bool DECAY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(B16<D>::WPE, B16<D>::WPE)))
 void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
+    using C = B16<D>;
     extern __shared__ __align__(16) float fsm[];
     constexpr bool born = OP == OP_BORN;
     const int tid = threadIdx.x;
@@ -236,14 +258,14 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     // K', V' of this wave's 16 keys over the lane group's quarter of the row
     const int kt0 = kb0 + TR * wave;
     const int krow = kt0 + j16;
-    float kre[KQ], vre[KQ];
+    float kre[C::KQ], vre[C::KQ];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < KQ / 4; ++i) {
+    for (int i = 0; i < C::KQ / 4; ++i) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, v = x;
         if (krow < T) {
-            x = load4<LAY>(p.k_re, p.k_im, hrow + krow, g * KQ + 4 * i);
-            v = load4<LAY>(p.v_re, p.v_im, hrow + krow, g * KQ + 4 * i);
+            x = load4<D, LAY>(p.k_re, p.k_im, hrow + krow, g * C::KQ + 4 * i);
+            v = load4<D, LAY>(p.v_re, p.v_im, hrow + krow, g * C::KQ + 4 * i);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -257,24 +279,24 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     const float rk = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;   // PCT: 1 / ||k||
     const float sqd = sqrtf((float)D);
 
-    f32x4 dk[NC], dv[NC];
+    f32x4 dk[C::NC], dv[C::NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) dk[c] = dv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < C::NC; ++c) dk[c] = dv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // query stages: with the causal mask only queries >= this workgroup's first key
     const int qstart = p.causal ? kb0 : 0;
     const int nst = qstart < T ? (T - qstart + BN - 1) / BN : 0;
-    const Stager stg(tid);
-    f32x4 qreg[CPT], greg[CPT];
+    const Stager<C::NCH> stg(tid);
+    f32x4 qreg[C::CPT], greg[C::CPT];
     f32x2 tab = {0.f, 0.f};
     auto load_stage = [&](int q0) {
         const int qr = q0 + stg.row;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
+        for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
             if (qr < T) {
-                a = load4<LAY>(p.q_re, p.q_im, hrow + qr, 4 * stg.chunk(i));
-                b = load4<LAY>(p.g_re, p.g_im, hrow + qr, 4 * stg.chunk(i));
+                a = load4<D, LAY>(p.q_re, p.q_im, hrow + qr, 4 * stg.chunk(i));
+                b = load4<D, LAY>(p.g_re, p.g_im, hrow + qr, 4 * stg.chunk(i));
             }
             qreg[i] = a;
             greg[i] = b;
@@ -286,15 +308,15 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     };
     // per query: Born (1 / l, delta); PCT (1 / ||q||, unused)
     auto store_stage = [&](int buf) {
-        float *qs = fsm + buf * STAGE;
-        float *gs = qs + BN * ROW;
-        float *sa = gs + BN * ROW;
+        float *qs = fsm + buf * C::STAGE;
+        float *gs = qs + BN * C::ROW;
+        float *sa = gs + BN * C::ROW;
         float *sb = sa + BN;
         float x2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            *reinterpret_cast<f32x4 *>(qs + stg.row * ROW + 4 * stg.chunk(i)) = qreg[i];
-            *reinterpret_cast<f32x4 *>(gs + stg.row * ROW + 4 * stg.chunk(i)) = greg[i];
+        for (int i = 0; i < C::CPT; ++i) {
+            *reinterpret_cast<f32x4 *>(qs + stg.row * C::ROW + 4 * stg.chunk(i)) = qreg[i];
+            *reinterpret_cast<f32x4 *>(gs + stg.row * C::ROW + 4 * stg.chunk(i)) = greg[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x2 += qreg[i][e] * qreg[i][e];
         }
@@ -324,20 +346,20 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
         if (st + 1 < nst) load_stage(qb0s + BN);
 #pragma unroll
         for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes queries before a lane's key
-            const float *qs = fsm + buf * STAGE + 16 * sbk * ROW;
-            const float *gs = fsm + buf * STAGE + BN * ROW + 16 * sbk * ROW;
-            const float *sa = fsm + buf * STAGE + 2 * BN * ROW + 16 * sbk;
+            const float *qs = fsm + buf * C::STAGE + 16 * sbk * C::ROW;
+            const float *gs = fsm + buf * C::STAGE + BN * C::ROW + 16 * sbk * C::ROW;
+            const float *sa = fsm + buf * C::STAGE + 2 * BN * C::ROW + 16 * sbk;
             const float *sb = sa + BN;
             const int qb0 = qb0s + 16 * sbk;
             // S, E for 16 queries x 16 keys: lane = key j16, registers = queries 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll
-            for (int p0 = 0; p0 < KQ; p0 += KP) {
-                float qa[KP], ga[KP];
-                lds_row<KP>(qs + j16 * ROW + g * KQ + p0, qa);
-                lds_row<KP>(gs + j16 * ROW + g * KQ + p0, ga);
+            for (int p0 = 0; p0 < C::KQ; p0 += C::KP) {
+                float qa[C::KP], ga[C::KP];
+                lds_row<C::KP>(qs + j16 * C::ROW + g * C::KQ + p0, qa);
+                lds_row<C::KP>(gs + j16 * C::ROW + g * C::KQ + p0, ga);
 #pragma unroll
-                for (int s = 0; s < KP; ++s) {
+                for (int s = 0; s < C::KP; ++s) {
                     sr = mfma16(qa[s], kre[p0 + s], sr);
                     ev = mfma16(ga[s], vre[p0 + s], ev);
                     // Im <q, k> = sum_n q'''[n] k'[n] with q''' = (Im q0, -Re q0, ...): the sign
@@ -370,11 +392,11 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
             // dV'^T += G'^T W, dK'^T += Q'^T Re P - Q''^T Im P; step t takes query 4 g + t
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                float ga2[16], qa2[16];
-                lds_run16(gs + (4 * g + t) * ROW, j16, ga2);
-                lds_run16(qs + (4 * g + t) * ROW, j16, qa2);
+                float ga2[C::NC], qa2[C::NC];
+                lds_run<C>(gs + (4 * g + t) * C::ROW, j16, ga2);
+                lds_run<C>(qs + (4 * g + t) * C::ROW, j16, qa2);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
+                for (int c = 0; c < C::NC; ++c) {
                     dv[c] = mfma16(ga2[c], wl[t], dv[c]);
                     dk[c] = mfma16(qa2[c], pr[t], dk[c]);
                 }
@@ -382,7 +404,7 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
                     // -q''[n]: q'[n + 1] on even n, -q'[n - 1] on odd n
                     const float npi = -pi[t];
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) dk[c] = mfma16(qa2[c ^ 1], (c & 1) ? npi : pi[t], dk[c]);
+                    for (int c = 0; c < C::NC; ++c) dk[c] = mfma16(qa2[c ^ 1], (c & 1) ? npi : pi[t], dk[c]);
                 }
             }
         }
@@ -390,39 +412,39 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
         __syncthreads();
     }
 
-    // lane (key j16, group g), tile c, register r: channel 64 g + 16 r +
-    // 4 ((c / 4 + g) mod 4) + c mod 4, the float own_of(kre, c, r)
+    // lane (key j16, group g), tile c, register r: the owned float own_of(kre, c, r)
     if (!born) {
         float dot = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dot += dk[c][r] * own_of(kre, g, c, r);
+            for (int r = 0; r < 4; ++r) dot += dk[c][r] * own_of<C>(kre, g, c, r);
         dot += __shfl_xor(dot, 16);
         dot += __shfl_xor(dot, 32);
         dot *= rk * rk;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dk[c][r] = (dk[c][r] - dot * own_of(kre, g, c, r)) * rk;
+            for (int r = 0; r < 4; ++r) dk[c][r] = (dk[c][r] - dot * own_of<C>(kre, g, c, r)) * rk;
     }
     if (krow >= T) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int f = g * KQ + 16 * r + 4 * ((q + g) & 3);
-            store4<LAY>(p.dk_re, p.dk_im, hrow + krow, f,
+        for (int q = 0; q < C::NCK; ++q) {
+            const int f = g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK);
+            store4<D, LAY>(p.dk_re, p.dk_im, hrow + krow, f,
                         f32x4{dk[4 * q][r], dk[4 * q + 1][r], dk[4 * q + 2][r], dk[4 * q + 3][r]});
-            store4<LAY>(p.dv_re, p.dv_im, hrow + krow, f,
+            store4<D, LAY>(p.dv_re, p.dv_im, hrow + krow, f,
                         f32x4{dv[4 * q][r], dv[4 * q + 1][r], dv[4 * q + 2][r], dv[4 * q + 3][r]});
         }
 }
 
 // ------------------------------------------------------------------------------ dQ (and db)
-template <int OP, int LAY, bool DECAY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int OP, int LAY, bool DECAY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(B16<D>::WPE, B16<D>::WPE)))
 void bwd16_dq_kernel(BwdProblem p, int nrb) {
+    using C = B16<D>;
     extern __shared__ __align__(16) float fsm[];
     constexpr bool born = OP == OP_BORN;
     const int tid = threadIdx.x;
@@ -441,15 +463,15 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     // Q', G' of this wave's 16 queries over the lane group's quarter of the row
     const int qt0 = m0 + TR * wave;
     const int qrow = qt0 + j16;
-    float qre[KQ], gre[KQ];
+    float qre[C::KQ], gre[C::KQ];
     float dl = 0.f, ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < KQ / 4; ++i) {
+    for (int i = 0; i < C::KQ / 4; ++i) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, gg = x, o = x;
         if (qrow < T) {
-            x = load4<LAY>(p.q_re, p.q_im, hrow + qrow, g * KQ + 4 * i);
-            gg = load4<LAY>(p.g_re, p.g_im, hrow + qrow, g * KQ + 4 * i);
-            if (born) o = load4<LAY>(p.o_re, p.o_im, hrow + qrow, g * KQ + 4 * i);
+            x = load4<D, LAY>(p.q_re, p.q_im, hrow + qrow, g * C::KQ + 4 * i);
+            gg = load4<D, LAY>(p.g_re, p.g_im, hrow + qrow, g * C::KQ + 4 * i);
+            if (born) o = load4<D, LAY>(p.o_re, p.o_im, hrow + qrow, g * C::KQ + 4 * i);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -471,37 +493,37 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     const float iq = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;   // PCT: 1 / ||q|| (0 for a zero row)
     const float rq = sqrtf((float)D) * iq;
 
-    f32x4 dq[NC];
+    f32x4 dq[C::NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) dq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < C::NC; ++c) dq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dsum = 0.f;
 
     const int kend = p.causal ? min(T, m0 + BM) : T;
     const int nst = (kend + BN - 1) / BN;
-    const Stager stg(tid);
-    f32x4 kreg[CPT], vreg[CPT];
+    const Stager<C::NCH> stg(tid);
+    f32x4 kreg[C::CPT], vreg[C::CPT];
     auto load_stage = [&](int k0) {
         const int kr = k0 + stg.row;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
+        for (int i = 0; i < C::CPT; ++i) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
             if (kr < T) {
-                a = load4<LAY>(p.k_re, p.k_im, hrow + kr, 4 * stg.chunk(i));
-                b = load4<LAY>(p.v_re, p.v_im, hrow + kr, 4 * stg.chunk(i));
+                a = load4<D, LAY>(p.k_re, p.k_im, hrow + kr, 4 * stg.chunk(i));
+                b = load4<D, LAY>(p.v_re, p.v_im, hrow + kr, 4 * stg.chunk(i));
             }
             kreg[i] = a;
             vreg[i] = b;
         }
     };
     auto store_stage = [&](int buf) {
-        float *ks = fsm + buf * STAGE;
-        float *vs = ks + BN * ROW;
-        float *rks = vs + BN * ROW;
+        float *ks = fsm + buf * C::STAGE;
+        float *vs = ks + BN * C::ROW;
+        float *rks = vs + BN * C::ROW;
         float s2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            *reinterpret_cast<f32x4 *>(ks + stg.row * ROW + 4 * stg.chunk(i)) = kreg[i];
-            *reinterpret_cast<f32x4 *>(vs + stg.row * ROW + 4 * stg.chunk(i)) = vreg[i];
+        for (int i = 0; i < C::CPT; ++i) {
+            *reinterpret_cast<f32x4 *>(ks + stg.row * C::ROW + 4 * stg.chunk(i)) = kreg[i];
+            *reinterpret_cast<f32x4 *>(vs + stg.row * C::ROW + 4 * stg.chunk(i)) = vreg[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) s2 += kreg[i][e] * kreg[i][e];
         }
@@ -523,19 +545,19 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
         if (st + 1 < nst) load_stage(kb0s + BN);
 #pragma unroll
         for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes keys past a lane's query
-            const float *ks = fsm + buf * STAGE + 16 * sbk * ROW;
-            const float *vs = fsm + buf * STAGE + BN * ROW + 16 * sbk * ROW;
-            const float *rks = fsm + buf * STAGE + 2 * BN * ROW + 16 * sbk;
+            const float *ks = fsm + buf * C::STAGE + 16 * sbk * C::ROW;
+            const float *vs = fsm + buf * C::STAGE + BN * C::ROW + 16 * sbk * C::ROW;
+            const float *rks = fsm + buf * C::STAGE + 2 * BN * C::ROW + 16 * sbk;
             const int kb0 = kb0s + 16 * sbk;
             // S^T, E^T for 16 keys x 16 queries: lane = query j16, registers = keys 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll
-            for (int p0 = 0; p0 < KQ; p0 += KP) {
-                float ka[KP], va[KP];
-                lds_row<KP>(ks + j16 * ROW + g * KQ + p0, ka);
-                lds_row<KP>(vs + j16 * ROW + g * KQ + p0, va);
+            for (int p0 = 0; p0 < C::KQ; p0 += C::KP) {
+                float ka[C::KP], va[C::KP];
+                lds_row<C::KP>(ks + j16 * C::ROW + g * C::KQ + p0, ka);
+                lds_row<C::KP>(vs + j16 * C::ROW + g * C::KQ + p0, va);
 #pragma unroll
-                for (int s = 0; s < KP; ++s) {
+                for (int s = 0; s < C::KP; ++s) {
                     sr = mfma16(ka[s], qre[p0 + s], sr);
                     ev = mfma16(va[s], gre[p0 + s], ev);
                     // Im <q, k> = sum_n k''[n] q'[n] with k'' = (-Im k0, Re k0, ...): the sign and
@@ -566,15 +588,15 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
             // dQ'^T += K'^T Re P^T + K''^T Im P^T; step t takes key 4 g + t
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                float a[16];
-                lds_run16(ks + (4 * g + t) * ROW, j16, a);
+                float a[C::NC];
+                lds_run<C>(ks + (4 * g + t) * C::ROW, j16, a);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) dq[c] = mfma16(a[c], pr[t], dq[c]);
+                for (int c = 0; c < C::NC; ++c) dq[c] = mfma16(a[c], pr[t], dq[c]);
                 if (born) {
                     // k''[n]: -k'[n + 1] on even n, k'[n - 1] on odd n
                     const float npi = -pi[t];
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) dq[c] = mfma16(a[c ^ 1], (c & 1) ? pi[t] : npi, dq[c]);
+                    for (int c = 0; c < C::NC; ++c) dq[c] = mfma16(a[c ^ 1], (c & 1) ? pi[t] : npi, dq[c]);
                 }
             }
         }
@@ -582,25 +604,24 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
         __syncthreads();
     }
 
-    // lane (query j16, group g), tile c, register r: channel 64 g + 16 r +
-    // 4 ((c / 4 + g) mod 4) + c mod 4, the float own_of(qre, c, r)
+    // lane (query j16, group g), tile c, register r: the owned float own_of(qre, c, r)
     if (!born) {
         const float sq = sqrtf((float)D);
         float dot = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < C::NC; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 dq[c][r] *= sq;
-                dot += dq[c][r] * own_of(qre, g, c, r);
+                dot += dq[c][r] * own_of<C>(qre, g, c, r);
             }
         dot += __shfl_xor(dot, 16);
         dot += __shfl_xor(dot, 32);
         dot *= iq * iq;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dq[c][r] = (dq[c][r] - dot * own_of(qre, g, c, r)) * iq;
+            for (int r = 0; r < 4; ++r) dq[c][r] = (dq[c][r] - dot * own_of<C>(qre, g, c, r)) * iq;
         float db = dsum + __shfl_xor(dsum, 16);
         db += __shfl_xor(db, 32);
         if (p.db_rows && g == 0 && qrow < T) p.db_rows[hrow + qrow] = db;
@@ -609,53 +630,63 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            store4<LAY>(p.dq_re, p.dq_im, hrow + qrow, g * KQ + 16 * r + 4 * ((q + g) & 3),
+        for (int q = 0; q < C::NCK; ++q)
+            store4<D, LAY>(p.dq_re, p.dq_im, hrow + qrow, g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK),
                         f32x4{dq[4 * q][r], dq[4 * q + 1][r], dq[4 * q + 2][r], dq[4 * q + 3][r]});
 }
 
-template <int OP, int LAY, bool DECAY = false>
+template <int D, int OP, int LAY, bool DECAY = false>
 hipError_t launch_cfg(const BwdProblem &p) {
+    using C = B16<D>;
     static std::atomic<uint64_t> dq_set{0}, kv_set{0};
     const int nblk = (p.T + BM - 1) / BM;
     const int64_t blocks = (int64_t)p.BH * nblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    auto kkv = bwd16_dkdv_kernel<OP, LAY, DECAY>;
-    auto kdq = bwd16_dq_kernel<OP, LAY, DECAY>;
-    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), LDS_BYTES, kv_set);
+    auto kkv = bwd16_dkdv_kernel<D, OP, LAY, DECAY>;
+    auto kdq = bwd16_dq_kernel<D, OP, LAY, DECAY>;
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kkv), C::LDS_BYTES, kv_set);
     if (e != hipSuccess) return e;
-    e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), LDS_BYTES, dq_set);
+    e = set_dynamic_lds(reinterpret_cast<const void *>(kdq), C::LDS_BYTES, dq_set);
     if (e != hipSuccess) return e;
     if (OP == OP_BORN) {
         const int64_t rows = (int64_t)p.BH * p.T;
         const int64_t sblocks = (rows + 15) / 16;
         if (sblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd16_scal_kernel<LAY>, dim3((unsigned)sblocks), dim3(256), 0, p.stream, p, rows);
+        hipLaunchKernelGGL((bwd16_scal_kernel<D, LAY>), dim3((unsigned)sblocks), dim3(256), 0, p.stream, p, rows);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, p.stream, p, nblk);
+    hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kdq, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, p.stream, p, nblk);
+    hipLaunchKernelGGL(kdq, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nblk);
     return hipGetLastError();
 }
 
-template <int LAY>
+template <int D, int LAY>
 hipError_t launch_op(const BwdProblem &p) {
     if (p.op == OP_BORN)
-        return p.decay.on ? launch_cfg<OP_BORN, LAY, true>(p) : launch_cfg<OP_BORN, LAY>(p);
-    return launch_cfg<OP_PCT, LAY>(p);
+        return p.decay.on ? launch_cfg<D, OP_BORN, LAY, true>(p) : launch_cfg<D, OP_BORN, LAY>(p);
+    return launch_cfg<D, OP_PCT, LAY>(p);
+}
+
+template <int D>
+hipError_t launch_d(const BwdProblem &p) {
+    return p.layout == LAYOUT_C64 ? launch_op<D, LAYOUT_C64>(p) : launch_op<D, LAYOUT_BF16>(p);
 }
 
 }  // namespace
 
 bool supports_bwd_f32_mfma16(const BwdProblem &p) {
-    return (p.op == OP_BORN || p.op == OP_PCT) && p.d == D;
+    return (p.op == OP_BORN || p.op == OP_PCT) && (p.d == 32 || p.d == 64 || p.d == 128);
 }
 
 hipError_t launch_bwd_f32_mfma16(const BwdProblem &p) {
-    return p.layout == LAYOUT_C64 ? launch_op<LAYOUT_C64>(p) : launch_op<LAYOUT_BF16>(p);
+    switch (p.d) {
+        case 32: return launch_d<32>(p);
+        case 64: return launch_d<64>(p);
+        default: return launch_d<128>(p);
+    }
 }
 
 }  // namespace cattn
