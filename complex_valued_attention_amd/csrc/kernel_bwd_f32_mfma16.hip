@@ -20,14 +20,20 @@
 // holds two such operands (Q', G' or K', V') beside gradient accumulators of
 // the same size.  With 32-row tiles that is 128 floats per operand at d = 128,
 // more than a lane has, and at d = 64 it allows one wave per SIMD; with 16-row
-// tiles it is KD / 4 floats: one wave per SIMD at 128, two at 64 and 32.
+// tiles it is KD / 4 floats: two waves per SIMD at 64 and 32.  At 128 Born
+// splits each row tile over two waves, each holding one half of the channels
+// of every owned row and of every gradient row; the two add their partial
+// scores through LDS (one more barrier per block), and two waves per SIMD fit.
+// PCT at 128 (fewer products per block to amortise that exchange) keeps one
+// wave per SIMD with whole rows.
 //
 // Products (lane l: j16 = l % 16, lane group g = l / 16; an A operand row and
 // a B operand column are j16, the contraction index of a step is g; a result
 // lane holds rows 4 g + r of column j16).
-//  * Scores: the contraction runs over the real row in any order both
-//    operands share; lane group g takes the contiguous quarter
-//    [KQ g, KQ g + KQ), KQ = KD / 4, of the row, so a lane reads its slice of a streamed row
+//  * Scores: the contraction runs over the real row (over the wave's channel
+//    group when a row tile is split) in any order both operands share; lane
+//    group g takes the contiguous quarter [KQ g, KQ g + KQ), KQ = KDC / 4, of
+//    it, so a lane reads its slice of a streamed row
 //    with 16-byte LDS reads.  Re <q, k> = k' . q' and Im <q, k> = k'' . q'
 //    with k'' = (-Im k0, Re k0, ...) (equally q''' . k' with
 //    q''' = (Im q0, -Re q0, ...)): the swapped, sign-flipped partner is formed
@@ -35,7 +41,7 @@
 //    it stands.
 //  * Gradients: over a 16-row block in 4 steps of 4 rows; step t takes row
 //    4 g + t from lane group g, which is its own result register r = t, so the
-//    weights need no shuffle.  With NC = KD / 16 tiles, channel tile c, row i
+//    weights need no shuffle.  With NC = KDC / 16 tiles, channel tile c, row i
 //    stands for real channel NC i + 4 ((c / 4 + rho(i)) mod (NC / 4)) + c mod 4,
 //    rho(i) = i / (64 / NC): the streamed operand a lane needs for one row is
 //    NC contiguous floats (NC / 4 16-byte reads, taken in an order rotated by
@@ -47,13 +53,12 @@
 //  * Born only: per query, 1 / l and delta, written as float pairs into the
 //    dq buffer (it holds B H T 8 bytes many times over, and nothing reads it
 //    until the dq kernel overwrites it);
-//  * dkdv: a wave owns 16 keys (K', V' in registers) and streams 32-query
-//    stages of Q', G' (with the pairs, or 1 / ||q||) through LDS, two 16-query
-//    blocks each: lane = key, registers = queries; dV'^T += G'^T W,
-//    dK'^T += Q'^T P;
-//  * dq: a wave owns 16 queries (Q', G' in registers) and streams 32-key stages
-//    of K', V' through LDS, two 16-key blocks each: lane = query, registers =
-//    keys; dQ'^T += K'^T P^T.
+//  * dkdv: a wave owns 16 keys (K', V' in registers) and streams stages of
+//    32 queries (16 with split row tiles) of Q', G' (with the pairs, or
+//    1 / ||q||) through LDS, in 16-query blocks: lane = key, registers =
+//    queries; dV'^T += G'^T W, dK'^T += Q'^T P;
+//  * dq: a wave owns 16 queries (Q', G' in registers) and streams stages of K',
+//    V' the same way: lane = query, registers = keys; dQ'^T += K'^T P^T.
 // Every wave runs every stage of its workgroup with no branch around the
 // products: the causal mask, applied per weight, zeroes the blocks above a
 // wave's diagonal.  (A branch there made the compiler copy the loop-carried
@@ -69,29 +74,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;              // waves per workgroup, one per SIMD
-constexpr int NT = 64 * NW;
-constexpr int TR = 16;             // rows owned per wave
-constexpr int BM = TR * NW;        // rows owned per workgroup
-constexpr int BN = 32;             // streamed rows per LDS stage (two 16-row blocks)
-constexpr int LPK = NT / BN;       // staging lanes per row
+constexpr int TR = 16;             // rows owned per row tile
+constexpr int NW = 4;              // waves per workgroup
 
-template <int D>
+template <int D, int CH_ = 1>
 struct B16 {
+    // Channel groups per row tile: at width 128 two waves share a row tile,
+    // each holding one half of every owned row and of every gradient row
+    // (about 250 registers a wave instead of 450: two waves per SIMD), and
+    // they add their partial scores through LDS.
+    static constexpr int CH = CH_;
+    static constexpr int NRT = NW / CH;       // row tiles per workgroup
+    static constexpr int BM = TR * NRT;       // rows owned per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int BN = CH > 1 ? 16 : 32;   // streamed rows per LDS stage (16-row blocks)
+    static constexpr int LPK = NT / BN;       // staging lanes per row
     static constexpr int KD = 2 * D;          // real width of a row (floats)
-    static constexpr int KQ = KD / 4;         // contraction floats per lane group
-    static constexpr int NC = KD / 16;        // 16-row tiles of a gradient; also the floats of a lane's run
+    static constexpr int KDC = KD / CH;       // real channels of a wave's group
+    static constexpr int KQ = KDC / 4;        // contraction floats per lane group
+    static constexpr int NC = KDC / 16;       // 16-row tiles of a gradient; also the floats of a lane's run
     static constexpr int NCK = NC / 4;        // 16-byte reads per run
     static constexpr int RDIV = 16 / NCK;     // a run's reads are rotated by (row / RDIV) mod NCK
     static constexpr int ROW = KD + 4;        // padded LDS row (floats): a 16-lane read of 16 rows covers every bank once
     static constexpr int NCH = KD / 4;        // 16-byte chunks per row
     static constexpr int CPT = NCH / LPK;     // chunks per staging lane and operand
     static constexpr int STAGE = 2 * BN * ROW + 2 * BN;   // two operands and two per-row scalars (floats)
-    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    static constexpr int XCH = CH > 1 ? NW * 12 * 64 : 0;  // per wave, 12 partial sums a lane
+    static constexpr int LDS_BYTES = (2 * STAGE + XCH) * 4;
     static constexpr int KP = KQ < 16 ? KQ : 16;          // contraction floats per LDS read batch of the scores
-    // waves per SIMD: at width 128 the owned operands and accumulators need
-    // about 450 registers (dK/dV); at 64 half that, and two waves fit
-    static constexpr int WPE = D >= 128 ? 1 : 2;
+    // waves per SIMD: two, except at width 128 without channel groups (about
+    // 450 registers a wave)
+    static constexpr int WPE = D >= 128 && CH == 1 ? 1 : 2;
     static_assert(CPT * LPK == NCH && NCK >= 1 && NC % 4 == 0, "width");
 };
 
@@ -133,6 +146,10 @@ __device__ inline void store4(void *re, void *im, int64_t row, int f, f32x4 v) {
             __builtin_bit_cast(uint32_t, __builtin_convertvector(i, bf16x2));
     }
 }
+
+// Channel groups per row tile: two for Born at width 128 (its products per
+// block amortise the score exchange); PCT there keeps one wave per SIMD.
+constexpr int ch_of(int D, int OP) { return D >= 128 && OP == OP_BORN ? 2 : 1; }
 
 // n floats from LDS with 16-byte reads
 template <int N>
@@ -201,12 +218,28 @@ __device__ inline void map_block(int BH, int nblk, bool heavy_last, int &bh, int
 // Streamed rows: thread t stages row t / LPK, chunks t % LPK + LPK i of each
 // operand, rotated by 7 chunks on odd rows: the 16 lanes of one LDS write,
 // two rows, then cover every bank once.
-template <int NCH>
+template <int NCH, int LPK>
 struct Stager {
     int row, sc, rot;
     __device__ Stager(int tid) : row(tid / LPK), sc(tid % LPK), rot(7 * ((tid / LPK) & 1)) {}
     __device__ int chunk(int i) const { return (sc + LPK * i + rot) % NCH; }
 };
+
+// CH > 1: the sum of value x over the waves of a row tile, through the
+// exchange area (slot k of 12), the same in every wave of the tile; a
+// workgroup barrier makes the partners' values visible and another frees the
+// slot again (all waves reach both).
+template <class C>
+__device__ inline float tile_sum(float *xch, int wave, int lane, int k, float x) {
+    const int w0 = wave - wave % C::CH;
+    xch[(wave * 12 + k) * 64 + lane] = x;
+    __syncthreads();
+    float t = xch[(w0 * 12 + k) * 64 + lane];
+#pragma unroll
+    for (int c = 1; c < C::CH; ++c) t += xch[((w0 + c) * 12 + k) * 64 + lane];
+    __syncthreads();
+    return t;
+}
 
 // ------------------------------------------------------------------------------ per-query scalars (Born)
 // 16 lanes per query row: 1 / l (0 for a zero denominator: O = 0, no gradient)
@@ -217,11 +250,12 @@ __global__ __launch_bounds__(256) void bwd16_scal_kernel(BwdProblem p, int64_t r
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int sp = threadIdx.x & 15;
     float dl = 0.f;
+    constexpr int PER = C::KD / 16;   // floats of the row per lane
     if (row < rows) {
 #pragma unroll
-        for (int i = 0; i < C::NCK; ++i) {
-            const f32x4 gg = load4<D, LAY>(p.g_re, p.g_im, row, C::NC * sp + 4 * i);
-            const f32x4 o = load4<D, LAY>(p.o_re, p.o_im, row, C::NC * sp + 4 * i);
+        for (int i = 0; i < PER / 4; ++i) {
+            const f32x4 gg = load4<D, LAY>(p.g_re, p.g_im, row, PER * sp + 4 * i);
+            const f32x4 o = load4<D, LAY>(p.o_re, p.o_im, row, PER * sp + 4 * i);
             dl += gg[0] * o[0] + gg[1] * o[1] + gg[2] * o[2] + gg[3] * o[3];
         }
     }
@@ -237,9 +271,10 @@ __global__ __launch_bounds__(256) void bwd16_scal_kernel(BwdProblem p, int64_t r
 // DECAY (Born): every weight and D2 carries gamma^(query - key), one
 // exponential per weight (the distance clamped at 0 where the mask zeroes it).
 template <int D, int OP, int LAY, bool DECAY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(B16<D>::WPE, B16<D>::WPE)))
+__global__ __launch_bounds__((B16<D, ch_of(D, OP)>::NT))
+__attribute__((amdgpu_waves_per_eu((B16<D, ch_of(D, OP)>::WPE), (B16<D, ch_of(D, OP)>::WPE))))
 void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
-    using C = B16<D>;
+    using C = B16<D, ch_of(D, OP)>;
     extern __shared__ __align__(16) float fsm[];
     constexpr bool born = OP == OP_BORN;
     const int tid = threadIdx.x;
@@ -248,15 +283,18 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     const int j16 = lane & 15;
     const int g = lane >> 4;
     const int T = p.T;
+    const int rt = wave / C::CH, hc = wave % C::CH;   // row tile, channel group
+    const int cg0 = C::KDC * hc;                      // first real channel of the group
+    float *xch = fsm + 2 * C::STAGE;                  // CH > 1: the exchange area
 
     int bh, kblk;
     map_block(p.BH, nkb, false, bh, kblk);
-    const int kb0 = kblk * BM;
+    const int kb0 = kblk * C::BM;
     const int64_t hrow = (int64_t)bh * T;   // this head's first row
     const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
 
-    // K', V' of this wave's 16 keys over the lane group's quarter of the row
-    const int kt0 = kb0 + TR * wave;
+    // K', V' of this wave's 16 keys over the lane group's quarter of its channel group
+    const int kt0 = kb0 + TR * rt;
     const int krow = kt0 + j16;
     float kre[C::KQ], vre[C::KQ];
     float ss = 0.f;
@@ -264,8 +302,8 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     for (int i = 0; i < C::KQ / 4; ++i) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, v = x;
         if (krow < T) {
-            x = load4<D, LAY>(p.k_re, p.k_im, hrow + krow, g * C::KQ + 4 * i);
-            v = load4<D, LAY>(p.v_re, p.v_im, hrow + krow, g * C::KQ + 4 * i);
+            x = load4<D, LAY>(p.k_re, p.k_im, hrow + krow, cg0 + g * C::KQ + 4 * i);
+            v = load4<D, LAY>(p.v_re, p.v_im, hrow + krow, cg0 + g * C::KQ + 4 * i);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -276,6 +314,7 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
+    if constexpr (C::CH > 1) ss = tile_sum<C>(xch, wave, lane, 0, ss);
     const float rk = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;   // PCT: 1 / ||k||
     const float sqd = sqrtf((float)D);
 
@@ -285,8 +324,8 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
 
     // query stages: with the causal mask only queries >= this workgroup's first key
     const int qstart = p.causal ? kb0 : 0;
-    const int nst = qstart < T ? (T - qstart + BN - 1) / BN : 0;
-    const Stager<C::NCH> stg(tid);
+    const int nst = qstart < T ? (T - qstart + C::BN - 1) / C::BN : 0;
+    const Stager<C::NCH, C::LPK> stg(tid);
     f32x4 qreg[C::CPT], greg[C::CPT];
     f32x2 tab = {0.f, 0.f};
     auto load_stage = [&](int q0) {
@@ -309,9 +348,9 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     // per query: Born (1 / l, delta); PCT (1 / ||q||, unused)
     auto store_stage = [&](int buf) {
         float *qs = fsm + buf * C::STAGE;
-        float *gs = qs + BN * C::ROW;
-        float *sa = gs + BN * C::ROW;
-        float *sb = sa + BN;
+        float *gs = qs + C::BN * C::ROW;
+        float *sa = gs + C::BN * C::ROW;
+        float *sb = sa + C::BN;
         float x2 = 0.f;
 #pragma unroll
         for (int i = 0; i < C::CPT; ++i) {
@@ -322,7 +361,7 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
         }
         if (!born) {
 #pragma unroll
-            for (int o = 1; o < LPK; o <<= 1) x2 += __shfl_xor(x2, o);
+            for (int o = 1; o < C::LPK; o <<= 1) x2 += __shfl_xor(x2, o);
         }
         if (stg.sc == 0) {
             if (born) {
@@ -341,23 +380,23 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
-        const int qb0s = qstart + st * BN;
+        const int qb0s = qstart + st * C::BN;
         const int buf = st & 1;
-        if (st + 1 < nst) load_stage(qb0s + BN);
+        if (st + 1 < nst) load_stage(qb0s + C::BN);
 #pragma unroll
-        for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes queries before a lane's key
+        for (int sbk = 0; sbk < C::BN / 16; ++sbk) {   // every wave, every block: the mask zeroes queries before a lane's key
             const float *qs = fsm + buf * C::STAGE + 16 * sbk * C::ROW;
-            const float *gs = fsm + buf * C::STAGE + BN * C::ROW + 16 * sbk * C::ROW;
-            const float *sa = fsm + buf * C::STAGE + 2 * BN * C::ROW + 16 * sbk;
-            const float *sb = sa + BN;
+            const float *gs = fsm + buf * C::STAGE + C::BN * C::ROW + 16 * sbk * C::ROW;
+            const float *sa = fsm + buf * C::STAGE + 2 * C::BN * C::ROW + 16 * sbk;
+            const float *sb = sa + C::BN;
             const int qb0 = qb0s + 16 * sbk;
             // S, E for 16 queries x 16 keys: lane = key j16, registers = queries 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll
             for (int p0 = 0; p0 < C::KQ; p0 += C::KP) {
                 float qa[C::KP], ga[C::KP];
-                lds_row<C::KP>(qs + j16 * C::ROW + g * C::KQ + p0, qa);
-                lds_row<C::KP>(gs + j16 * C::ROW + g * C::KQ + p0, ga);
+                lds_row<C::KP>(qs + j16 * C::ROW + cg0 + g * C::KQ + p0, qa);
+                lds_row<C::KP>(gs + j16 * C::ROW + cg0 + g * C::KQ + p0, ga);
 #pragma unroll
                 for (int s = 0; s < C::KP; ++s) {
                     sr = mfma16(qa[s], kre[p0 + s], sr);
@@ -365,6 +404,28 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
                     // Im <q, k> = sum_n q'''[n] k'[n] with q''' = (Im q0, -Re q0, ...): the sign
                     // and the swap on the streamed operand (a quarter starts on an even index)
                     if (born) si = mfma16((s & 1) ? -qa[s - 1] : qa[s + 1], kre[p0 + s], si);
+                }
+            }
+            if constexpr (C::CH > 1) {   // the partial sums of the tile's channel groups
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xch[(wave * 12 + r) * 64 + lane] = sr[r];
+                    xch[(wave * 12 + 4 + r) * 64 + lane] = si[r];
+                    xch[(wave * 12 + 8 + r) * 64 + lane] = ev[r];
+                }
+                __syncthreads();
+                const int w0 = C::CH * rt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sr[r] = xch[(w0 * 12 + r) * 64 + lane];
+                    si[r] = xch[(w0 * 12 + 4 + r) * 64 + lane];
+                    ev[r] = xch[(w0 * 12 + 8 + r) * 64 + lane];
+#pragma unroll
+                    for (int c = 1; c < C::CH; ++c) {
+                        sr[r] += xch[((w0 + c) * 12 + r) * 64 + lane];
+                        si[r] += xch[((w0 + c) * 12 + 4 + r) * 64 + lane];
+                        ev[r] += xch[((w0 + c) * 12 + 8 + r) * 64 + lane];
+                    }
                 }
             }
             const f32x4 av = *reinterpret_cast<const f32x4 *>(sa + 4 * g);
@@ -393,8 +454,8 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 float ga2[C::NC], qa2[C::NC];
-                lds_run<C>(gs + (4 * g + t) * C::ROW, j16, ga2);
-                lds_run<C>(qs + (4 * g + t) * C::ROW, j16, qa2);
+                lds_run<C>(gs + (4 * g + t) * C::ROW + cg0, j16, ga2);
+                lds_run<C>(qs + (4 * g + t) * C::ROW + cg0, j16, qa2);
 #pragma unroll
                 for (int c = 0; c < C::NC; ++c) {
                     dv[c] = mfma16(ga2[c], wl[t], dv[c]);
@@ -421,6 +482,7 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
             for (int r = 0; r < 4; ++r) dot += dk[c][r] * own_of<C>(kre, g, c, r);
         dot += __shfl_xor(dot, 16);
         dot += __shfl_xor(dot, 32);
+        if constexpr (C::CH > 1) dot = tile_sum<C>(xch, wave, lane, 0, dot);
         dot *= rk * rk;
 #pragma unroll
         for (int c = 0; c < C::NC; ++c)
@@ -432,7 +494,7 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < C::NCK; ++q) {
-            const int f = g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK);
+            const int f = cg0 + g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK);
             store4<D, LAY>(p.dk_re, p.dk_im, hrow + krow, f,
                         f32x4{dk[4 * q][r], dk[4 * q + 1][r], dk[4 * q + 2][r], dk[4 * q + 3][r]});
             store4<D, LAY>(p.dv_re, p.dv_im, hrow + krow, f,
@@ -442,9 +504,10 @@ void bwd16_dkdv_kernel(BwdProblem p, int nkb) {
 
 // ------------------------------------------------------------------------------ dQ (and db)
 template <int D, int OP, int LAY, bool DECAY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(B16<D>::WPE, B16<D>::WPE)))
+__global__ __launch_bounds__((B16<D, ch_of(D, OP)>::NT))
+__attribute__((amdgpu_waves_per_eu((B16<D, ch_of(D, OP)>::WPE), (B16<D, ch_of(D, OP)>::WPE))))
 void bwd16_dq_kernel(BwdProblem p, int nrb) {
-    using C = B16<D>;
+    using C = B16<D, ch_of(D, OP)>;
     extern __shared__ __align__(16) float fsm[];
     constexpr bool born = OP == OP_BORN;
     const int tid = threadIdx.x;
@@ -453,15 +516,18 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     const int j16 = lane & 15;
     const int g = lane >> 4;
     const int T = p.T;
+    const int rt = wave / C::CH, hc = wave % C::CH;   // row tile, channel group
+    const int cg0 = C::KDC * hc;                      // first real channel of the group
+    float *xch = fsm + 2 * C::STAGE;                  // CH > 1: the exchange area
 
     int bh, rb;
     map_block(p.BH, nrb, true, bh, rb);
-    const int m0 = rb * BM;
+    const int m0 = rb * C::BM;
     const int64_t hrow = (int64_t)bh * T;
     const float lg2 = DECAY ? p.decay.lg2[bh % p.H] : 0.f;
 
-    // Q', G' of this wave's 16 queries over the lane group's quarter of the row
-    const int qt0 = m0 + TR * wave;
+    // Q', G' of this wave's 16 queries over the lane group's quarter of its channel group
+    const int qt0 = m0 + TR * rt;
     const int qrow = qt0 + j16;
     float qre[C::KQ], gre[C::KQ];
     float dl = 0.f, ss = 0.f;
@@ -469,9 +535,9 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     for (int i = 0; i < C::KQ / 4; ++i) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, gg = x, o = x;
         if (qrow < T) {
-            x = load4<D, LAY>(p.q_re, p.q_im, hrow + qrow, g * C::KQ + 4 * i);
-            gg = load4<D, LAY>(p.g_re, p.g_im, hrow + qrow, g * C::KQ + 4 * i);
-            if (born) o = load4<D, LAY>(p.o_re, p.o_im, hrow + qrow, g * C::KQ + 4 * i);
+            x = load4<D, LAY>(p.q_re, p.q_im, hrow + qrow, cg0 + g * C::KQ + 4 * i);
+            gg = load4<D, LAY>(p.g_re, p.g_im, hrow + qrow, cg0 + g * C::KQ + 4 * i);
+            if (born) o = load4<D, LAY>(p.o_re, p.o_im, hrow + qrow, cg0 + g * C::KQ + 4 * i);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -485,6 +551,10 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     dl += __shfl_xor(dl, 32);
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
+    if constexpr (C::CH > 1) {
+        dl = tile_sum<C>(xch, wave, lane, 0, dl);
+        ss = tile_sum<C>(xch, wave, lane, 1, ss);
+    }
     float inv_l = 0.f;   // Born: 1 / l (0 for a zero denominator: O = 0, no gradient)
     if (born && qrow < T) {
         const float l = p.row_den[hrow + qrow];
@@ -498,9 +568,9 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     for (int c = 0; c < C::NC; ++c) dq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dsum = 0.f;
 
-    const int kend = p.causal ? min(T, m0 + BM) : T;
-    const int nst = (kend + BN - 1) / BN;
-    const Stager<C::NCH> stg(tid);
+    const int kend = p.causal ? min(T, m0 + C::BM) : T;
+    const int nst = (kend + C::BN - 1) / C::BN;
+    const Stager<C::NCH, C::LPK> stg(tid);
     f32x4 kreg[C::CPT], vreg[C::CPT];
     auto load_stage = [&](int k0) {
         const int kr = k0 + stg.row;
@@ -517,8 +587,8 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     };
     auto store_stage = [&](int buf) {
         float *ks = fsm + buf * C::STAGE;
-        float *vs = ks + BN * C::ROW;
-        float *rks = vs + BN * C::ROW;
+        float *vs = ks + C::BN * C::ROW;
+        float *rks = vs + C::BN * C::ROW;
         float s2 = 0.f;
 #pragma unroll
         for (int i = 0; i < C::CPT; ++i) {
@@ -529,7 +599,7 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
         }
         if (!born) {
 #pragma unroll
-            for (int o = 1; o < LPK; o <<= 1) s2 += __shfl_xor(s2, o);
+            for (int o = 1; o < C::LPK; o <<= 1) s2 += __shfl_xor(s2, o);
             if (stg.sc == 0) rks[stg.row] = s2 > 0.f ? 1.f / sqrtf(s2) : 0.f;
         }
     };
@@ -540,22 +610,22 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
-        const int kb0s = st * BN;
+        const int kb0s = st * C::BN;
         const int buf = st & 1;
-        if (st + 1 < nst) load_stage(kb0s + BN);
+        if (st + 1 < nst) load_stage(kb0s + C::BN);
 #pragma unroll
-        for (int sbk = 0; sbk < BN / 16; ++sbk) {   // every wave, every block: the mask zeroes keys past a lane's query
+        for (int sbk = 0; sbk < C::BN / 16; ++sbk) {   // every wave, every block: the mask zeroes keys past a lane's query
             const float *ks = fsm + buf * C::STAGE + 16 * sbk * C::ROW;
-            const float *vs = fsm + buf * C::STAGE + BN * C::ROW + 16 * sbk * C::ROW;
-            const float *rks = fsm + buf * C::STAGE + 2 * BN * C::ROW + 16 * sbk;
+            const float *vs = fsm + buf * C::STAGE + C::BN * C::ROW + 16 * sbk * C::ROW;
+            const float *rks = fsm + buf * C::STAGE + 2 * C::BN * C::ROW + 16 * sbk;
             const int kb0 = kb0s + 16 * sbk;
             // S^T, E^T for 16 keys x 16 queries: lane = query j16, registers = keys 4 g + r
             f32x4 sr = {0.f, 0.f, 0.f, 0.f}, si = sr, ev = sr;
 #pragma unroll
             for (int p0 = 0; p0 < C::KQ; p0 += C::KP) {
                 float ka[C::KP], va[C::KP];
-                lds_row<C::KP>(ks + j16 * C::ROW + g * C::KQ + p0, ka);
-                lds_row<C::KP>(vs + j16 * C::ROW + g * C::KQ + p0, va);
+                lds_row<C::KP>(ks + j16 * C::ROW + cg0 + g * C::KQ + p0, ka);
+                lds_row<C::KP>(vs + j16 * C::ROW + cg0 + g * C::KQ + p0, va);
 #pragma unroll
                 for (int s = 0; s < C::KP; ++s) {
                     sr = mfma16(ka[s], qre[p0 + s], sr);
@@ -563,6 +633,28 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
                     // Im <q, k> = sum_n k''[n] q'[n] with k'' = (-Im k0, Re k0, ...): the sign and
                     // the swap on the streamed operand
                     if (born) si = mfma16((s & 1) ? ka[s - 1] : -ka[s + 1], qre[p0 + s], si);
+                }
+            }
+            if constexpr (C::CH > 1) {   // the partial sums of the tile's channel groups
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xch[(wave * 12 + r) * 64 + lane] = sr[r];
+                    xch[(wave * 12 + 4 + r) * 64 + lane] = si[r];
+                    xch[(wave * 12 + 8 + r) * 64 + lane] = ev[r];
+                }
+                __syncthreads();
+                const int w0 = C::CH * rt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sr[r] = xch[(w0 * 12 + r) * 64 + lane];
+                    si[r] = xch[(w0 * 12 + 4 + r) * 64 + lane];
+                    ev[r] = xch[(w0 * 12 + 8 + r) * 64 + lane];
+#pragma unroll
+                    for (int c = 1; c < C::CH; ++c) {
+                        sr[r] += xch[((w0 + c) * 12 + r) * 64 + lane];
+                        si[r] += xch[((w0 + c) * 12 + 4 + r) * 64 + lane];
+                        ev[r] += xch[((w0 + c) * 12 + 8 + r) * 64 + lane];
+                    }
                 }
             }
             f32x4 rkv = {0.f, 0.f, 0.f, 0.f};
@@ -589,7 +681,7 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 float a[C::NC];
-                lds_run<C>(ks + (4 * g + t) * C::ROW, j16, a);
+                lds_run<C>(ks + (4 * g + t) * C::ROW + cg0, j16, a);
 #pragma unroll
                 for (int c = 0; c < C::NC; ++c) dq[c] = mfma16(a[c], pr[t], dq[c]);
                 if (born) {
@@ -617,6 +709,7 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
             }
         dot += __shfl_xor(dot, 16);
         dot += __shfl_xor(dot, 32);
+        if constexpr (C::CH > 1) dot = tile_sum<C>(xch, wave, lane, 0, dot);
         dot *= iq * iq;
 #pragma unroll
         for (int c = 0; c < C::NC; ++c)
@@ -624,22 +717,22 @@ void bwd16_dq_kernel(BwdProblem p, int nrb) {
             for (int r = 0; r < 4; ++r) dq[c][r] = (dq[c][r] - dot * own_of<C>(qre, g, c, r)) * iq;
         float db = dsum + __shfl_xor(dsum, 16);
         db += __shfl_xor(db, 32);
-        if (p.db_rows && g == 0 && qrow < T) p.db_rows[hrow + qrow] = db;
+        if (p.db_rows && g == 0 && hc == 0 && qrow < T) p.db_rows[hrow + qrow] = db;
     }
     if (qrow >= T) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < C::NCK; ++q)
-            store4<D, LAY>(p.dq_re, p.dq_im, hrow + qrow, g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK),
+            store4<D, LAY>(p.dq_re, p.dq_im, hrow + qrow, cg0 + g * C::KQ + C::NC * r + 4 * ((q + run_rot<C>(g, r)) % C::NCK),
                         f32x4{dq[4 * q][r], dq[4 * q + 1][r], dq[4 * q + 2][r], dq[4 * q + 3][r]});
 }
 
 template <int D, int OP, int LAY, bool DECAY = false>
 hipError_t launch_cfg(const BwdProblem &p) {
-    using C = B16<D>;
+    using C = B16<D, ch_of(D, OP)>;
     static std::atomic<uint64_t> dq_set{0}, kv_set{0};
-    const int nblk = (p.T + BM - 1) / BM;
+    const int nblk = (p.T + C::BM - 1) / C::BM;
     const int64_t blocks = (int64_t)p.BH * nblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     auto kkv = bwd16_dkdv_kernel<D, OP, LAY, DECAY>;
@@ -656,10 +749,10 @@ hipError_t launch_cfg(const BwdProblem &p) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nblk);
+    hipLaunchKernelGGL(kkv, dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES, p.stream, p, nblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kdq, dim3((unsigned)blocks), dim3(NT), C::LDS_BYTES, p.stream, p, nblk);
+    hipLaunchKernelGGL(kdq, dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES, p.stream, p, nblk);
     return hipGetLastError();
 }
 
