@@ -23,8 +23,9 @@
 // each lane's 16 accumulator values are directly the bf16 B operand of the
 // next product (no shuffles).
 //
-//  * dQ kernel: a workgroup of 8 waves owns 256 queries (32 per wave, the
-//    wave's Q' and G' in registers) and streams K and V.  Per 32-key block:
+//  * dQ kernel: a workgroup of 4 waves owns 128 queries (32 per wave, the
+//    wave's Q' and G' in registers) and streams K and V; two workgroups per
+//    compute unit.  Per 32-key block:
 //    S^T and E^T (keys x queries), P^T, then dQ^T += K^T P^T.
 //  * dK/dV kernel: a workgroup owns 128 keys (K' and V' in registers) and
 //    streams Q and G with the per-query 1/l and delta/l (formed once per
@@ -209,14 +210,16 @@ __device__ inline void work_item(const BwdProblem &p, int nwork, int &bh, int &i
 
 // ---------------------------------------------------------------------------- dQ
 constexpr int QREG = 4;   // K re, K im, V re, V im, each staged once (swizzle swz_b)
-// The dQ kernel runs 8 waves (two per SIMD) over 256 queries: every staged
-// K/V stage feeds twice the queries, and one wave's waits are filled by the other.
-constexpr int QNW = 8;
+// The dQ kernel runs two waves per SIMD (256 registers) from two workgroups
+// of 4 waves over 128 queries each: one wave's waits, barriers included, are
+// filled by a wave of the other workgroup.
+constexpr int QNW = 4;
 constexpr int QNT = 64 * QNW;
 constexpr int QBT = 32 * QNW;
 
 template <bool DECAY>
-__global__ __launch_bounds__(QNT) void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
+__global__ __launch_bounds__(QNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void born_bf16_d64_bwd_dq_kernel(BwdProblem p, int nrb, int nwork) {
     __shared__ __align__(16) char lds[2 * QREG * REGION];
 
     const int tid = threadIdx.x;
