@@ -43,9 +43,10 @@
 //    4 g + t from lane group g, which is its own result register r = t, so the
 //    weights need no shuffle.  With NC = KDC / 16 tiles, channel tile c, row i
 //    stands for real channel NC i + 4 ((c / 4 + rho(i)) mod (NC / 4)) + c mod 4,
-//    rho(i) = i / (64 / NC): the streamed operand a lane needs for one row is
-//    NC contiguous floats (NC / 4 16-byte reads, taken in an order rotated by
-//    rho(i) so that the 16 lanes of a read cover every LDS bank once), and the
+//    rho(i) = (i / (32 / NC) + i / 8) mod (NC / 4): the streamed operand a lane
+//    needs for one row is NC contiguous floats (NC / 4 16-byte reads, taken in
+//    an order rotated by rho(i) so that each bank is touched once by every 16
+//    lanes of a read over 64 banks and by every 8 over 32), and the
 //    gradient a lane ends with is the KQ contiguous channels of its quarter.  The imaginary part of a complex product uses
 //    the partner channel (c ^ 1, the same rotation) with the sign on the weight.
 //
@@ -94,7 +95,7 @@ struct B16 {
     static constexpr int KQ = KDC / 4;        // contraction floats per lane group
     static constexpr int NC = KDC / 16;       // 16-row tiles of a gradient; also the floats of a lane's run
     static constexpr int NCK = NC / 4;        // 16-byte reads per run
-    static constexpr int RDIV = 16 / NCK;     // a run's reads are rotated by (row / RDIV) mod NCK
+    static constexpr int RDIV = 8 / NCK;      // a run's reads are rotated by (row / RDIV + row / 8) mod NCK
     static constexpr int ROW = KD + 4;        // padded LDS row (floats): a 16-lane read of 16 rows covers every bank once
     static constexpr int NCH = KD / 4;        // 16-byte chunks per row
     static constexpr int CPT = NCH / LPK;     // chunks per staging lane and operand
@@ -166,11 +167,13 @@ __device__ inline void lds_row(const float *p, float (&out)[N]) {
 
 // The run of NC floats NC j16 .. NC j16 + NC - 1 of a streamed LDS row as the
 // gradient products' operand: out[4 p + e] is float 4 ((p + rho) mod NCK) + e
-// of the run, rho = (j16 / RDIV) mod NCK.
+// of the run, rho = rho_of(j16).
+template <class C>
+__device__ inline int rho_of(int i) { return (i / C::RDIV + i / 8) % C::NCK; }
 template <class C>
 __device__ inline void lds_run(const float *rowp, int j16, float (&out)[C::NC]) {
     const float *run = rowp + C::NC * j16;
-    const int rho = (j16 / C::RDIV) % C::NCK;
+    const int rho = rho_of<C>(j16);
 #pragma unroll
     for (int p = 0; p < C::NCK; ++p) {
         const f32x4 x = *reinterpret_cast<const f32x4 *>(run + 4 * ((p + rho) % C::NCK));
@@ -182,10 +185,10 @@ __device__ inline void lds_run(const float *rowp, int j16, float (&out)[C::NC]) 
 }
 
 // Gradient tile c, register r of lane group g is row i = 4 g + r, real channel
-// NC i + 4 ((c / 4 + rho(i)) mod NCK) + c mod 4 with rho(i) = (i / RDIV) mod NCK:
-// in the lane's quarter of the row, float own_idx = NC r + 4 m + c mod 4.
+// NC i + 4 ((c / 4 + rho_of(i)) mod NCK) + c mod 4: in the lane's quarter of
+// the row, float own_idx = NC r + 4 m + c mod 4.
 template <class C>
-__device__ inline int run_rot(int g, int r) { return ((4 * g + r) / C::RDIV) % C::NCK; }
+__device__ inline int run_rot(int g, int r) { return rho_of<C>(4 * g + r); }
 // The owned operand's float at gradient tile c, register r, selected with
 // compile-time indices (c and r unrolled) so that the array stays in registers.
 template <class C>
