@@ -60,6 +60,12 @@ MEASURED_TRAFFIC = {
         "sha256": "edb94da4d42529beee88a404769fb38cbc9b91943c03cc8dbe8a342660201698",
         "bytes": 85.4e6,    # read 67.9 MB + write 17.5 MB
     },
+    # the whole backward call of --pass bwd (per-query scalars, dK/dV, dQ), per call
+    "bwd:born_causal_bf16_b8h16t4096d64_rotary": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_d64_bwd.hip",
+        "sha256": "3a47f8b1fc6f43fd8f52a742cde89a6d31ccafbd70382cc973e98c163609ea1a",
+        "bytes": 2153.9e6,  # read 270.8 + 561.6 + 876.9 MB, write 4.2 + 268.4 + 172.0 MB
+    },
 }
 
 
@@ -162,7 +168,7 @@ def main_bwd(args, w):
         "config": {"workload": w.name, "pass": "bwd", "op": w.op, "causal": w.causal, "B": w.B, "H": w.H,
                    "T": w.T, "d_h": w.d_h, "layout": w.layout},
         "roofline": {"bound": "mfma" if (mfma or mfma32) else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tflops / peak, "traffic": None, "kernel": kern},
+                     "frac": tflops / peak, "traffic": measured_traffic(f"bwd:{w.name}"), "kernel": kern},
     }
     if not args.no_cpu_baseline:
         import oracle
