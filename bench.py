@@ -93,8 +93,8 @@ def algorithmic_flops(w) -> float:
 
 def kernel_name(w) -> str:
     """The HIP kernel the library dispatches for this workload."""
-    if w.op == "born" and w.layout == "bf16":
-        return "born_bf16_d64_kernel" if w.d_h == 64 else "born_bf16_mfma_kernel"
+    if w.op == "born" and w.layout == "bf16" and w.d_h in (16, 32, 64, 128):
+        return {64: "born_bf16_d64_kernel", 128: "born_bf16_q16_kernel"}.get(w.d_h, "born_bf16_mfma_kernel")
     if w.d_h in (16, 32, 64, 128):   # complex64, and PCT on bf16 planes
         return "attn_f32_mfma16_kernel"
     return "generic_fwd_kernel"

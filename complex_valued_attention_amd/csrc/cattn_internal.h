@@ -91,6 +91,9 @@ hipError_t launch_generic(const Problem &p);
 bool supports_born_bf16_d64(const Problem &p);
 hipError_t launch_born_bf16_d64(const Problem &p);
 
+bool supports_born_bf16_q16(const Problem &p);
+hipError_t launch_born_bf16_q16(const Problem &p);
+
 bool supports_born_bf16_mfma(const Problem &p);
 hipError_t launch_born_bf16_mfma(const Problem &p);
 
