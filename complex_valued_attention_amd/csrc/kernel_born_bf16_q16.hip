@@ -28,7 +28,7 @@
 // 4 x 16 block), one for keys 4 g .., one for 16 + 4 g ...  Output tile c then
 // holds four consecutive channels of the lane's query in rows 4 g + r.
 //
-// LDS.  A stage of 32 keys holds four 8 KiB regions (Re K, Im K, Re V, Im V),
+// LDS.  A stage of 64 keys holds four 16 KiB regions (Re K, Im K, Re V, Im V),
 // rows of 256 bytes = 16 chunks of 16 bytes, chunk c of row r stored at slot
 // c ^ swz(r): K takes swz = r mod 16, so the 16 rows that one operand read
 // touches at one chunk fall on 16 distinct slots; V takes swz = 2 (r mod 8),
@@ -36,9 +36,15 @@
 // distinct slots.  Stages go from global memory straight into LDS (buffer
 // loads to LDS: each lane's 16 bytes land at base + 16 lane, so the swizzle is
 // applied by choosing which chunk a lane fetches).  Rows past T read as zero.
-// Three stage buffers, each its own LDS variable named at compile time: the
-// loads of stage s + 2 are issued when stage s begins, into the buffer stage
-// s - 1 used, and each stage waits only for its own loads.
+// Two stage buffers, each its own LDS variable named at compile time: the
+// loads of stage s + 1 are issued when stage s begins and are the only ones in
+// flight while it runs, so the compiler knows they never touch the buffer
+// being read and holds no read back for them.
+//
+// Pipeline.  A stage is two 32-key blocks.  When neither needs a mask, the
+// second block's score products run beside the first block's weights, and
+// the first block's value product beside the second block's weights (one
+// stretch of code, so the matrix products fill the vector work's gaps).
 //
 // Work split.  8 waves (two per SIMD), 16 queries each: row blocks of 128
 // queries.  Causal: a workgroup takes the mirrored row blocks nrb-1-i and i,
@@ -72,15 +78,16 @@ constexpr int NW = 8;                 // waves per workgroup, two per SIMD
 constexpr int NT = 64 * NW;
 constexpr int QT = 16;                // queries per wave
 constexpr int BM = QT * NW;           // query rows per row block
-constexpr int BN = 32;                // keys per stage: one block of two 16-key tiles
+constexpr int BN = 64;                // keys per stage: two blocks of two 16-key tiles
 constexpr int ROWB = 2 * D;           // bytes per row of one plane region
-constexpr int REGION = BN * ROWB;     // 8 KiB
+constexpr int REGION = BN * ROWB;     // 16 KiB
 constexpr int STAGE = 4 * REGION;     // Re K, Im K, Re V, Im V
 constexpr int TILEB = 16 * ROWB;      // bytes of 16 rows
+constexpr int BLKB = 32 * ROWB;       // bytes of a 32-key block
 constexpr int KSTEPS = 2 * D / 32;    // score k-steps of 32 real channels
 constexpr int CT = 2 * D / 16;        // 16-channel tiles of O^T (Re, then Im)
-constexpr int LOADS = 4;              // LDS-direct loads per thread and stage
-static_assert(NW * 4 == BN, "a wave stages 4 rows of each region");
+constexpr int NBUF = 2;               // stage buffers
+static_assert(NW * 8 == BN, "a wave stages 8 rows of each region, 4 per load");
 
 // gfx9 raw-buffer descriptor format word (dword 3)
 constexpr int RSRC_WORD3 = 0x00020000;
@@ -109,8 +116,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
     __shared__ __align__(16) char buf0[STAGE];
     __shared__ __align__(16) char buf1[STAGE];
-    __shared__ __align__(16) char buf2[STAGE];
-    char *const bufs[3] = {buf0, buf1, buf2};
+    char *const bufs[NBUF] = {buf0, buf1};
     // ROT: theta_m of the 128 channels
     __shared__ double rtheta[D];
 
@@ -145,18 +151,23 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
     uint16_t *oim = reinterpret_cast<uint16_t *>(p.o_im) + ho;
 
     // ---- staging: global -> LDS, no registers ------------------------------
-    // Lane (j16, g) of wave w covers row 4 w + g of each region and physical
-    // slot j16, and fetches logical chunk j16 ^ swz(row) of that row.  The
-    // descriptor's base is the stage's first key row and its extent ends at
-    // row T; each lane adds a 32-bit offset below 32 rows.
-    const int srow = 4 * wave + g;
+    // Load h (0, 1) of lane (j16, g) of wave w covers row 8 w + 4 h + g of
+    // each region and physical slot j16, and fetches logical chunk
+    // j16 ^ swz(row) of that row.  The descriptor's base is the stage's first
+    // key row and its extent ends at row T; each lane adds a 32-bit offset
+    // below 64 rows.
     const int64_t rbk = 2 * p.sk.t, rbv = 2 * p.sv.t;   // bytes from one key row to the next
-    const uint32_t offk = (uint32_t)(srow * rbk) + 16u * (uint32_t)(j16 ^ swz_k(srow));
-    const uint32_t offv = (uint32_t)(srow * rbv) + 16u * (uint32_t)(j16 ^ swz_v(srow));
+    uint32_t offk[2], offv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int srow = 8 * wave + 4 * h + g;
+        offk[h] = (uint32_t)(srow * rbk) + 16u * (uint32_t)(j16 ^ swz_k(srow));
+        offv[h] = (uint32_t)(srow * rbv) + 16u * (uint32_t)(j16 ^ swz_v(srow));
+    }
     // live = false: an extent of 0, so the loads touch no memory (they fill
-    // the buffer with zeros) and every stage issues the same number of loads.
+    // the buffer with zeros).
     auto dma_stage = [&](int k0, char *buf, bool live) {
-        char *dst = buf + wave * 1024;
+        char *dst = buf + wave * 2048;
         const int64_t left = live ? T - k0 : 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -165,21 +176,23 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(planes[r] + (int64_t)k0 * rb), 0, (int)(uint32_t)(ext < 0xffffffffll ? ext : 0xffffffffll),
                 RSRC_WORD3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(dst + r * REGION), 16,
-                                                     r < 2 ? offk : offv, 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(dst + r * REGION + h * 1024), 16,
+                                                         r < 2 ? offk[h] : offv[h], 0, 0, 0);
         }
     };
 
     // ---- per-lane LDS read offsets ----------------------------------------
-    // K' A operand, k-step ks, tile kt: row 16 kt + j16, logical chunk
-    // 4 (ks % 4) + g of the Re K (ks < 4) or Im K region.
+    // K' A operand, block sb, k-step ks, tile kt: row 32 sb + 16 kt + j16,
+    // logical chunk 4 (ks % 4) + g of the Re K (ks < 4) or Im K region.
     int koff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) koff[i] = j16 * ROWB + 16 * ((4 * i + g) ^ swz_k(j16));
     // V^T A operand of channel tile c (16 channels of the Re V or Im V region
     // from 16 (c % 8)): lane 4 r + c4 of group g points at row 4 g + r,
     // channels 16 (c % 8) + 4 c4 .. + 3, i.e. logical chunk 2 (c % 8) + c4 / 2,
-    // half c4 % 2; the second read is 16 rows further.
+    // half c4 % 2, of block sb; the second read is 16 rows further.
     int voff[8];
     {
         const int r = (lane >> 2) & 3, c4 = lane & 3;
@@ -233,22 +246,25 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
     // the row sum of the packed weights in four independent partial sums
     float rsum[4];
 
-    // One 32-key block from stage buffer st, first key kb0; the wave's first
-    // query qt0.  masked: keys above a query or at or past T get weight 0.
-    auto block = [&](const char *st, int kb0, int qt0, bool masked) {
-        f32x4 sr[2], si[2];
+    // Score products of 32-key block sb of stage buffer st.
+    auto scores = [&](const char *st, int sb, f32x4 (&sr)[2], f32x4 (&si)[2]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) sr[kt] = si[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + (ks >> 2) * REGION + kt * TILEB + koff[ks & 3]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + (ks >> 2) * REGION + sb * BLKB + kt * TILEB +
+                                                                   koff[ks & 3]);
                 sr[kt] = mfma(a, qb[ks], sr[kt]);
                 si[kt] = mfma(a, ks < 4 ? qb[ks + 4] : qn[ks - 4], si[kt]);
             }
-        __builtin_amdgcn_sched_barrier(0);
-        // weights: register r of tile kt is key kb0 + 16 kt + 4 g + r
+    };
+    // The block's weights (first key kb0; the wave's first query qt0), packed
+    // to bf16 as the B operand of its value product and added to the row sums.
+    // Register r of tile kt is key kb0 + 16 kt + 4 g + r.  masked: keys above
+    // the query or at or past T get weight 0.
+    auto weights = [&](const f32x4 (&sr)[2], const f32x4 (&si)[2], int kb0, int qt0, bool masked) {
         const int q = qt0 + j16;
         uint32_t pk[4];
 #pragma unroll
@@ -272,16 +288,19 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
                 rsum[2 * kt + rp] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[2 * kt + rp]), ones,
                                                                     rsum[2 * kt + rp], false);
             }
-        const bf16x8 wop = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+        return as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+    };
+    // The value product of block sb: its packed weights wop against its V
+    // tile in stage buffer st.
+    auto values = [&](const char *st, int sb, bf16x8 wop) {
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            const char *vb = st + (2 + (c >> 3)) * REGION + voff[c & 7];
+            const char *vb = st + (2 + (c >> 3)) * REGION + sb * BLKB + voff[c & 7];
             const u32x2 lo = ds_read_tr(vb);
             const u32x2 hi = ds_read_tr(vb + TILEB);
             oacc[c] = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), wop, oacc[c]);
         }
     };
-
     // ---- the workgroup's row blocks and their key stages --------------------
     const int nblocks = p.causal && item != nrb - 1 - item ? 2 : 1;
     auto row_block = [&](int blk) { return p.causal ? (blk == 0 ? nrb - 1 - item : item) : item; };
@@ -293,7 +312,7 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
     const int nst1 = nblocks > 1 ? stages_of(1) : 0;
     const int total = nst0 + nst1;
     // the workgroup's stages form one stream, row blocks in order; stage gs
-    // lives in buffer gs % 3
+    // lives in buffer gs % 2
     auto stage_k0 = [&](int gs) { return (gs < nst0 ? gs : gs - nst0) * BN; };
 
     auto epilogue = [&](int qt0) {
@@ -314,50 +333,66 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
         }
     };
 
-    // One stage: wait for its loads (the four newest of this wave belong to
-    // the next stage), barrier (every wave is past the previous stage, whose
-    // buffer the loads of stage gs + 2 now overwrite), issue those loads, run
-    // the block.
+    // One stage: every wave's loads of it have landed and every wave is past
+    // the previous stage (whose buffer the loads of stage gs + 1 now fill).
     auto step = [&](auto J, int gs) {
         constexpr int j = decltype(J)::value;
         __asm__ __volatile__("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(LOADS | (7 << 4) | (15 << 8));   // vmcnt(4)
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
         __builtin_amdgcn_s_barrier();
         __asm__ __volatile__("" ::: "memory");
-        dma_stage(stage_k0(gs + 2), bufs[(j + 2) % 3], gs + 2 < total);
-
         const int blk = gs < nst0 ? 0 : 1;
         const int s = gs - (blk ? nst0 : 0);
         const int qt0 = row_block(blk) * BM + QT * wave;
         if (s == 0) {
+            // before the stage loads, so that waiting for Q leaves them in flight
             load_q(qt0);
 #pragma unroll
             for (int c = 0; c < CT; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
             rsum[0] = rsum[1] = rsum[2] = rsum[3] = 0.f;
         }
+        dma_stage(stage_k0(gs + 1), bufs[(j + 1) % NBUF], gs + 1 < total);
+        const char *st = bufs[j];
         const int kb0 = s * BN;
-        const bool skip = qt0 >= T || kb0 >= T || (p.causal && kb0 > qt0 + QT - 1);
-        const bool full = (!p.causal || kb0 + BN - 1 <= qt0) && kb0 + BN <= T;
-        if (!skip) {
-            if (full)
-                block(bufs[j], kb0, qt0, false);
-            else
-                block(bufs[j], kb0, qt0, true);
+        bool skip[2], full[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kb = kb0 + 32 * sb;
+            skip[sb] = qt0 >= T || kb >= T || (p.causal && kb > qt0 + QT - 1);
+            full[sb] = (!p.causal || kb + 31 <= qt0) && kb + 32 <= T;
+        }
+        if (full[0] && full[1]) {
+            f32x4 sr0[2], si0[2], sr1[2], si1[2];
+            scores(st, 0, sr0, si0);
+            const bf16x8 w0 = weights(sr0, si0, kb0, qt0, false);
+            scores(st, 1, sr1, si1);
+            values(st, 0, w0);
+            const bf16x8 w1 = weights(sr1, si1, kb0 + 32, qt0, false);
+            values(st, 1, w1);
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                if (!skip[sb]) {
+                    f32x4 sr[2], si[2];
+                    scores(st, sb, sr, si);
+                    const bf16x8 w = full[sb] ? weights(sr, si, kb0 + 32 * sb, qt0, false)
+                                              : weights(sr, si, kb0 + 32 * sb, qt0, true);
+                    values(st, sb, w);
+                }
+            }
         }
         if (s == (blk ? nst1 : nst0) - 1) epilogue(qt0);
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
 
     if (ROT) {
         if (tid < D) rtheta[tid] = rotary_theta(tid, p.rot_log_base, D);
         __syncthreads();
     }
     dma_stage(stage_k0(0), buf0, total > 0);
-    dma_stage(stage_k0(1), buf1, total > 1);
-    for (int gs = 0; gs < total; gs += 3) {
+    for (int gs = 0; gs < total; gs += NBUF) {
         // The read offsets are loop-invariant, and so is every address of a
         // statically named buffer: left alone, the compiler holds one register
         // per address across the loop.  Made opaque here, they are formed
@@ -367,7 +402,6 @@ void born_bf16_q16_kernel(Problem p, int nrb, int nwork) {
                              "+v"(voff[4]), "+v"(voff[5]), "+v"(voff[6]), "+v"(voff[7]));
         step(I0{}, gs);
         if (gs + 1 < total) step(I1{}, gs + 1);
-        if (gs + 2 < total) step(I2{}, gs + 2);
     }
     // Loads past the stream's end (extent 0) still write zeros into LDS: let
     // them land before the workgroup's LDS can be handed to another.
