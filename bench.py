@@ -49,6 +49,12 @@ MEASURED_TRAFFIC = {
         "sha256": "7c6c753ec257cb2bcb7994a9cefdb6a4d9be0ae4b53adfd20d83b712767e6259",
         "bytes": 930.9e6,   # read 796.7 MB + write 134.2 MB
     },
+    # the bench workload's shape at head width 128 (bench.py --d-h 128)
+    "born_causal_bf16_b8h16t4096d64_rotary@d128": {
+        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_q16.hip",
+        "sha256": "7eaddfbe61c6d9bc2617346432df5dc9ec3eb0302827839d8d319cd84165d843",
+        "bytes": 1701.9e6,  # read 1433.4 MB + write 268.4 MB
+    },
     # the carried-state kernels of --pass linear at chunk 4096 (mean per launch over a pass)
     "linear-state:born_causal_bf16_b1h16t32768d64_rotary:4096": {
         "source": "complex_valued_attention_amd/csrc/kernel_born_linear_bf16.hip",
