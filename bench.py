@@ -51,9 +51,9 @@ MEASURED_TRAFFIC = {
     },
     # the bench workload's shape at head width 128 (bench.py --d-h 128)
     "born_causal_bf16_b8h16t4096d64_rotary@d128": {
-        "source": "complex_valued_attention_amd/csrc/kernel_born_bf16_q16.hip",
-        "sha256": "7eaddfbe61c6d9bc2617346432df5dc9ec3eb0302827839d8d319cd84165d843",
-        "bytes": 1701.9e6,  # read 1433.4 MB + write 268.4 MB
+        "source": "complex_valued_attention_amd/csrc/born_bf16_q16_impl.h",
+        "sha256": "68eb1accd09ff91e97b784ae0e67cd3dccffb6158e3ba261555a07ebea288074",
+        "bytes": 1706.9e6,  # read 1438.5 MB + write 268.4 MB
     },
     # the carried-state kernels of --pass linear at chunk 4096 (mean per launch over a pass)
     "linear-state:born_causal_bf16_b1h16t32768d64_rotary:4096": {
@@ -100,7 +100,8 @@ def algorithmic_flops(w) -> float:
 def kernel_name(w) -> str:
     """The HIP kernel the library dispatches for this workload."""
     if w.op == "born" and w.layout == "bf16" and w.d_h in (16, 32, 64, 128):
-        return {64: "born_bf16_d64_kernel", 128: "born_bf16_q16_kernel"}.get(w.d_h, "born_bf16_mfma_kernel")
+        return {64: "born_bf16_d64_kernel", 128: "born_bf16_q16_kernel", 32: "born_bf16_q16_kernel"}.get(
+            w.d_h, "born_bf16_mfma_kernel")
     if w.d_h in (16, 32, 64, 128):   # complex64, and PCT on bf16 planes
         return "attn_f32_mfma16_kernel"
     return "generic_fwd_kernel"

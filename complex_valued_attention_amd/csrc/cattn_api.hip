@@ -175,8 +175,10 @@ cattn_status run(const Problem &p) {
     hipError_t e;
     if (cattn::supports_born_bf16_d64(p))
         e = cattn::launch_born_bf16_d64(p);
-    else if (cattn::supports_born_bf16_q16(p))
-        e = cattn::launch_born_bf16_q16(p);
+    else if (cattn::supports_born_bf16_q16<128>(p))
+        e = cattn::launch_born_bf16_q16<128>(p);
+    else if (cattn::supports_born_bf16_q16<32>(p))
+        e = cattn::launch_born_bf16_q16<32>(p);
     else if (cattn::supports_born_bf16_mfma(p))
         e = cattn::launch_born_bf16_mfma(p);
     else if (cattn::supports_f32_mfma16(p))

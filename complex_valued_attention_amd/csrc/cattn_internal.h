@@ -91,8 +91,9 @@ hipError_t launch_generic(const Problem &p);
 bool supports_born_bf16_d64(const Problem &p);
 hipError_t launch_born_bf16_d64(const Problem &p);
 
-bool supports_born_bf16_q16(const Problem &p);
-hipError_t launch_born_bf16_q16(const Problem &p);
+// Width D (128 or 32), one translation unit each.
+template <int D> bool supports_born_bf16_q16(const Problem &p);
+template <int D> hipError_t launch_born_bf16_q16(const Problem &p);
 
 bool supports_born_bf16_mfma(const Problem &p);
 hipError_t launch_born_bf16_mfma(const Problem &p);

@@ -377,13 +377,12 @@ hipError_t launch_cfg(const Problem &p) {
 }  // namespace
 
 bool supports_born_bf16_mfma(const Problem &p) {
-    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && (p.d == 16 || p.d == 32) && p.aligned16;
+    return p.op == OP_BORN && p.layout == LAYOUT_BF16 && p.d == 16 && p.aligned16;
 }
 
 hipError_t launch_born_bf16_mfma(const Problem &p) {
     switch (p.d) {
         case 16: return launch_cfg<16, 1, 8, 64>(p);
-        case 32: return launch_cfg<32, 1, 8, 64>(p);
         default: return hipErrorNotSupported;
     }
 }

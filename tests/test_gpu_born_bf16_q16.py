@@ -1,13 +1,14 @@
-"""GPU parity of the width-128 Born forward on bf16 planes (16-query tiles,
-16 x 16 x 32 products) against the fp64 oracle, through the C ABI.
+"""GPU parity of the Born forward on bf16 planes at head widths 128 and 32
+(16-query tiles, 16 x 16 x 32 products) against the fp64 oracle, through the
+C ABI.
 
 Small cases cover every output row and denominator: one query, ragged tails
 around the 16-query tile, the 32-key stage and the 128-query row block, odd
 and even row-block counts (the causal mirrored pairs), non-causal, eps > 0,
-both head mappings (BH a multiple of 8 or not), decay and rotary Q.  The full
-workload at this width (B8 H16 T4096, causal, rotary inputs) runs in the
-benchmark's launch configuration and is checked on sampled rows, and its
-output is bitwise the same over repeated calls.
+both head mappings (BH a multiple of 8 or not), decay and rotary Q.  The
+benchmark workload's shape at these widths (B8 H16 T4096, causal, rotary
+inputs) runs in the benchmark's launch configuration and is checked on
+sampled rows, and its output is bitwise the same over repeated calls.
 """
 import dataclasses
 
@@ -21,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-D = 128
+WIDTHS = [128, 32]
 
 
 def _cattn():
@@ -57,8 +58,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", WIDTHS)
 @pytest.mark.parametrize("causal,B,H,T,eps", CASES)
-def test_born_bf16_d128_small(causal, B, H, T, eps):
+def test_born_bf16_q16_small(D, causal, B, H, T, eps):
     import oracle
     c = _cattn()
     w = gen.Workload("q16", "born", causal, B, H, T, D, "bf16", seed=61, qk_unit=True, rotary=True)
@@ -70,14 +72,15 @@ def test_born_bf16_d128_small(causal, B, H, T, eps):
     torch.cuda.synchronize()
     ref, rden = oracle.born_attention(inp.q64, inp.k64, inp.v64, causal=causal, eps=eps, return_den=True)
     err = rowwise_rel_err(from_device(o), ref)
-    say(f"q16 causal={causal} B{B} H{H} T{T} eps={eps}: rowwise rel err {err:.3e}")
+    say(f"q16 d{D} causal={causal} B{B} H{H} T{T} eps={eps}: rowwise rel err {err:.3e}")
     assert err <= TOL["bf16"]
     gd = den.cpu().numpy().reshape(B, H, T).astype(np.float64)
     np.testing.assert_allclose(gd, rden, rtol=2e-2)
 
 
 @pytest.mark.parametrize("T,gammas", [(300, (0.9, 0.995)), (129, (0.5, 1.0))])
-def test_born_bf16_d128_decay(T, gammas):
+@pytest.mark.parametrize("D", WIDTHS)
+def test_born_bf16_q16_decay(D, T, gammas):
     import oracle
     c = _cattn()
     w = gen.Workload("q16d", "born", True, 1, 2, T, D, "bf16", seed=62, qk_unit=True, rotary=True)
@@ -89,12 +92,13 @@ def test_born_bf16_d128_decay(T, gammas):
     g32 = np.asarray(gammas, dtype=np.float32).astype(np.float64)
     ref = oracle.born_attention(inp.q64, inp.k64, inp.v64, causal=True, decay=g32)
     err = rowwise_rel_err(from_device(o), ref)
-    say(f"q16 decay T{T}: rowwise rel err {err:.3e}")
+    say(f"q16 decay d{D} T{T}: rowwise rel err {err:.3e}")
     assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("T,pos0", [(300, 0), (77, 123_457)])
-def test_born_bf16_d128_rotary_q(T, pos0):
+@pytest.mark.parametrize("D", WIDTHS)
+def test_born_bf16_q16_rotary_q(D, T, pos0):
     # rotary Q in the kernel against the rotary pass over Q followed by the plain kernel
     c = _cattn()
     w = gen.Workload("q16r", "born", True, 1, 2, T, D, "bf16", seed=63, qk_unit=True)
@@ -107,11 +111,12 @@ def test_born_bf16_d128_rotary_q(T, pos0):
     torch.cuda.synchronize()
     a, b = from_device(o_in), from_device(o_pass)
     err = rowwise_rel_err(a, b)
-    say(f"q16 rotary T{T} pos0 {pos0}: in-kernel vs pass {err:.3e}")
+    say(f"q16 rotary d{D} T{T} pos0 {pos0}: in-kernel vs pass {err:.3e}")
     assert err <= 1e-2
 
 
-def test_born_bf16_d128_full_size_sampled_and_deterministic():
+@pytest.mark.parametrize("D", WIDTHS)
+def test_born_bf16_q16_full_size_sampled_and_deterministic(D):
     import oracle
     c = _cattn()
     w = dataclasses.replace(gen.WORKLOADS["born_causal_bf16_b8h16t4096d64_rotary"], d_h=D)
@@ -128,5 +133,5 @@ def test_born_bf16_d128_full_size_sampled_and_deterministic():
     rows = sample_rows(w.B, w.H, w.T, 96, seed=w.seed, tile=128)
     ref = oracle.born_attention_rows(inp.q64, inp.k64, inp.v64, rows, causal=True)
     err = rowwise_rel_err(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref)
-    say(f"q16 full size, {len(rows)} sampled rows: rowwise rel err {err:.3e}")
+    say(f"q16 d{D} full size, {len(rows)} sampled rows: rowwise rel err {err:.3e}")
     assert err <= TOL["bf16"]
